@@ -1,0 +1,53 @@
+"""Shared comparison helpers for the tests (no method arithmetic here)."""
+from __future__ import annotations
+
+import numpy as np
+
+# Tolerances for floating-point results of the attention path: relative
+# Frobenius error and elementwise error relative to the reference's max.
+REL_FRO_TOL = 5e-3
+ELEM_TOL = 2e-2
+
+
+def as_np64(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def rel_fro(got, ref) -> float:
+    got, ref = as_np64(got), as_np64(ref)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(got - ref)
+    return float(num / den) if den > 0 else float(num)
+
+
+def check_close(got, ref, name: str = "", rel_tol: float = REL_FRO_TOL,
+                elem_tol: float = ELEM_TOL):
+    """Relative Frobenius error <= rel_tol and max|err| <= elem_tol * max|ref|."""
+    got, ref = as_np64(got), as_np64(ref)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    rf = rel_fro(got, ref)
+    amax = float(np.max(np.abs(ref))) if ref.size else 0.0
+    emax = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert rf <= rel_tol, f"{name}: rel Frobenius error {rf:.3e} > {rel_tol}"
+    assert emax <= elem_tol * amax + 1e-30, (
+        f"{name}: max abs error {emax:.3e} > {elem_tol} * max|ref| ({amax:.3e})")
+    return rf, emax
+
+
+def bf16_bits(x) -> np.ndarray:
+    """Raw 16-bit patterns of a bf16 torch tensor."""
+    import torch
+    return x.detach().to("cpu").contiguous().view(torch.int16).numpy().astype(np.uint16)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """bf16 bit patterns of fp64 values that are exactly representable in bf16."""
+    x = np.asarray(x, dtype=np.float64)
+    f32 = x.astype(np.float32)
+    assert np.array_equal(f32.astype(np.float64), x, equal_nan=True), "not fp32-exact"
+    bits = f32.view(np.uint32)
+    assert np.all((bits & 0xFFFF) == 0), "value not exactly representable in bf16"
+    return (bits >> 16).astype(np.uint16)
