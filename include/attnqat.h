@@ -1,0 +1,159 @@
+/*
+ * attnqat.h -- C ABI of the MI355X (gfx950) NVFP4 fake-quantized attention
+ * QAT library (libattnqat.so).
+ *
+ * The operation is the one defined in "NVFP4 Attention QAT Backward"
+ * (cuDNN frontend docs), §Overview, formula block:
+ *
+ *   Q^, K^, V^ = fake_nvfp4(Q), fake_nvfp4(K), fake_nvfp4(V)
+ *   P          = softmax(softmax_scale * Q^ K^T)          (unquantized)
+ *   O_hp       = P V^                                     (forward auxiliary)
+ *   dS         = P * (dO V^T - rowsum(O_hp * dO))
+ *   dQ         = softmax_scale * dS K^,  dK = softmax_scale * dS^T Q^   (STE)
+ *   dV         = fake_nvfp4(P)^T dO      (P grouped in 16s along keys)
+ *
+ * fake_nvfp4 (same page, §Overview): per 16 contiguous values, an E4M3FN
+ * block scale s = RNE(amax / 6) (saturating at 448) and E2M1 codes
+ * c = RNE(|x| / s) by precise division (exact midpoints round to even),
+ * then x^ = sign(x) * c * s.  x^ is exact in bf16.
+ *
+ * Conventions (after the page's §Class API and §Tensor contract):
+ *  - Tensors are contiguous BHSD: (batch, heads, seqlen, head_dim), bf16
+ *    (raw 16-bit words), lse fp32 (batch, heads, seqlen_q), natural log.
+ *    Every pointer is a device pointer, 16-byte aligned, on the current
+ *    HIP device.
+ *  - The caller owns every buffer.  No call allocates device memory or keeps
+ *    a pointer after it returns; fwd/bwd take a caller-supplied workspace
+ *    whose size comes from the *_workspace_bytes queries.
+ *  - Calls are asynchronous on the given stream (0 = the null stream).
+ *    Buffers belong to the call until the stream has passed it.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    error nothing is launched and outputs are untouched.
+ *  - Outputs are fully overwritten, never accumulated into.  Results are
+ *    bitwise deterministic (no atomics).
+ *  - The library is stateless apart from a per-device architecture check
+ *    cache; concurrent calls on different streams are safe when each call
+ *    has its own workspace and outputs.
+ *  - Limits (§Current support and limitations of the same page, plus
+ *    head_dim 64): MHA only, head_dim in {64, 128}, causal is
+ *    self-attention only (seqlen_q == seqlen_kv), no dropout, bias,
+ *    padding masks or GQA.  NaN/Inf inputs are unsupported.
+ */
+#ifndef ATTNQAT_H_
+#define ATTNQAT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTNQAT_API __attribute__((visibility("default")))
+
+/* Status codes. */
+#define ATTNQAT_OK 0
+#define ATTNQAT_ERR_INVALID_ARGUMENT (-1) /* null pointer, size <= 0, non-finite or <= 0 scale */
+#define ATTNQAT_ERR_UNSUPPORTED (-2)      /* head_dim, causal cross-attention, device not gfx950 */
+#define ATTNQAT_ERR_MISALIGNED (-3)       /* a pointer is not 16-byte aligned */
+#define ATTNQAT_ERR_WORKSPACE_TOO_SMALL (-4)
+#define ATTNQAT_ERR_HIP (-5)              /* a HIP runtime call or kernel launch failed */
+
+/* Element types for attnqat_fake_nvfp4. */
+#define ATTNQAT_DTYPE_BF16 0
+#define ATTNQAT_DTYPE_F32 1
+
+/* Which workspace layout attnqat_workspace_layout describes. */
+#define ATTNQAT_WS_FWD 0
+#define ATTNQAT_WS_BWD 1
+
+/* One attention problem.  softmax_scale must be the forward's (the page's
+ * default is 1/sqrt(128)); p_scale pre-scales P before its fake
+ * quantization in dV: P^F = fake_nvfp4(p_scale * P) / p_scale.  1.0 is the
+ * literal formula; any finite value > 0 is accepted. */
+typedef struct attnqat_problem {
+  int32_t batch;
+  int32_t heads;
+  int32_t seqlen_q;
+  int32_t seqlen_kv;
+  int32_t head_dim; /* 64 or 128 */
+  int32_t causal;   /* 0 or 1; 1 requires seqlen_q == seqlen_kv */
+  float softmax_scale;
+  float p_scale;
+} attnqat_problem;
+
+/* Byte offsets into a workspace (see attnqat_workspace_layout).  Absent
+ * parts are SIZE_MAX. */
+typedef struct attnqat_ws_layout {
+  size_t total_bytes;
+  size_t q_hat;   /* bf16 (B,H,Nq,D): fake_nvfp4(Q) */
+  size_t k_hat;   /* bf16 (B,H,Nkv,D) */
+  size_t v_hat;   /* bf16 (B,H,Nkv,D) */
+  size_t q_scale; /* uint8 E4M3FN (B,H,Nq,D/16): the block scales of Q^ */
+  size_t k_scale; /* uint8 (B,H,Nkv,D/16) */
+  size_t v_scale; /* uint8 (B,H,Nkv,D/16) */
+  size_t delta;   /* fp32 (B,H,Nq): rowsum(O_hp * dO); backward only */
+} attnqat_ws_layout;
+
+/* A short English description of a status code (static storage). */
+ATTNQAT_API const char* attnqat_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+ATTNQAT_API int attnqat_version(void);
+
+/* Validates a problem on the host only (no HIP call): sizes > 0,
+ * head_dim in {64,128}, causal only with seqlen_q == seqlen_kv, finite
+ * scales > 0.  Returns ATTNQAT_OK or the error code. */
+ATTNQAT_API int attnqat_check_support(const attnqat_problem* p);
+
+/* Checks that HIP device `device` is a gfx950 (MI355X class) GPU.  Returns
+ * ATTNQAT_OK, ATTNQAT_ERR_UNSUPPORTED or ATTNQAT_ERR_HIP. */
+ATTNQAT_API int attnqat_check_device(int device);
+
+/* Workspace sizes, in bytes, for attnqat_fwd / attnqat_bwd (host only). */
+ATTNQAT_API int attnqat_fwd_workspace_bytes(const attnqat_problem* p, size_t* bytes);
+ATTNQAT_API int attnqat_bwd_workspace_bytes(const attnqat_problem* p, size_t* bytes);
+
+/* Where each intermediate lives in the fwd (which = ATTNQAT_WS_FWD) or bwd
+ * (ATTNQAT_WS_BWD) workspace, so callers can read Q^/K^/V^, their scales
+ * and delta after a call (host only). */
+ATTNQAT_API int attnqat_workspace_layout(const attnqat_problem* p, int which,
+                                         attnqat_ws_layout* out);
+
+/* fake_nvfp4 along rows: x is (rows, row_len) of `dtype` (bf16 or fp32),
+ * row_len % 16 == 0, groups of 16 contiguous values along each row.
+ * Writes x_hat (same dtype and shape; may alias x) and, when `scales` is
+ * not NULL, the E4M3FN byte of every group (rows, row_len/16).  rows == 0
+ * is a no-op.  Results are bit-exact to the definition above.
+ * (Page: "NVFP4 Attention QAT Backward", §Overview.) */
+ATTNQAT_API int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_t* scales,
+                                   int64_t rows, int64_t row_len, hipStream_t stream);
+
+/* QAT forward producing the backward's auxiliaries (page §High-level
+ * wrapper: O_hp is softmax(Q^ K^T * scale) V^ saved before probability
+ * quantization; lse its natural-log log-sum-exp).
+ * In: q (B,H,Nq,D), k, v (B,H,Nkv,D) bf16.  Out: o_hp (B,H,Nq,D) bf16,
+ * lse (B,H,Nq) fp32.  The workspace (>= attnqat_fwd_workspace_bytes) holds
+ * Q^/K^/V^ and their scales afterwards (attnqat_workspace_layout). */
+ATTNQAT_API int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k,
+                            const void* v, void* o_hp, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* QAT backward (page §Overview formula block and four-kernel structure:
+ * Q fake-quant + delta, K/V fake-quant, dQ, dK/dV).
+ * In: q, o_hp, d_o (B,H,Nq,D) bf16; k, v (B,H,Nkv,D) bf16; lse (B,H,Nq)
+ * fp32 from the matching forward.  Out: dq (B,H,Nq,D), dk, dv (B,H,Nkv,D)
+ * bf16.  The workspace (>= attnqat_bwd_workspace_bytes) holds Q^/K^/V^,
+ * their scales and delta afterwards. */
+ATTNQAT_API int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k,
+                            const void* v, const void* o_hp, const void* d_o,
+                            const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNQAT_H_ */

@@ -1,0 +1,224 @@
+"""Thin ctypes binding of libattnqat.so (include/attnqat.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch supplies device memory (``data_ptr()``) and streams.  The functions
+keep the C names; ``nvfp4_attention_qat_backward`` additionally mirrors the
+high-level wrapper of "NVFP4 Attention QAT Backward" (§High-level wrapper:
+it returns ``dq_tensor``/``dk_tensor``/``dv_tensor``, accepts preallocated
+outputs and an explicit stream).
+
+If the library is missing this module raises on import: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattnqat.so")
+
+OK = 0
+ERR_INVALID_ARGUMENT = -1
+ERR_UNSUPPORTED = -2
+ERR_MISALIGNED = -3
+ERR_WORKSPACE_TOO_SMALL = -4
+ERR_HIP = -5
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+WS_FWD = 0
+WS_BWD = 1
+
+
+class attnqat_problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("seqlen_q", ctypes.c_int32), ("seqlen_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("p_scale", ctypes.c_float)]
+
+
+class attnqat_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("total_bytes", "q_hat", "k_hat", "v_hat", "q_scale", "k_scale", "v_scale",
+                 "delta")]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m nvfp4_fake_quantized_amd.csrc.build` (no fallback exists)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.POINTER(attnqat_problem)
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_SIGS = {
+    "attnqat_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "attnqat_version": (ctypes.c_int, []),
+    "attnqat_check_support": (ctypes.c_int, [_P]),
+    "attnqat_check_device": (ctypes.c_int, [ctypes.c_int]),
+    "attnqat_fwd_workspace_bytes": (ctypes.c_int, [_P, ctypes.POINTER(_sz)]),
+    "attnqat_bwd_workspace_bytes": (ctypes.c_int, [_P, ctypes.POINTER(_sz)]),
+    "attnqat_workspace_layout": (ctypes.c_int, [_P, ctypes.c_int,
+                                                ctypes.POINTER(attnqat_ws_layout)]),
+    "attnqat_fake_nvfp4": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int64,
+                                          ctypes.c_int64, _vp]),
+    "attnqat_fwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "attnqat_bwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                   _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class AttnQatError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+def status_string(status: int) -> str:
+    return _lib.attnqat_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise AttnQatError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_problem(batch, heads, seqlen_q, seqlen_kv, head_dim, causal=False,
+                 softmax_scale=None, p_scale=1.0) -> attnqat_problem:
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    return attnqat_problem(batch, heads, seqlen_q, seqlen_kv, head_dim, int(bool(causal)),
+                           float(softmax_scale), float(p_scale))
+
+
+def problem_for(q, k, causal=False, softmax_scale=None, p_scale=1.0) -> attnqat_problem:
+    B, H, Nq, D = q.shape
+    return make_problem(B, H, Nq, k.shape[2], D, causal, softmax_scale, p_scale)
+
+
+# ---- C-ABI functions (same names) --------------------------------------------
+
+def attnqat_version() -> int:
+    return _lib.attnqat_version()
+
+
+def attnqat_check_support(p: attnqat_problem) -> int:
+    return _lib.attnqat_check_support(ctypes.byref(p))
+
+
+def attnqat_check_device(device: int = 0) -> int:
+    return _lib.attnqat_check_device(device)
+
+
+def attnqat_fwd_workspace_bytes(p: attnqat_problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.attnqat_fwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)),
+           "attnqat_fwd_workspace_bytes")
+    return n.value
+
+
+def attnqat_bwd_workspace_bytes(p: attnqat_problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.attnqat_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)),
+           "attnqat_bwd_workspace_bytes")
+    return n.value
+
+
+def attnqat_workspace_layout(p: attnqat_problem, which: int) -> dict:
+    out = attnqat_ws_layout()
+    _check(_lib.attnqat_workspace_layout(ctypes.byref(p), which, ctypes.byref(out)),
+           "attnqat_workspace_layout")
+    return {name: getattr(out, name) for name, _ in attnqat_ws_layout._fields_}
+
+
+def attnqat_fake_nvfp4(x, x_hat=None, scales=None, stream=None):
+    """fake_nvfp4 of a contiguous bf16/fp32 CUDA tensor in groups of 16 along
+    its last dim.  Returns ``(x_hat, scales)`` (scales: uint8 E4M3FN bytes)."""
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be bf16 or fp32")
+    dtype = DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_F32
+    L = x.shape[-1] if x.dim() > 0 else 1
+    rows = x.numel() // L if L else 0
+    if x_hat is None:
+        x_hat = torch.empty_like(x)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (max(L // 16, 0),), dtype=torch.uint8,
+                             device=x.device)
+    for t in (x, x_hat, scales):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    _check(_lib.attnqat_fake_nvfp4(_ptr(x), dtype, _ptr(x_hat), _ptr(scales), rows, L,
+                                   _stream(stream)), "attnqat_fake_nvfp4")
+    return x_hat, scales
+
+
+def attnqat_fwd(p: attnqat_problem, q, k, v, o_hp, lse, workspace, stream=None):
+    _check(_lib.attnqat_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp), _ptr(lse),
+                            _ptr(workspace), workspace.numel(), _stream(stream)), "attnqat_fwd")
+
+
+def attnqat_bwd(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace, stream=None):
+    _check(_lib.attnqat_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp), _ptr(d_o),
+                            _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                            workspace.numel(), _stream(stream)), "attnqat_bwd")
+
+
+# ---- conveniences (allocation via torch, then one C call) --------------------
+
+def _check_bhsd(*ts):
+    for t in ts:
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("expected contiguous bf16 (B, H, S, D) tensors")
+
+
+def nvfp4_attention_qat_forward(q, k, v, is_causal=False, softmax_scale=None, p_scale=1.0,
+                                workspace=None, current_stream=None):
+    """Returns ``(high_precision_o, lse)`` of the QAT forward."""
+    _check_bhsd(q, k, v)
+    p = problem_for(q, k, is_causal, softmax_scale, p_scale)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(attnqat_fwd_workspace_bytes(p), dtype=torch.uint8,
+                                device=q.device)
+    attnqat_fwd(p, q, k, v, o, lse, workspace, current_stream)
+    return o, lse
+
+
+def nvfp4_attention_qat_backward(do, q, k, v, high_precision_o, lse, is_causal=False,
+                                 softmax_scale=None, p_scale=1.0, dq_tensor=None,
+                                 dk_tensor=None, dv_tensor=None, workspace=None,
+                                 current_stream=None):
+    """Returns ``{"dq_tensor", "dk_tensor", "dv_tensor"}``."""
+    _check_bhsd(do, q, k, v, high_precision_o)
+    p = problem_for(q, k, is_causal, softmax_scale, p_scale)
+    dq = torch.empty_like(q) if dq_tensor is None else dq_tensor
+    dk = torch.empty_like(k) if dk_tensor is None else dk_tensor
+    dv = torch.empty_like(v) if dv_tensor is None else dv_tensor
+    if workspace is None:
+        workspace = torch.empty(attnqat_bwd_workspace_bytes(p), dtype=torch.uint8,
+                                device=q.device)
+    attnqat_bwd(p, q, k, v, high_precision_o, do, lse, dq, dk, dv, workspace, current_stream)
+    return {"dq_tensor": dq, "dk_tensor": dk, "dv_tensor": dv}

@@ -1,0 +1,263 @@
+// C ABI of libattnqat.so: host-side validation, workspace layout and the
+// ordered kernel launches (declared in include/attnqat.h).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "attnqat.h"
+#include "kernels.hpp"
+
+namespace {
+
+using attnqat::AttnArgs;
+using attnqat::QuantJob;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate_problem(const attnqat_problem* p) {
+  if (p == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (p->batch <= 0 || p->heads <= 0 || p->seqlen_q <= 0 || p->seqlen_kv <= 0 ||
+      p->head_dim <= 0)
+    return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (!(isfinite(p->softmax_scale) && p->softmax_scale > 0.0f)) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (!(isfinite(p->p_scale) && p->p_scale > 0.0f)) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (p->causal != 0 && p->causal != 1) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (p->head_dim != 64 && p->head_dim != 128) return ATTNQAT_ERR_UNSUPPORTED;
+  if (p->causal && p->seqlen_q != p->seqlen_kv) return ATTNQAT_ERR_UNSUPPORTED;
+  // batch*heads is the grid's y extent
+  if ((int64_t)p->batch * p->heads > 65535) return ATTNQAT_ERR_UNSUPPORTED;
+  return ATTNQAT_OK;
+}
+
+struct Layout {
+  size_t q_hat, k_hat, v_hat, q_scale, k_scale, v_scale, delta, total;
+};
+
+Layout make_layout(const attnqat_problem* p, bool bwd) {
+  const size_t bh = (size_t)p->batch * p->heads;
+  const size_t nq = bh * p->seqlen_q, nkv = bh * p->seqlen_kv;
+  const size_t D = p->head_dim;
+  Layout L;
+  size_t off = 0;
+  L.q_hat = off;   off = align_up(off + nq * D * 2);
+  L.k_hat = off;   off = align_up(off + nkv * D * 2);
+  L.v_hat = off;   off = align_up(off + nkv * D * 2);
+  L.q_scale = off; off = align_up(off + nq * D / 16);
+  L.k_scale = off; off = align_up(off + nkv * D / 16);
+  L.v_scale = off; off = align_up(off + nkv * D / 16);
+  if (bwd) {
+    L.delta = off;
+    off = align_up(off + nq * 4);
+  } else {
+    L.delta = SIZE_MAX;
+  }
+  L.total = off;
+  return L;
+}
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+int8_t g_arch_state[256];
+
+int device_status() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTNQAT_ERR_HIP;
+  return attnqat_check_device(dev);
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attnqat_status_string(int status) {
+  switch (status) {
+    case ATTNQAT_OK: return "ok";
+    case ATTNQAT_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ATTNQAT_ERR_UNSUPPORTED: return "unsupported problem or device";
+    case ATTNQAT_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case ATTNQAT_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case ATTNQAT_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+int attnqat_version(void) { return 100; }
+
+int attnqat_check_support(const attnqat_problem* p) { return validate_problem(p); }
+
+int attnqat_check_device(int device) {
+  if (device < 0 || device >= 256) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  const int8_t st = __atomic_load_n(&g_arch_state[device], __ATOMIC_RELAXED);
+  if (st == 1) return ATTNQAT_OK;
+  if (st == 2) return ATTNQAT_ERR_UNSUPPORTED;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return ATTNQAT_ERR_HIP;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  __atomic_store_n(&g_arch_state[device], (int8_t)(ok ? 1 : 2), __ATOMIC_RELAXED);
+  return ok ? ATTNQAT_OK : ATTNQAT_ERR_UNSUPPORTED;
+}
+
+int attnqat_fwd_workspace_bytes(const attnqat_problem* p, size_t* bytes) {
+  const int st = validate_problem(p);
+  if (st != ATTNQAT_OK) return st;
+  if (bytes == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  *bytes = make_layout(p, false).total;
+  return ATTNQAT_OK;
+}
+
+int attnqat_bwd_workspace_bytes(const attnqat_problem* p, size_t* bytes) {
+  const int st = validate_problem(p);
+  if (st != ATTNQAT_OK) return st;
+  if (bytes == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  *bytes = make_layout(p, true).total;
+  return ATTNQAT_OK;
+}
+
+int attnqat_workspace_layout(const attnqat_problem* p, int which, attnqat_ws_layout* out) {
+  const int st = validate_problem(p);
+  if (st != ATTNQAT_OK) return st;
+  if (out == nullptr || (which != ATTNQAT_WS_FWD && which != ATTNQAT_WS_BWD))
+    return ATTNQAT_ERR_INVALID_ARGUMENT;
+  const Layout L = make_layout(p, which == ATTNQAT_WS_BWD);
+  out->total_bytes = L.total;
+  out->q_hat = L.q_hat;
+  out->k_hat = L.k_hat;
+  out->v_hat = L.v_hat;
+  out->q_scale = L.q_scale;
+  out->k_scale = L.k_scale;
+  out->v_scale = L.v_scale;
+  out->delta = L.delta;
+  return ATTNQAT_OK;
+}
+
+int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_t* scales, int64_t rows,
+                       int64_t row_len, hipStream_t stream) {
+  if (dtype != ATTNQAT_DTYPE_BF16 && dtype != ATTNQAT_DTYPE_F32) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (rows < 0 || row_len <= 0 || (row_len % 16) != 0) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (rows > ((int64_t)1 << 40) / row_len) return ATTNQAT_ERR_UNSUPPORTED;
+  if (rows == 0) return ATTNQAT_OK;
+  if (x == nullptr || x_hat == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(x_hat)) return ATTNQAT_ERR_MISALIGNED;
+  const int dst = device_status();
+  if (dst != ATTNQAT_OK) return dst;
+  (void)hipGetLastError();
+  QuantJob job{x, x_hat, scales, rows * (row_len / 16)};
+  const hipError_t e = dtype == ATTNQAT_DTYPE_BF16 ? attnqat::launch_quant_bf16(&job, 1, stream)
+                                                   : attnqat::launch_quant_f32(job, stream);
+  return e == hipSuccess ? ATTNQAT_OK : ATTNQAT_ERR_HIP;
+}
+
+int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st != ATTNQAT_OK) return st;
+  const void* ptrs[] = {q, k, v, o_hp, lse, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTNQAT_ERR_MISALIGNED;
+  const Layout L = make_layout(p, false);
+  if (workspace_bytes < L.total) return ATTNQAT_ERR_WORKSPACE_TOO_SMALL;
+  st = device_status();
+  if (st != ATTNQAT_OK) return st;
+  (void)hipGetLastError();
+
+  const int64_t bh = (int64_t)p->batch * p->heads;
+  const int64_t D = p->head_dim;
+  uint16_t* qh = at<uint16_t>(workspace, L.q_hat);
+  uint16_t* kh = at<uint16_t>(workspace, L.k_hat);
+  uint16_t* vh = at<uint16_t>(workspace, L.v_hat);
+  QuantJob jobs[3] = {
+      {q, qh, at<uint8_t>(workspace, L.q_scale), bh * p->seqlen_q * D / 16},
+      {k, kh, at<uint8_t>(workspace, L.k_scale), bh * p->seqlen_kv * D / 16},
+      {v, vh, at<uint8_t>(workspace, L.v_scale), bh * p->seqlen_kv * D / 16},
+  };
+  if (attnqat::launch_quant_bf16(jobs, 3, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+
+  AttnArgs a = {};
+  a.q_hat = qh;
+  a.k_hat = kh;
+  a.v_hat = vh;
+  a.o_hp = static_cast<uint16_t*>(o_hp);
+  a.lse_out = lse;
+  a.bh = (int)bh;
+  a.nq = p->seqlen_q;
+  a.nkv = p->seqlen_kv;
+  a.causal = p->causal;
+  a.softmax_scale = p->softmax_scale;
+  a.p_scale = p->p_scale;
+  if (attnqat::launch_fwd(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  return ATTNQAT_OK;
+}
+
+int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                const void* o_hp, const void* d_o, const float* lse, void* dq, void* dk,
+                void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st != ATTNQAT_OK) return st;
+  const void* ptrs[] = {q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTNQAT_ERR_MISALIGNED;
+  const Layout L = make_layout(p, true);
+  if (workspace_bytes < L.total) return ATTNQAT_ERR_WORKSPACE_TOO_SMALL;
+  st = device_status();
+  if (st != ATTNQAT_OK) return st;
+  (void)hipGetLastError();
+
+  const int64_t bh = (int64_t)p->batch * p->heads;
+  const int64_t D = p->head_dim;
+  uint16_t* qh = at<uint16_t>(workspace, L.q_hat);
+  uint16_t* kh = at<uint16_t>(workspace, L.k_hat);
+  uint16_t* vh = at<uint16_t>(workspace, L.v_hat);
+  float* delta = at<float>(workspace, L.delta);
+
+  // 1) Q fake-quantization fused with delta = rowsum(O_hp * dO)
+  if (attnqat::launch_quant_q_delta(static_cast<const uint16_t*>(q),
+                                    static_cast<const uint16_t*>(o_hp),
+                                    static_cast<const uint16_t*>(d_o), qh,
+                                    at<uint8_t>(workspace, L.q_scale), delta,
+                                    bh * p->seqlen_q, p->head_dim, stream) != hipSuccess)
+    return ATTNQAT_ERR_HIP;
+  // 2) K/V fake-quantization
+  QuantJob jobs[2] = {
+      {k, kh, at<uint8_t>(workspace, L.k_scale), bh * p->seqlen_kv * D / 16},
+      {v, vh, at<uint8_t>(workspace, L.v_scale), bh * p->seqlen_kv * D / 16},
+  };
+  if (attnqat::launch_quant_bf16(jobs, 2, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+
+  AttnArgs a = {};
+  a.q_hat = qh;
+  a.k_hat = kh;
+  a.v_hat = vh;
+  a.d_o = static_cast<const uint16_t*>(d_o);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.bh = (int)bh;
+  a.nq = p->seqlen_q;
+  a.nkv = p->seqlen_kv;
+  a.causal = p->causal;
+  a.softmax_scale = p->softmax_scale;
+  a.p_scale = p->p_scale;
+  // 3) dQ and 4) dK/dV
+  if (attnqat::launch_bwd_dq(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  if (attnqat::launch_bwd_dkdv(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  return ATTNQAT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Host-side launchers of the attnqat kernels.  Each returns hipSuccess or the
+// launch error; arguments are validated by the C-ABI layer beforehand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnqat {
+
+// Per-problem pointers and sizes passed to the attention kernels.  All
+// tensors are contiguous BHSD; bf16 tensors are raw 16-bit words.
+struct AttnArgs {
+  const uint16_t* q_hat;  // (BH, nq, D)
+  const uint16_t* k_hat;  // (BH, nkv, D)
+  const uint16_t* v_hat;  // (BH, nkv, D)
+  const uint16_t* d_o;    // (BH, nq, D)       backward only
+  const float* lse;       // (BH, nq)          backward input / forward output
+  const float* delta;     // (BH, nq)          backward only
+  uint16_t* o_hp;         // (BH, nq, D)       forward output
+  float* lse_out;         // (BH, nq)          forward output
+  uint16_t* dq;           // (BH, nq, D)
+  uint16_t* dk;           // (BH, nkv, D)
+  uint16_t* dv;           // (BH, nkv, D)
+  int bh;                 // batch * heads
+  int nq, nkv;
+  int causal;
+  float softmax_scale;
+  float p_scale;
+};
+
+// One tensor to fake-quantize along its contiguous dim in groups of 16.
+struct QuantJob {
+  const void* src;
+  void* dst;
+  uint8_t* scales;  // may be null
+  int64_t groups;   // number of 16-element groups
+};
+
+// fake_nvfp4 over up to three bf16 tensors in one launch.
+hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream);
+// fake_nvfp4 over one fp32 tensor.
+hipError_t launch_quant_f32(const QuantJob& job, hipStream_t stream);
+// Q fake-quant fused with delta = rowsum(O_hp * dO) (fp32), D in {64,128}.
+hipError_t launch_quant_q_delta(const uint16_t* q, const uint16_t* o_hp, const uint16_t* d_o,
+                                uint16_t* q_hat, uint8_t* q_scale, float* delta,
+                                int64_t rows, int head_dim, hipStream_t stream);
+
+hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream);
+
+}  // namespace attnqat

@@ -1,0 +1,176 @@
+// NVFP4 fake-quantization kernels (HBM-bound codec work).
+//
+// One thread owns one group of 16 contiguous values ("NVFP4 Attention QAT
+// Backward", §Overview: one E4M3 scale per 16 values); a wave covers 64
+// consecutive groups, i.e. 2 KiB of contiguous bf16 input.  The fused
+// Q + delta kernel is the first of the backward's four kernels (same page,
+// §Overview: "fused Q fake-quantization/delta preprocessing").
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attnqat {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct QuantJobs3 {
+  QuantJob job[3];
+};
+
+__device__ __forceinline__ void unpack_bf16x16(u32x4 lo, u32x4 hi, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_bits_to_f32(lo[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_bits_to_f32(lo[i] >> 16);
+    x[8 + 2 * i] = bf16_bits_to_f32(hi[i] & 0xFFFFu);
+    x[8 + 2 * i + 1] = bf16_bits_to_f32(hi[i] >> 16);
+  }
+}
+
+__device__ __forceinline__ void pack_bf16x16(const float* x, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // values are exact in bf16: truncation of the low half is exact
+    lo[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xFFFF0000u);
+    hi[i] = (__float_as_uint(x[8 + 2 * i]) >> 16) |
+            (__float_as_uint(x[8 + 2 * i + 1]) & 0xFFFF0000u);
+  }
+}
+
+// Quantizes 16 floats in place; returns the scale.
+__device__ __forceinline__ float fq16(float* x) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float s = e4m3_scale_from_amax(amax);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = e2m1_dequant(x[i], s);
+  return s;
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_bf16(QuantJobs3 jobs) {
+  const QuantJob& J = jobs.job[blockIdx.y];
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= J.groups) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(J.src) + 2 * g;
+  u32x4 lo = src[0], hi = src[1];
+  float x[16];
+  unpack_bf16x16(lo, hi, x);
+  const float s = fq16(x);
+  pack_bf16x16(x, lo, hi);
+  u32x4* dst = reinterpret_cast<u32x4*>(J.dst) + 2 * g;
+  dst[0] = lo;
+  dst[1] = hi;
+  if (J.scales) J.scales[g] = (uint8_t)e4m3_byte(s);
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_f32(QuantJob J) {
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= J.groups) return;
+  const f32x4* src = reinterpret_cast<const f32x4*>(J.src) + 4 * g;
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f32x4 v = src[i];
+    x[4 * i] = v[0];
+    x[4 * i + 1] = v[1];
+    x[4 * i + 2] = v[2];
+    x[4 * i + 3] = v[3];
+  }
+  const float s = fq16(x);
+  f32x4* dst = reinterpret_cast<f32x4*>(J.dst) + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f32x4 v = {x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+    dst[i] = v;
+  }
+  if (J.scales) J.scales[g] = (uint8_t)e4m3_byte(s);
+}
+
+// GPR = groups per row (D / 16): 8 for D = 128, 4 for D = 64.  The GPR lanes
+// of a row are consecutive and aligned within the wave.
+template <int GPR>
+__global__ __launch_bounds__(kThreads) void k_quant_q_delta(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ o_hp,
+                                                            const uint16_t* __restrict__ d_o,
+                                                            uint16_t* __restrict__ q_hat,
+                                                            uint8_t* __restrict__ q_scale,
+                                                            float* __restrict__ delta,
+                                                            int64_t rows) {
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t groups = rows * GPR;
+  const bool active = g < groups;
+  const int64_t gg = active ? g : 0;
+  float part = 0.0f;
+  {
+    const u32x4* po = reinterpret_cast<const u32x4*>(o_hp) + 2 * gg;
+    const u32x4* pd = reinterpret_cast<const u32x4*>(d_o) + 2 * gg;
+    float o[16], d[16];
+    unpack_bf16x16(po[0], po[1], o);
+    unpack_bf16x16(pd[0], pd[1], d);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part = fmaf(o[i], d[i], part);
+  }
+  if (active) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(q) + 2 * g;
+    u32x4 lo = src[0], hi = src[1];
+    float x[16];
+    unpack_bf16x16(lo, hi, x);
+    const float s = fq16(x);
+    pack_bf16x16(x, lo, hi);
+    u32x4* dst = reinterpret_cast<u32x4*>(q_hat) + 2 * g;
+    dst[0] = lo;
+    dst[1] = hi;
+    q_scale[g] = (uint8_t)e4m3_byte(s);
+  }
+  // reduce the row's partial dot products over its GPR lanes (fixed order)
+#pragma unroll
+  for (int off = 1; off < GPR; off <<= 1) part += __shfl_xor(part, off, 64);
+  if (active && (g % GPR) == 0) delta[g / GPR] = part;
+}
+
+inline unsigned grid_for(int64_t groups) {
+  return (unsigned)((groups + kThreads - 1) / kThreads);
+}
+
+}  // namespace
+
+hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream) {
+  QuantJobs3 j3 = {};
+  int64_t maxg = 0;
+  for (int i = 0; i < njobs; ++i) {
+    j3.job[i] = jobs[i];
+    if (jobs[i].groups > maxg) maxg = jobs[i].groups;
+  }
+  if (maxg == 0) return hipSuccess;
+  dim3 grid(grid_for(maxg), njobs);
+  hipLaunchKernelGGL(k_quant_bf16, grid, dim3(kThreads), 0, stream, j3);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_f32(const QuantJob& job, hipStream_t stream) {
+  if (job.groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_f32, dim3(grid_for(job.groups)), dim3(kThreads), 0, stream, job);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_q_delta(const uint16_t* q, const uint16_t* o_hp, const uint16_t* d_o,
+                                uint16_t* q_hat, uint8_t* q_scale, float* delta, int64_t rows,
+                                int head_dim, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int gpr = head_dim / 16;
+  const unsigned grid = grid_for(rows * gpr);
+  if (gpr == 8) {
+    hipLaunchKernelGGL(k_quant_q_delta<8>, dim3(grid), dim3(kThreads), 0, stream, q, o_hp, d_o,
+                       q_hat, q_scale, delta, rows);
+  } else {
+    hipLaunchKernelGGL(k_quant_q_delta<4>, dim3(grid), dim3(kThreads), 0, stream, q, o_hp, d_o,
+                       q_hat, q_scale, delta, rows);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attnqat

@@ -1,0 +1,155 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function include/attnqat.h declares,
+and reject invalid arguments on the host, before any HIP call, with the
+documented status codes.  Pointers handed to the library here are never
+dereferenced: every call below returns during validation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from nvfp4_fake_quantized_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnqat.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"ATTNQAT_API\s+[\w\s\*]+?\b(attnqat_\w+)\s*\(", text)
+
+
+def test_header_declares_expected_functions():
+    names = _declared_functions()
+    assert set(names) == set(B.EXPORTED), (names, B.EXPORTED)
+    for required in ("attnqat_fake_nvfp4", "attnqat_fwd", "attnqat_bwd"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(B.attnqat_problem) == 32
+    assert ctypes.sizeof(B.attnqat_ws_layout) == 8 * ctypes.sizeof(ctypes.c_size_t)
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert B.status_string(code) and B.status_string(code) != "unknown status"
+    assert B.status_string(7) == "unknown status"
+
+
+def _prob(**kw):
+    base = dict(batch=1, heads=16, seqlen_q=4096, seqlen_kv=4096, head_dim=128, causal=False,
+                softmax_scale=1 / math.sqrt(128), p_scale=1.0)
+    base.update(kw)
+    return B.make_problem(base["batch"], base["heads"], base["seqlen_q"], base["seqlen_kv"],
+                          base["head_dim"], base["causal"], base["softmax_scale"],
+                          base["p_scale"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, B.OK),
+    ({"head_dim": 64}, B.OK),
+    ({"seqlen_q": 100, "seqlen_kv": 333}, B.OK),
+    ({"causal": True}, B.OK),
+    ({"head_dim": 96}, B.ERR_UNSUPPORTED),
+    ({"head_dim": 256}, B.ERR_UNSUPPORTED),
+    ({"causal": True, "seqlen_kv": 2048}, B.ERR_UNSUPPORTED),
+    ({"batch": 0}, B.ERR_INVALID_ARGUMENT),
+    ({"heads": -1}, B.ERR_INVALID_ARGUMENT),
+    ({"seqlen_q": 0}, B.ERR_INVALID_ARGUMENT),
+    ({"softmax_scale": 0.0}, B.ERR_INVALID_ARGUMENT),
+    ({"softmax_scale": float("nan")}, B.ERR_INVALID_ARGUMENT),
+    ({"softmax_scale": float("inf")}, B.ERR_INVALID_ARGUMENT),
+    ({"p_scale": -1.0}, B.ERR_INVALID_ARGUMENT),
+    ({"batch": 300, "heads": 300}, B.ERR_UNSUPPORTED),
+])
+def test_check_support(kw, code):
+    assert B.attnqat_check_support(_prob(**kw)) == code
+
+
+def test_check_support_null():
+    assert B._lib.attnqat_check_support(None) == B.ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes_and_layout():
+    p = _prob()
+    bh, n, d = 16, 4096, 128
+    L = B.attnqat_workspace_layout(p, B.WS_BWD)
+    assert L["total_bytes"] == B.attnqat_bwd_workspace_bytes(p)
+    assert L["q_hat"] == 0
+    assert L["k_hat"] >= bh * n * d * 2
+    assert L["v_hat"] >= L["k_hat"] + bh * n * d * 2
+    assert L["q_scale"] >= L["v_hat"] + bh * n * d * 2
+    assert L["delta"] >= L["v_scale"] + bh * n * d // 16
+    assert L["total_bytes"] >= L["delta"] + bh * n * 4
+    for key in ("q_hat", "k_hat", "v_hat", "q_scale", "k_scale", "v_scale", "delta"):
+        assert L[key] % 256 == 0
+    F = B.attnqat_workspace_layout(p, B.WS_FWD)
+    assert F["delta"] == ctypes.c_size_t(-1).value
+    assert F["total_bytes"] == B.attnqat_fwd_workspace_bytes(p)
+    with pytest.raises(B.AttnQatError):
+        B.attnqat_workspace_layout(p, 5)
+    with pytest.raises(B.AttnQatError):
+        B.attnqat_bwd_workspace_bytes(_prob(head_dim=80))
+
+
+def _vp(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_fwd_bwd_reject_bad_arguments_before_launch():
+    lib = B._lib
+    p = _prob(batch=1, heads=1, seqlen_q=128, seqlen_kv=128)
+    need = B.attnqat_bwd_workspace_bytes(p)
+    a = [_vp(0x10000 * (i + 1)) for i in range(10)]  # aligned, never dereferenced
+    # null pointer
+    args = list(a)
+    args[3] = None
+    assert lib.attnqat_bwd(ctypes.byref(p), *args[:9], args[9], need, None) == \
+        B.ERR_INVALID_ARGUMENT
+    # misaligned pointer
+    args = list(a)
+    args[2] = _vp(0x30008)
+    assert lib.attnqat_bwd(ctypes.byref(p), *args[:9], args[9], need, None) == B.ERR_MISALIGNED
+    # workspace too small
+    assert lib.attnqat_bwd(ctypes.byref(p), *a[:9], a[9], need - 1, None) == \
+        B.ERR_WORKSPACE_TOO_SMALL
+    # invalid problem wins over everything else
+    bad = _prob(head_dim=32)
+    assert lib.attnqat_bwd(ctypes.byref(bad), *a[:9], a[9], need, None) == B.ERR_UNSUPPORTED
+    assert lib.attnqat_bwd(None, *a[:9], a[9], need, None) == B.ERR_INVALID_ARGUMENT
+    # forward
+    fneed = B.attnqat_fwd_workspace_bytes(p)
+    assert lib.attnqat_fwd(ctypes.byref(p), a[0], a[1], None, a[3], a[4], a[5], fneed, None) == \
+        B.ERR_INVALID_ARGUMENT
+    assert lib.attnqat_fwd(ctypes.byref(p), a[0], a[1], a[2], _vp(0x40004), a[4], a[5], fneed,
+                           None) == B.ERR_MISALIGNED
+    assert lib.attnqat_fwd(ctypes.byref(p), *a[:6], fneed - 256, None) == \
+        B.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_fake_nvfp4_rejects_bad_arguments_before_launch():
+    lib = B._lib
+    x, y, s = _vp(0x10000), _vp(0x20000), _vp(0x30000)
+    assert lib.attnqat_fake_nvfp4(x, 7, y, s, 4, 16, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.attnqat_fake_nvfp4(x, B.DTYPE_BF16, y, s, 4, 24, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.attnqat_fake_nvfp4(x, B.DTYPE_BF16, y, s, -1, 16, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.attnqat_fake_nvfp4(x, B.DTYPE_BF16, y, s, 4, 0, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.attnqat_fake_nvfp4(None, B.DTYPE_BF16, y, s, 4, 16, None) == \
+        B.ERR_INVALID_ARGUMENT
+    assert lib.attnqat_fake_nvfp4(_vp(0x10002), B.DTYPE_BF16, y, s, 4, 16, None) == \
+        B.ERR_MISALIGNED
+    # empty input: nothing to do, nothing launched
+    assert lib.attnqat_fake_nvfp4(None, B.DTYPE_F32, None, None, 0, 16, None) == B.OK

@@ -1,0 +1,318 @@
+"""GPU parity of attnqat_fwd / attnqat_bwd against the fp64 oracle.
+
+Bars: Q^/K^/V^ and their E4M3 scale bytes bit-exact; O_hp, lse, delta, dQ,
+dK and dV within relative Frobenius error 5e-3 and elementwise error
+2e-2 * max|ref|.  The backward is run on the oracle forward's (O_hp, lse)
+rounded to (bf16, fp32), fed to both sides; the chain GPU fwd -> GPU bwd is
+checked against oracle fwd -> oracle bwd as well.
+
+Sizes: the small workloads over every head; the reference shape over three
+heads in full plus sampled rows of every head; the two largest workloads on
+sampled rows and 16-key groups (always including the last, partial group)
+of two heads, with the oracle forward computed in full for those heads.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_fake_quantized_amd import binding as B
+from oracle.attention import qat_backward_full_head, qat_backward_head, qat_forward_head
+from oracle.nvfp4 import fake_nvfp4
+from tests._util import bf16_bits, check_close, f64_to_bf16_bits
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+# ---- helpers -------------------------------------------------------------------
+
+def _ws_part(ws, off, shape, dtype):
+    n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+    return ws[off:off + n].view(dtype).view(*shape)
+
+
+def gpu_fwd(q, k, v, causal, scale, p_scale=1.0, stream=None):
+    p = B.problem_for(q, k, causal, scale, p_scale)
+    ws = torch.empty(B.attnqat_fwd_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    B.attnqat_fwd(p, q, k, v, o, lse, ws, stream)
+    torch.cuda.synchronize()
+    return o, lse, ws, B.attnqat_workspace_layout(p, B.WS_FWD)
+
+
+def gpu_bwd(q, k, v, o, do, lse, causal, scale, p_scale=1.0, stream=None):
+    p = B.problem_for(q, k, causal, scale, p_scale)
+    ws = torch.empty(B.attnqat_bwd_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B.attnqat_bwd(p, q, k, v, o, do, lse, dq, dk, dv, ws, stream)
+    torch.cuda.synchronize()
+    return dq, dk, dv, ws, B.attnqat_workspace_layout(p, B.WS_BWD)
+
+
+def check_quantized_workspace(ws, L, tensors, heads=None):
+    """Q^/K^/V^ and scale bytes in the workspace are bit-exact to the oracle."""
+    for name, t in zip(("q", "k", "v"), tensors):
+        Bb, H, N, D = t.shape
+        xh = _ws_part(ws, L[f"{name}_hat"], (Bb, H, N, D), torch.bfloat16).cpu()
+        sc = _ws_part(ws, L[f"{name}_scale"], (Bb, H, N, D // 16), torch.uint8).cpu()
+        hs = [(b, h) for b in range(Bb) for h in range(H)] if heads is None else heads
+        for b, h in hs:
+            ref, _, scode, _ = fake_nvfp4(t[b, h].double().numpy())
+            assert np.array_equal(bf16_bits(xh[b, h]), f64_to_bf16_bits(ref)), (name, b, h)
+            assert np.array_equal(sc[b, h].numpy(), scode), (name, b, h)
+
+
+def oracle_fwd_full(q, k, v, scale, causal, chunk=2048):
+    """Oracle forward over every row of one head, in row chunks."""
+    n = q.shape[0]
+    os_, ls_ = [], []
+    for r0 in range(0, n, chunk):
+        o, l = qat_forward_head(q, k, v, scale, causal, rows=np.arange(r0, min(n, r0 + chunk)))
+        os_.append(o)
+        ls_.append(l)
+    return np.concatenate(os_), np.concatenate(ls_)
+
+
+def rounded_aux(o64, lse64):
+    """The oracle forward's outputs as the backward receives them."""
+    return torch.from_numpy(o64).to(torch.bfloat16), torch.from_numpy(lse64).float()
+
+
+def run_full_case(q, k, v, do, causal, scale, p_scale=1.0, heads=None, label=""):
+    """Full parity on the given heads: fwd, quantized workspace, bwd, chain."""
+    Bb, H = q.shape[:2]
+    heads = [(b, h) for b in range(Bb) for h in range(H)] if heads is None else heads
+    print(f"[attn parity] {label} shape={tuple(q.shape)} nkv={k.shape[2]} causal={causal} "
+          f"p_scale={p_scale} heads={heads}", flush=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o_g, lse_g, wsf, Lf = gpu_fwd(qd, kd, vd, causal, scale, p_scale)
+    check_quantized_workspace(wsf, Lf, (q, k, v), heads)
+    # oracle forward per head; the backward's inputs are its rounded outputs
+    o_in = o_g.clone()
+    lse_in = lse_g.clone()
+    ref_f = {}
+    for b, h in heads:
+        o64, l64 = oracle_fwd_full(q[b, h], k[b, h], v[b, h], scale, causal)
+        ref_f[(b, h)] = (o64, l64)
+        check_close(o_g[b, h].cpu(), o64, f"{label} O_hp[{b},{h}]")
+        check_close(lse_g[b, h].cpu(), l64, f"{label} lse[{b},{h}]")
+        ob, lb = rounded_aux(o64, l64)
+        o_in[b, h] = ob.to(DEV)
+        lse_in[b, h] = lb.to(DEV)
+    dq, dk, dv, wsb, Lb = gpu_bwd(qd, kd, vd, o_in, dod, lse_in, causal, scale, p_scale)
+    check_quantized_workspace(wsb, Lb, (q, k, v), heads)
+    delta = _ws_part(wsb, Lb["delta"], q.shape[:3], torch.float32).cpu()
+    # chain: GPU fwd -> GPU bwd
+    cq, ck, cv, _, _ = gpu_bwd(qd, kd, vd, o_g, dod, lse_g, causal, scale, p_scale)
+    for b, h in heads:
+        ob, lb = o_in[b, h].cpu(), lse_in[b, h].cpu()
+        check_close(delta[b, h], (ob.double() * do[b, h].double()).sum(-1).numpy(),
+                    f"{label} delta[{b},{h}]")
+        rq, rk, rv = qat_backward_full_head(q[b, h], k[b, h], v[b, h], ob, do[b, h], lb, scale,
+                                            causal, p_scale)
+        check_close(dq[b, h].cpu(), rq, f"{label} dQ[{b},{h}]")
+        check_close(dk[b, h].cpu(), rk, f"{label} dK[{b},{h}]")
+        check_close(dv[b, h].cpu(), rv, f"{label} dV[{b},{h}]")
+        o64, l64 = ref_f[(b, h)]
+        cq_ref, ck_ref, cv_ref = qat_backward_full_head(q[b, h], k[b, h], v[b, h], o64,
+                                                        do[b, h], l64, scale, causal, p_scale)
+        check_close(cq[b, h].cpu(), cq_ref, f"{label} chain dQ[{b},{h}]")
+        check_close(ck[b, h].cpu(), ck_ref, f"{label} chain dK[{b},{h}]")
+        check_close(cv[b, h].cpu(), cv_ref, f"{label} chain dV[{b},{h}]")
+
+
+def _synthetic(n, d, seed, nk=None, heads=1, batch=1):
+    g = torch.Generator().manual_seed(seed)
+    nk = n if nk is None else nk
+    mk = lambda m: torch.randn(batch, heads, m, d, generator=g).to(torch.bfloat16)
+    return mk(n), mk(nk), mk(nk), mk(n)
+
+
+# ---- workloads -----------------------------------------------------------------
+
+@pytest.mark.parametrize("p_scale", [1.0, 2688.0])
+def test_tiny_workload(p_scale):
+    w = WORKLOADS["tiny"]
+    q, k, v, do = make_inputs(w)
+    run_full_case(q, k, v, do, w.causal, w.softmax_scale, p_scale, label="tiny")
+
+
+def test_small_causal_workload():
+    w = WORKLOADS["small_causal"]
+    q, k, v, do = make_inputs(w)
+    run_full_case(q, k, v, do, w.causal, w.softmax_scale, label="small_causal")
+
+
+@pytest.mark.timeout(900)
+def test_ref_shape_workload():
+    w = WORKLOADS["ref_shape"]
+    q, k, v, do = make_inputs(w)
+    run_full_case(q, k, v, do, w.causal, w.softmax_scale, heads=[(0, 0), (0, 8), (0, 15)],
+                  label="ref_shape")
+    # every head: sampled forward rows
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o_g, lse_g, _, _ = gpu_fwd(qd, kd, vd, w.causal, w.softmax_scale)
+    rows = np.sort(np.random.default_rng(2).choice(w.seqlen, 48, replace=False))
+    for h in range(w.heads):
+        o64, l64 = qat_forward_head(q[0, h], k[0, h], v[0, h], w.softmax_scale, w.causal,
+                                    rows=rows)
+        check_close(o_g[0, h, rows].cpu(), o64, f"ref_shape O_hp rows h={h}")
+        check_close(lse_g[0, h, rows].cpu(), l64, f"ref_shape lse rows h={h}")
+
+
+def _sampled_big_workload(name, heads, n_rows=96, n_groups=6):
+    w = WORKLOADS[name]
+    q, k, v, do = make_inputs(w)
+    N = w.seqlen
+    print(f"[attn parity] {name} full size, heads {heads}", flush=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o_g, lse_g, wsf, Lf = gpu_fwd(qd, kd, vd, w.causal, w.softmax_scale)
+    check_quantized_workspace(wsf, Lf, (q, k, v), heads)
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([[0, 1, N - 1], rng.choice(N, n_rows, replace=False)]))
+    ngroups = -(-N // 16)
+    groups = sorted(set([0, ngroups - 1] + list(rng.choice(ngroups, n_groups, replace=False))))
+    o_in, lse_in = o_g.clone(), lse_g.clone()
+    ref_f = {}
+    for b, h in heads:
+        o64, l64 = oracle_fwd_full(q[b, h], k[b, h], v[b, h], w.softmax_scale, w.causal)
+        ref_f[(b, h)] = (o64, l64)
+        check_close(o_g[b, h].cpu(), o64, f"{name} O_hp[{b},{h}]")
+        check_close(lse_g[b, h].cpu(), l64, f"{name} lse[{b},{h}]")
+        ob, lb = rounded_aux(o64, l64)
+        o_in[b, h] = ob.to(DEV)
+        lse_in[b, h] = lb.to(DEV)
+    dq, dk, dv, wsb, Lb = gpu_bwd(qd, kd, vd, o_in, dod, lse_in, w.causal, w.softmax_scale)
+    keys = np.concatenate([np.arange(16 * g, min(16 * g + 16, N)) for g in groups])
+    for b, h in heads:
+        ob, lb = o_in[b, h].cpu(), lse_in[b, h].cpu()
+        rq, rk, rv = qat_backward_head(q[b, h], k[b, h], v[b, h], ob, do[b, h], lb,
+                                       w.softmax_scale, w.causal, rows=rows, key_groups=groups)
+        check_close(dq[b, h, rows].cpu(), rq, f"{name} dQ rows [{b},{h}]")
+        check_close(dk[b, h, keys].cpu(), rk, f"{name} dK groups [{b},{h}]")
+        check_close(dv[b, h, keys].cpu(), rv, f"{name} dV groups [{b},{h}]")
+    return w, q, k, v, o_g, lse_g, rows
+
+
+@pytest.mark.timeout(900)
+def test_llm_causal_workload_sampled():
+    w, q, k, v, o_g, lse_g, rows = _sampled_big_workload("llm_causal", [(0, 0), (1, 39)])
+    # forward rows of further heads
+    for b, h in [(0, 20), (1, 7)]:
+        o64, l64 = qat_forward_head(q[b, h], k[b, h], v[b, h], w.softmax_scale, w.causal,
+                                    rows=rows)
+        check_close(o_g[b, h, rows].cpu(), o64, f"llm_causal O_hp rows [{b},{h}]")
+        check_close(lse_g[b, h, rows].cpu(), l64, f"llm_causal lse rows [{b},{h}]")
+
+
+@pytest.mark.timeout(1200)
+def test_video_dit_workload_sampled():
+    w, q, k, v, o_g, lse_g, rows = _sampled_big_workload("video_dit", [(0, 0)], n_rows=64,
+                                                         n_groups=4)
+    for b, h in [(0, 20), (0, 39)]:
+        o64, l64 = qat_forward_head(q[b, h], k[b, h], v[b, h], w.softmax_scale, w.causal,
+                                    rows=rows)
+        check_close(o_g[b, h, rows].cpu(), o64, f"video_dit O_hp rows [{b},{h}]")
+        check_close(lse_g[b, h, rows].cpu(), l64, f"video_dit lse rows [{b},{h}]")
+
+
+# ---- tails, causal, cross-attention, degenerate sizes --------------------------
+
+@pytest.mark.parametrize("n,d,causal,nk", [
+    (200, 64, True, None), (333, 128, False, None), (77, 64, True, None), (130, 128, True, None),
+    (100, 128, False, 260), (300, 64, False, 40), (17, 64, False, None), (16, 128, True, None),
+    (1, 64, True, None), (1, 128, False, 5),
+])
+def test_ragged_and_degenerate_shapes(n, d, causal, nk):
+    q, k, v, do = _synthetic(n, d, seed=n * 3 + d, nk=nk, heads=2)
+    run_full_case(q, k, v, do, causal, 1.0 / math.sqrt(d), label=f"ragged n={n} nk={nk}")
+
+
+def test_single_token_causal_closed_form():
+    """N = 1 causal: P = [[1]], fq(1) = 1.03125, so dV = 1.03125 dO; dQ = 0."""
+    q, k, v, do = _synthetic(1, 128, seed=5)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse, _, _ = gpu_fwd(qd, kd, vd, True, 0.1)
+    dq, dk, dv, _, _ = gpu_bwd(qd, kd, vd, o, dod, lse, True, 0.1)
+    want = (1.03125 * do.double()).to(torch.bfloat16)
+    assert torch.equal(dv.cpu(), want)
+    assert float(dq.abs().max()) <= 2e-3 * float(do.abs().max())
+
+
+def test_p_scale_on_causal_workload():
+    w = WORKLOADS["small_causal"]
+    q, k, v, do = make_inputs(w, heads=2)
+    run_full_case(q, k, v, do, True, w.softmax_scale, p_scale=2688.0, label="small_causal p2688")
+
+
+# ---- robustness ------------------------------------------------------------------
+
+def test_bitwise_deterministic_and_stream_ordered():
+    q, k, v, do = _synthetic(520, 128, seed=77, heads=3)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o1, l1, _, _ = gpu_fwd(qd, kd, vd, False, 0.09)
+    r1 = gpu_bwd(qd, kd, vd, o1, dod, l1, False, 0.09)[:3]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2, _, _ = gpu_fwd(qd, kd, vd, False, 0.09, stream=s)
+        r2 = gpu_bwd(qd, kd, vd, o2, dod, l2, False, 0.09, stream=s)[:3]
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_outputs_and_workspace_stay_in_bounds():
+    """Canary guard bands after every output and the workspace."""
+    n, d, H = 200, 64, 2
+    q, k, v, do = (t.to(DEV) for t in _synthetic(n, d, seed=9, heads=H))
+    p = B.problem_for(q, k, True, 0.125)
+    numel = H * n * d
+    guard = 4096
+    sentinel = -12345.0
+
+    def guarded(count, dtype):
+        buf = torch.full((count + guard,), sentinel, dtype=dtype, device=DEV)
+        return buf, buf[:count]
+
+    ob, o = guarded(numel, torch.bfloat16)
+    lb, lse = guarded(H * n, torch.float32)
+    need = B.attnqat_fwd_workspace_bytes(p)
+    wb = torch.full((need + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    B.attnqat_fwd(p, q, k, v, o.view(1, H, n, d), lse.view(1, H, n), wb[:need])
+    bneed = B.attnqat_bwd_workspace_bytes(p)
+    wb2 = torch.full((bneed + guard,), 0x5A, dtype=torch.uint8, device=DEV)
+    outs = [guarded(numel, torch.bfloat16) for _ in range(3)]
+    B.attnqat_bwd(p, q, k, v, o.view(1, H, n, d), do, lse.view(1, H, n),
+                  *(t[1].view(1, H, n, d) for t in outs), wb2[:bneed])
+    torch.cuda.synchronize()
+    assert torch.all(ob[numel:] == sentinel) and torch.all(lb[H * n:] == sentinel)
+    assert torch.all(wb[need:] == 0xA5) and torch.all(wb2[bneed:] == 0x5A)
+    for buf, _ in outs:
+        assert torch.all(buf[numel:] == sentinel)
+    assert torch.all(torch.isfinite(o.float()))
+
+
+def test_invalid_arguments_launch_nothing():
+    q, k, v, do = (t.to(DEV) for t in _synthetic(64, 128, seed=3))
+    p = B.problem_for(q, k, False, 0.1)
+    ws = torch.empty(B.attnqat_bwd_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    dq = torch.full_like(q, 7.0)
+    lse = torch.zeros(1, 1, 64, device=DEV)
+    with pytest.raises(B.AttnQatError) as e:
+        B.attnqat_bwd(p, q, k, v, q, do, lse, dq, torch.empty_like(k), torch.empty_like(v),
+                      ws[:100])
+    assert e.value.status == B.ERR_WORKSPACE_TOO_SMALL
+    base = torch.empty(64 * 128 + 8, dtype=torch.bfloat16, device=DEV)
+    mis = base[4:4 + 64 * 128].view(1, 1, 64, 128)  # 8-byte offset
+    with pytest.raises(B.AttnQatError) as e:
+        B.attnqat_bwd(p, q, k, v, q, do, lse, mis, torch.empty_like(k), torch.empty_like(v), ws)
+    assert e.value.status == B.ERR_MISALIGNED
+    torch.cuda.synchronize()
+    assert torch.all(dq == 7.0)
+    assert B.attnqat_check_device(torch.cuda.current_device()) == B.OK
