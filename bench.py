@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 fake-quantized attention QAT path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: attnqat_fwd (Q/K/V
+fake-quant + the QAT forward producing O_hp and lse) followed by
+attnqat_bwd on that output (Q fake-quant + delta, K/V fake-quant, dQ,
+dK/dV).  Inputs are resident in HBM before timing starts.
+
+The reported metric is the backward's throughput: counted backward work
+10*B*H*N^2*D (halved when causal) divided by the backward's own duration,
+measured with HIP events recorded by the library between its launches on
+the benchmark's stream (attnqat_bwd_timed); the same events give each
+kernel's average duration for the roofline entry.  Prints exactly one JSON
+line on stdout; human-readable details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QAT-attn bwd TFLOP/s & % bf16 MFMA peak, B1 H16 N4096 D128 non-causal"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEventCreate/ElapsedTime through the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.created = []
+
+    def array(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev
+            self.created.append(ev)
+        return arr
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for ev in self.created:
+            self.lib.hipEventDestroy(ev)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "nvfp4_fake_quantized_amd", "csrc", "*.h*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("source_digest") != digest:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, do):
+    """The oracle (fp64 NumPy) on one head of the same workload."""
+    from oracle.attention import qat_backward_full_head, qat_forward_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing or failing: fall back to the affinity set
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    o64, l64 = qat_forward_head(q[0, 0], k[0, 0], v[0, 0], w.softmax_scale, w.causal)
+    t1 = time.perf_counter()
+    import torch  # the backward's inputs as stored: O_hp in bf16, lse in fp32
+    o_in = torch.from_numpy(o64).to(torch.bfloat16)
+    l_in = torch.from_numpy(l64).float()
+    qat_backward_full_head(q[0, 0], k[0, 0], v[0, 0], o_in, do[0, 0], l_in, w.softmax_scale,
+                           w.causal)
+    t2 = time.perf_counter()
+    head_bwd_flops = w.bwd_flops() / (w.batch * w.heads)
+    return {
+        "value": head_bwd_flops / (t2 - t1) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one head (b=0,h=0) of {w.name} (N={w.seqlen}, D={w.head_dim}); oracle "
+                   f"backward {t2 - t1:.2f} s (after its forward, {t1 - t0:.2f} s), counted "
+                   f"{head_bwd_flops / 1e9:.1f} GFLOP; host has "
+                   f"{len(os.sched_getaffinity(0))} usable cores"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ref_shape")
+    ap.add_argument("--p-scale", type=float, default=1.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on a single GPU; multi-GPU runs are not part of this "
+              "build (the work shards over batch*heads with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from nvfp4_fake_quantized_amd import binding as B
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v, do = make_inputs(w)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    p = B.problem_for(qd, kd, w.causal, w.softmax_scale, args.p_scale)
+    wsf = torch.empty(B.attnqat_fwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(B.attnqat_bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    stream = torch.cuda.current_stream()
+    hip = HipEvents()
+    K, W = args.steps, args.warmup
+    evf = [hip.array(3) for _ in range(max(K, 1))]
+    evb = [hip.array(5) for _ in range(max(K, 1))]
+
+    def step(i):
+        B.attnqat_fwd_timed(p, qd, kd, vd, o, lse, wsf, evf[i % len(evf)], stream)
+        B.attnqat_bwd_timed(p, qd, kd, vd, o, dod, lse, dq, dk, dv, wsb, evb[i % len(evb)],
+                            stream)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    names_f = ["fwd_quant_qkv", "fwd_attention"]
+    names_b = ["bwd_quant_q_delta", "bwd_quant_kv", "bwd_dq", "bwd_dkdv"]
+    per = {n: 0.0 for n in names_f + names_b}
+    fwd_ms = bwd_ms = 0.0
+    for i in range(K):
+        for j, n in enumerate(names_f):
+            per[n] += hip.ms(evf[i][j], evf[i][j + 1]) / K
+        for j, n in enumerate(names_b):
+            per[n] += hip.ms(evb[i][j], evb[i][j + 1]) / K
+        fwd_ms += hip.ms(evf[i][0], evf[i][2]) / K
+        bwd_ms += hip.ms(evb[i][0], evb[i][4]) / K
+    hip.close()
+
+    if args.copy_calibration:
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)  # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    BH = w.batch * w.heads
+    N, D = w.seqlen, w.head_dim
+    half = 0.5 if w.causal else 1.0
+    bwd_tflops = w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
+    fwd_tflops = w.fwd_flops() / (fwd_ms * 1e-3) / 1e12
+    # algorithmic work of each kernel per launch (GEMM flops or HBM bytes)
+    elems = BH * N * D
+    work = {
+        "fwd_attention": ("mfma", 4.0 * BH * N * N * D * half),
+        "bwd_dq": ("mfma", 6.0 * BH * N * N * D * half),
+        "bwd_dkdv": ("mfma", 8.0 * BH * N * N * D * half),
+        "fwd_quant_qkv": ("hbm", 3 * elems * (4 + 1 / 16)),
+        "bwd_quant_q_delta": ("hbm", elems * (8 + 1 / 16) + BH * N * 4),
+        "bwd_quant_kv": ("hbm", 2 * elems * (4 + 1 / 16)),
+    }
+    dominant = max(per, key=per.get)
+    bound, amount = work[dominant]
+    kernel_name = {"fwd_attention": "k_fwd", "bwd_dq": "k_dq", "bwd_dkdv": "k_dkdv",
+                   "fwd_quant_qkv": "k_quant_bf16", "bwd_quant_q_delta": "k_quant_q_delta",
+                   "bwd_quant_kv": "k_quant_bf16"}[dominant]
+    secs = per[dominant] * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = amount / secs / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = amount / secs / 1e9, PEAK_HBM_GBS, "GB/s"
+    digest = source_digest()
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4),
+                "traffic": read_traffic(kernel_name, w.name, digest),
+                "kernel": kernel_name, "avg_launch_ms": round(per[dominant], 4),
+                "algorithmic_per_launch": amount}
+
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[receipt] device={props.name} arch={getattr(props, 'gcnArchName', '?')} "
+        f"CUs={props.multi_processor_count} workload={w.name} p_scale={args.p_scale} "
+        f"source={digest}")
+    for n in names_f + names_b:
+        log(f"  {n:20s} {per[n]:8.4f} ms")
+    log(f"  fwd {fwd_ms:.4f} ms ({fwd_tflops:.1f} TFLOP/s), bwd {bwd_ms:.4f} ms "
+        f"({bwd_tflops:.1f} TFLOP/s = {100 * bwd_tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(bwd_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round((t1 - t0) * 1e3 / max(K, 1), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.description, "batch": w.batch, "heads": w.heads,
+                   "seqlen": N, "head_dim": D, "causal": w.causal,
+                   "softmax_scale": w.softmax_scale, "p_scale": args.p_scale},
+        "pct_of_bf16_peak": round(100 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "bwd_ms": round(bwd_ms, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "kernels_ms": {n: round(per[n], 4) for n in names_f + names_b},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, do)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -152,6 +152,26 @@ ATTNQAT_API int attnqat_bwd(const attnqat_problem* p, const void* q, const void*
                             const float* lse, void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* Instrumented variants for measurement: identical work and results, plus
+ * hipEventRecord of caller-created events on `stream` around the kernel
+ * launches, so per-kernel durations can be read with hipEventElapsedTime
+ * without any synchronization inside the call.
+ * attnqat_fwd_timed: events[0] before the Q/K/V fake-quant kernel,
+ *   events[1] before the attention kernel, events[2] after it.
+ * attnqat_bwd_timed: events[0] before the Q fake-quant + delta kernel,
+ *   events[1] before the K/V fake-quant kernel, events[2] before the dQ
+ *   kernel, events[3] before the dK/dV kernel, events[4] after it.
+ * A NULL array or NULL event is ATTNQAT_ERR_INVALID_ARGUMENT. */
+ATTNQAT_API int attnqat_fwd_timed(const attnqat_problem* p, const void* q, const void* k,
+                                  const void* v, void* o_hp, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream,
+                                  hipEvent_t* events);
+ATTNQAT_API int attnqat_bwd_timed(const attnqat_problem* p, const void* q, const void* k,
+                                  const void* v, const void* o_hp, const void* d_o,
+                                  const float* lse, void* dq, void* dk, void* dv,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                  hipEvent_t* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,7 +48,7 @@ class attnqat_ws_layout(ctypes.Structure):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m nvfp4_fake_quantized_amd.csrc.build` (no fallback exists)")
+                      "`python nvfp4_fake_quantized_amd/csrc/build.py` (no fallback exists)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -69,6 +69,9 @@ _SIGS = {
     "attnqat_fwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "attnqat_bwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                    _vp]),
+    "attnqat_fwd_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "attnqat_bwd_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _sz, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -183,6 +186,22 @@ def attnqat_bwd(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspa
     _check(_lib.attnqat_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp), _ptr(d_o),
                             _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                             workspace.numel(), _stream(stream)), "attnqat_bwd")
+
+
+def attnqat_fwd_timed(p: attnqat_problem, q, k, v, o_hp, lse, workspace, events, stream=None):
+    """``events``: a ctypes array of 3 hipEvent_t handles (see the header)."""
+    _check(_lib.attnqat_fwd_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),
+                                  _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream),
+                                  events), "attnqat_fwd_timed")
+
+
+def attnqat_bwd_timed(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace,
+                      events, stream=None):
+    """``events``: a ctypes array of 5 hipEvent_t handles (see the header)."""
+    _check(_lib.attnqat_bwd_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),
+                                  _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _ptr(workspace), workspace.numel(), _stream(stream), events),
+           "attnqat_bwd_timed")
 
 
 # ---- conveniences (allocation via torch, then one C call) --------------------

@@ -157,9 +157,18 @@ int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_t* scales, i
   return e == hipSuccess ? ATTNQAT_OK : ATTNQAT_ERR_HIP;
 }
 
-int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
-                void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Records ev[i] on the stream when an event array is given.
+bool record(hipEvent_t* ev, int i, hipStream_t stream) {
+  return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess;
+}
+
+int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v, void* o_hp,
+            float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
+            hipEvent_t* ev) {
   int st = validate_problem(p);
   if (st != ATTNQAT_OK) return st;
   const void* ptrs[] = {q, k, v, o_hp, lse, workspace};
@@ -183,7 +192,9 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
       {k, kh, at<uint8_t>(workspace, L.k_scale), bh * p->seqlen_kv * D / 16},
       {v, vh, at<uint8_t>(workspace, L.v_scale), bh * p->seqlen_kv * D / 16},
   };
+  if (!record(ev, 0, stream)) return ATTNQAT_ERR_HIP;
   if (attnqat::launch_quant_bf16(jobs, 3, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  if (!record(ev, 1, stream)) return ATTNQAT_ERR_HIP;
 
   AttnArgs a = {};
   a.q_hat = qh;
@@ -198,12 +209,13 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
   a.softmax_scale = p->softmax_scale;
   a.p_scale = p->p_scale;
   if (attnqat::launch_fwd(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  if (!record(ev, 2, stream)) return ATTNQAT_ERR_HIP;
   return ATTNQAT_OK;
 }
 
-int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
-                const void* o_hp, const void* d_o, const float* lse, void* dq, void* dk,
-                void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+            const void* o_hp, const void* d_o, const float* lse, void* dq, void* dk, void* dv,
+            void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev) {
   int st = validate_problem(p);
   if (st != ATTNQAT_OK) return st;
   const void* ptrs[] = {q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace};
@@ -225,6 +237,7 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
   float* delta = at<float>(workspace, L.delta);
 
   // 1) Q fake-quantization fused with delta = rowsum(O_hp * dO)
+  if (!record(ev, 0, stream)) return ATTNQAT_ERR_HIP;
   if (attnqat::launch_quant_q_delta(static_cast<const uint16_t*>(q),
                                     static_cast<const uint16_t*>(o_hp),
                                     static_cast<const uint16_t*>(d_o), qh,
@@ -236,7 +249,9 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
       {k, kh, at<uint8_t>(workspace, L.k_scale), bh * p->seqlen_kv * D / 16},
       {v, vh, at<uint8_t>(workspace, L.v_scale), bh * p->seqlen_kv * D / 16},
   };
+  if (!record(ev, 1, stream)) return ATTNQAT_ERR_HIP;
   if (attnqat::launch_quant_bf16(jobs, 2, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  if (!record(ev, 2, stream)) return ATTNQAT_ERR_HIP;
 
   AttnArgs a = {};
   a.q_hat = qh;
@@ -256,8 +271,50 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
   a.p_scale = p->p_scale;
   // 3) dQ and 4) dK/dV
   if (attnqat::launch_bwd_dq(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  if (!record(ev, 3, stream)) return ATTNQAT_ERR_HIP;
   if (attnqat::launch_bwd_dkdv(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  if (!record(ev, 4, stream)) return ATTNQAT_ERR_HIP;
   return ATTNQAT_OK;
+}
+
+bool events_ok(const hipEvent_t* ev, int n) {
+  if (ev == nullptr) return false;
+  for (int i = 0; i < n; ++i)
+    if (ev[i] == nullptr) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  return run_fwd(p, q, k, v, o_hp, lse, workspace, workspace_bytes, stream, nullptr);
+}
+
+int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                const void* o_hp, const void* d_o, const float* lse, void* dq, void* dk,
+                void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_bwd(p, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace, workspace_bytes, stream,
+                 nullptr);
+}
+
+int attnqat_fwd_timed(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                      void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream, hipEvent_t* events) {
+  if (!events_ok(events, 3)) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  return run_fwd(p, q, k, v, o_hp, lse, workspace, workspace_bytes, stream, events);
+}
+
+int attnqat_bwd_timed(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                      const void* o_hp, const void* d_o, const float* lse, void* dq, void* dk,
+                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t* events) {
+  if (!events_ok(events, 5)) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  return run_bwd(p, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace, workspace_bytes, stream,
+                 events);
 }
 
 }  // extern "C"

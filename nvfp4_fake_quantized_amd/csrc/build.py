@@ -1,6 +1,7 @@
 """Builds libattnqat.so (HIP C++ for gfx950) next to the Python package.
 
-Usage: ``python -m nvfp4_fake_quantized_amd.csrc.build`` or ``build()``.
+Usage: ``python nvfp4_fake_quantized_amd/csrc/build.py`` (run it by path: the
+package itself loads the library on import) or ``build()``.
 Each translation unit is compiled in parallel, then linked into one shared
 library whose only exported symbols are the C ABI of include/attnqat.h.
 """

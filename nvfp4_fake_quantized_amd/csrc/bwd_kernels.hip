@@ -14,16 +14,20 @@
 // Layout choices (gfx950, wave64):
 //  * k_dq: each wave owns 32 queries (Q^ and dO rows in registers as B
 //    operands).  S^T and dP^T accumulators hold one query per lane, so dS^T
-//    feeds the B operand of dQ^T = K^T dS^T from registers; K^ is staged in
-//    LDS both row-major (A operand of S^T) and transposed (A of dQ^T).
+//    feeds the B operand of dQ^T = K^T dS^T from registers; K^ and V^ tiles
+//    are staged row-major in double-buffered LDS (prefetched one tile ahead
+//    through registers) and the K^T operand is read with LDS transpose reads.
 //  * k_dkdv: each wave owns 32 keys.  Its K^ and V^ rows sit in registers as
 //    A operands with the row order permuted so that, in the S^T accumulator,
 //    each lane holds one query and 16 *consecutive* keys: exactly one P
 //    quantization group.  The group amax, the E4M3 scale and the E2M1
-//    rounding are then per-lane work with no cross-lane reduction.  P^F and
-//    dS go through a per-wave LDS transpose ([key][query]) to become the A
-//    operands of dV = P^F^T dO and dK = dS^T Q^; dO and Q^ are staged in LDS
-//    both row-major and transposed ([d][query]).
+//    rounding are then per-lane work with no cross-lane reduction (the
+//    rounding uses the hardware FP4 conversion on an FMA-refined quotient).
+//    P^F and dS are written as [query][key] rows of per-wave LDS tiles and
+//    read back with LDS transpose reads as the A operands of dV = P^F^T dO
+//    and dK = dS^T Q^; the B operands (dO and Q^ with lanes over d) come the
+//    same way from the row-major, double-buffered Q^/dO tiles.
+//  * Only tiles on a boundary (tails, causal diagonal) evaluate masks.
 //  * Causal: tiles entirely above the diagonal are skipped per wave; the
 //    diagonal tile keeps the elementwise key <= query mask.  Tails: keys >= Nkv
 //    and queries >= Nq get P = 0 (so a short last P group is zero-padded),
@@ -38,7 +42,7 @@ namespace attnqat {
 namespace {
 
 constexpr int kDqBM = 128;    // queries per workgroup (k_dq)
-constexpr int kDqBN = 64;     // keys per tile (k_dq)
+constexpr int kDqBN = 32;     // keys per tile (k_dq)
 constexpr int kDkvBN = 128;   // keys per workgroup (k_dkdv)
 constexpr int kDkvBM = 32;    // queries per tile (k_dkdv)
 
@@ -46,16 +50,60 @@ __device__ __forceinline__ u32x4 ld_u32x4(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <int D>
+// One 32-key tile of k_dq for one wave (32 queries).
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void dq_tile(const bf16x8* qf, const bf16x8* df, f32x16* acc,
+                                        const uint16_t* sKb, const uint16_t* sVb, int k0, int qi,
+                                        bool qok, int nkv, float lse2, float dl, float sl2,
+                                        int lane) {
+  constexpr int KB = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int SK = D + 8;
+  const int h = lane >> 5, l32 = lane & 31;
+  f32x16 s = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int off = l32 * SK + 16 * kb + 8 * h;
+    s = mfma32x32x16(ld_bf16x8(sKb + off), qf[kb], s);
+    dp = mfma32x32x16(ld_bf16x8(sVb + off), df[kb], dp);
+  }
+  float ds[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float x = __builtin_fmaf(s[v], sl2, -lse2);
+    if (MASK) {
+      const int key = k0 + 8 * (v >> 2) + 4 * h + (v & 3);
+      const bool ok = qok && key < nkv && (!CAUSAL || key <= qi);
+      x = ok ? x : -INFINITY;
+    }
+    ds[v] = fast_exp2(x) * (dp[v] - dl);
+  }
+  // dQ^T += K^T dS^T over two 16-key k-blocks: lane half h, element e of
+  // k-block kh holds key 16*kh + 8*(e/4) + 4h + e%4 in both operands.
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const u32x4 bw = {pack_bf16x2(ds[8 * kh], ds[8 * kh + 1]),
+                      pack_bf16x2(ds[8 * kh + 2], ds[8 * kh + 3]),
+                      pack_bf16x2(ds[8 * kh + 4], ds[8 * kh + 5]),
+                      pack_bf16x2(ds[8 * kh + 6], ds[8 * kh + 7])};
+    const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
+    const int r0 = 16 * kh + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      acc[db] = mfma32x32x16(lds_operand_cols(sKb, SK, 32 * db, r0, r0 + 8, lane), b, acc[db]);
+  }
+}
+
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void k_dq(AttnArgs a) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int BN = kDqBN;
-  constexpr int SK = D + 8;    // row stride of sK / sV
-  constexpr int SKT = BN + 4;  // row stride of sKt
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * SK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * SK];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * SKT];
+  constexpr int SK = D + 8;          // row stride of sK / sV
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int CH = BN * CPR / 256;  // chunks per thread per tensor per tile
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * SK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * SK];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -84,72 +132,54 @@ __global__ __launch_bounds__(256) void k_dq(AttnArgs a) {
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
-  const int kend = a.causal ? min(nkv, qblk0 + kDqBM) : nkv;
+  // keys above the workgroup's last query are masked (causal)
+  const int kend = CAUSAL ? min(nkv, qblk0 + kDqBM) : nkv;
+  const int ntiles = (kend + BN - 1) / BN;
 
-  for (int k0 = 0; k0 < kend; k0 += BN) {
-    __syncthreads();
-    for (int c = tid; c < BN * D / 8; c += 256) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+  u32x4 rk[CH], rv[CH];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 256 * c;
+      const int r = idx / CPR, col = (idx % CPR) * 8;
       const int key = k0 + r;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < nkv) {
-        kv = ld_u32x4(K + (size_t)key * D + col);
-        vv = ld_u32x4(V + (size_t)key * D + col);
-      }
-      *reinterpret_cast<u32x4*>(&sK[r * SK + col]) = kv;
-      *reinterpret_cast<u32x4*>(&sV[r * SK + col]) = vv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sKt[(col + 2 * e) * SKT + r] = (uint16_t)(kv[e] & 0xFFFFu);
-        sKt[(col + 2 * e + 1) * SKT + r] = (uint16_t)(kv[e] >> 16);
-      }
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      rk[c] = key < nkv ? ld_u32x4(K + (size_t)key * D + col) : z;
+      rv[c] = key < nkv ? ld_u32x4(V + (size_t)key * D + col) : z;
     }
-    __syncthreads();
-    if (a.causal && qw0 + 31 < k0) continue;
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 256 * c;
+      const int r = idx / CPR, col = (idx % CPR) * 8;
+      *reinterpret_cast<u32x4*>(&sK[buf][r * SK + col]) = rk[c];
+      *reinterpret_cast<u32x4*>(&sV[buf][r * SK + col]) = rv[c];
+    }
+  };
 
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      s[nb] = zero_f32x16();
-      dp[nb] = zero_f32x16();
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int off = (32 * nb + l32) * SK + 16 * kb + 8 * h;
-        s[nb] = mfma32x32x16(ld_bf16x8(&sK[off]), qf[kb], s[nb]);
-        dp[nb] = mfma32x32x16(ld_bf16x8(&sV[off]), df[kb], dp[nb]);
-      }
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int k0 = it * BN;
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(k0 + BN);
+    const bool active = !(CAUSAL && qw0 + 31 < k0);  // every key above every row
+    if (active) {
+      const bool mask = (k0 + BN > nkv) || (qw0 + 32 > nq) || (CAUSAL && k0 + BN - 1 > qw0);
+      if (mask)
+        dq_tile<D, CAUSAL, true>(qf, df, acc, sK[buf], sV[buf], k0, qi, qok, nkv, lse2, dl,
+                                 sl2, lane);
+      else
+        dq_tile<D, CAUSAL, false>(qf, df, acc, sK[buf], sV[buf], k0, qi, qok, nkv, lse2, dl,
+                                  sl2, lane);
     }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = k0 + 32 * nb + 8 * (v >> 2) + 4 * h + (v & 3);
-        const bool ok = qok && key < nkv && (!a.causal || key <= qi);
-        const float p = ok ? fast_exp2(s[nb][v] * sl2 - lse2) : 0.0f;
-        s[nb][v] = p * (dp[nb][v] - dl);  // dS
-      }
-    }
-    // dQ^T += K^T dS^T over four 16-key k-blocks (key mapping as in the
-    // forward: lane half h, element e -> 16*kblk + 8*(e/4) + 4h + e%4).
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        float dsv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dsv[e] = s[nb][8 * kh + e];
-        const bf16x8 b = pack_bf16x8(dsv);
-        const int kb0 = 32 * nb + 16 * kh + 4 * h;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint16_t* row = &sKt[(32 * db + l32) * SKT];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row + kb0);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + kb0 + 8);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), b, acc[db]);
-        }
-      }
-    }
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   if (qok) {
@@ -159,11 +189,8 @@ __global__ __launch_bounds__(256) void k_dq(AttnArgs a) {
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const uint32_t w0 = f32_to_bf16_bits(acc[db][4 * g4] * sc) |
-                            (f32_to_bf16_bits(acc[db][4 * g4 + 1] * sc) << 16);
-        const uint32_t w1 = f32_to_bf16_bits(acc[db][4 * g4 + 2] * sc) |
-                            (f32_to_bf16_bits(acc[db][4 * g4 + 3] * sc) << 16);
-        const u32x2 w = {w0, w1};
+        const u32x2 w = {pack_bf16x2(acc[db][4 * g4] * sc, acc[db][4 * g4 + 1] * sc),
+                         pack_bf16x2(acc[db][4 * g4 + 2] * sc, acc[db][4 * g4 + 3] * sc)};
         *reinterpret_cast<u32x2*>(out + 32 * db + 8 * g4 + 4 * h) = w;
       }
     }
@@ -177,22 +204,91 @@ __device__ __forceinline__ int key_perm(int r) {
   return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 }
 
-template <int D>
+// One 32-query tile of k_dkdv for one wave (32 keys).  MASK selects the
+// boundary version (tails, causal diagonal); interior tiles skip all masking.
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void dkdv_tile(const bf16x8* kf, const bf16x8* vf, f32x16* dk,
+                                          f32x16* dv, const uint16_t* sQb, const uint16_t* sdOb,
+                                          const float* sLseb, const float* sDlb, uint16_t* myPF,
+                                          uint16_t* myDS, int q0, int kw0, int nq, int nkv,
+                                          float sl2, float psc, int lane) {
+  constexpr int KB = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int SQ = D + 8;
+  constexpr int SP = 40;
+  const int h = lane >> 5, l32 = lane & 31;
+  f32x16 s = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int off = l32 * SQ + 16 * kb + 8 * h;
+    s = mfma32x32x16(kf[kb], ld_bf16x8(sQb + off), s);
+    dp = mfma32x32x16(vf[kb], ld_bf16x8(sdOb + off), dp);
+  }
+  // this lane: query q0 + l32, keys kw0 + 16h + v (v = 0..15)
+  const int qj = q0 + l32;
+  const float lse2 = sLseb[l32];
+  const float dl = sDlb[l32];
+  float p[16], ds[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float x = __builtin_fmaf(s[v], sl2, -lse2);
+    if (MASK) {
+      const int key = kw0 + 16 * h + v;
+      const bool ok = qj < nq && key < nkv && (!CAUSAL || key <= qj);
+      x = ok ? x : -INFINITY;
+    }
+    const float pv = fast_exp2(x);
+    ds[v] = pv * (dp[v] - dl);
+    p[v] = pv * psc;
+    amax = fmaxf(amax, p[v]);
+  }
+  const FastP fq(e4m3_scale_from_amax(amax));
+  u32x4 pf[2], dsb[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float y0, y1;
+    fq.pair(p[2 * i], p[2 * i + 1], y0, y1);
+    pf[i >> 2][i & 3] = pack_bf16x2(y0, y1);
+    dsb[i >> 2][i & 3] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+  }
+  // P^F and dS as rows [query][key] of this wave's transposition tiles
+  *reinterpret_cast<u32x4*>(myPF + l32 * SP + 16 * h) = pf[0];
+  *reinterpret_cast<u32x4*>(myPF + l32 * SP + 16 * h + 8) = pf[1];
+  *reinterpret_cast<u32x4*>(myDS + l32 * SP + 16 * h) = dsb[0];
+  *reinterpret_cast<u32x4*>(myDS + l32 * SP + 16 * h + 8) = dsb[1];
+  wave_lds_fence();
+  // dV += P^F^T dO and dK += dS^T Q^: A operands are key columns of the
+  // [query][key] tiles, B operands are d columns of the [query][d] tiles.
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq) {
+    const int r0 = 16 * kq + 8 * h;
+    const bf16x8 ap = lds_operand_cols(myPF, SP, 0, r0, r0 + 4, lane);
+    const bf16x8 as = lds_operand_cols(myDS, SP, 0, r0, r0 + 4, lane);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dv[db] = mfma32x32x16(ap, lds_operand_cols(sdOb, SQ, 32 * db, r0, r0 + 4, lane), dv[db]);
+      dk[db] = mfma32x32x16(as, lds_operand_cols(sQb, SQ, 32 * db, r0, r0 + 4, lane), dk[db]);
+    }
+  }
+  wave_lds_fence();
+}
+
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void k_dkdv(AttnArgs a) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int BM = kDkvBM;
-  constexpr int SQ = D + 8;    // row stride of sQ / sdO
-  constexpr int SQT = BM + 8;  // row stride of sQt / sdOt
-  constexpr int SP = BM + 8;   // row stride of the per-wave transpose buffers
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[BM * SQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[BM * SQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * SQT];
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[D * SQT];
-  __shared__ __attribute__((aligned(16))) uint16_t sPt[4 * 32 * SP];
-  __shared__ __attribute__((aligned(16))) uint16_t sSt[4 * 32 * SP];
-  __shared__ float sLse[BM];
-  __shared__ float sDl[BM];
+  constexpr int SQ = D + 8;         // row stride of sQ / sdO
+  constexpr int SP = 40;            // row stride of the per-wave [query][key] tiles
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int CH = BM * CPR / 256;  // chunks per thread per tensor per tile
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BM * SQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BM * SQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sPF[4][BM * SP];
+  __shared__ __attribute__((aligned(16))) uint16_t sDS[4][BM * SP];
+  __shared__ float sLse[2][BM];
+  __shared__ float sDl[2][BM];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -226,84 +322,66 @@ __global__ __launch_bounds__(256) void k_dkdv(AttnArgs a) {
   }
   const float sl2 = a.softmax_scale * kLog2e;
   const float psc = a.p_scale;
-  uint16_t* myPt = &sPt[wave * 32 * SP];
-  uint16_t* mySt = &sSt[wave * 32 * SP];
-  // queries below the workgroup's first key are fully masked when causal
-  const int qstart = a.causal ? (kblk0 / BM) * BM : 0;
 
-  for (int q0 = qstart; q0 < nq; q0 += BM) {
-    __syncthreads();
-    for (int c = tid; c < BM * D / 8; c += 256) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int qq = q0 + r;
-      u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = {0u, 0u, 0u, 0u};
-      if (qq < nq) {
-        qv = ld_u32x4(Q + (size_t)qq * D + col);
-        dv4 = ld_u32x4(dO + (size_t)qq * D + col);
-      }
-      *reinterpret_cast<u32x4*>(&sQ[r * SQ + col]) = qv;
-      *reinterpret_cast<u32x4*>(&sdO[r * SQ + col]) = dv4;
+  // query tiles: below the workgroup's first key everything is masked (causal)
+  const int qfirst = CAUSAL ? kblk0 : 0;
+  const int ntiles = qfirst < nq ? (nq - qfirst + BM - 1) / BM : 0;
+
+  u32x4 rq[CH], rd[CH];
+  float rl = 0.0f, rdl = 0.0f;
+  auto load_tile = [&](int q0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sQt[(col + 2 * e) * SQT + r] = (uint16_t)(qv[e] & 0xFFFFu);
-        sQt[(col + 2 * e + 1) * SQT + r] = (uint16_t)(qv[e] >> 16);
-        sdOt[(col + 2 * e) * SQT + r] = (uint16_t)(dv4[e] & 0xFFFFu);
-        sdOt[(col + 2 * e + 1) * SQT + r] = (uint16_t)(dv4[e] >> 16);
-      }
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 256 * c;
+      const int r = idx / CPR, col = (idx % CPR) * 8;
+      const int qq = q0 + r;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      rq[c] = qq < nq ? ld_u32x4(Q + (size_t)qq * D + col) : z;
+      rd[c] = qq < nq ? ld_u32x4(dO + (size_t)qq * D + col) : z;
     }
     if (tid < BM) {
       const int qq = q0 + tid;
-      sLse[tid] = qq < nq ? LSE[qq] * kLog2e : 0.0f;
-      sDl[tid] = qq < nq ? DL[qq] : 0.0f;
+      rl = qq < nq ? LSE[qq] * kLog2e : 0.0f;
+      rdl = qq < nq ? DL[qq] : 0.0f;
     }
-    __syncthreads();
-    // every query of the tile is below this wave's first key: fully masked
-    const bool active = !(a.causal && q0 + BM - 1 < kw0);
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 256 * c;
+      const int r = idx / CPR, col = (idx % CPR) * 8;
+      *reinterpret_cast<u32x4*>(&sQ[buf][r * SQ + col]) = rq[c];
+      *reinterpret_cast<u32x4*>(&sdO[buf][r * SQ + col]) = rd[c];
+    }
+    if (tid < BM) {
+      sLse[buf][tid] = rl;
+      sDl[buf][tid] = rdl;
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(qfirst);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int q0 = qfirst + it * BM;
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(q0 + BM);
+    // every query of the tile below this wave's first key: nothing to do
+    const bool active = !(CAUSAL && q0 + BM - 1 < kw0);
     if (active) {
-      f32x16 s = zero_f32x16(), dp = zero_f32x16();
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int off = l32 * SQ + 16 * kb + 8 * h;
-        s = mfma32x32x16(kf[kb], ld_bf16x8(&sQ[off]), s);
-        dp = mfma32x32x16(vf[kb], ld_bf16x8(&sdO[off]), dp);
-      }
-      // this lane: query q0 + l32, keys kw0 + 16h + v (v = 0..15)
-      const int qj = q0 + l32;
-      const float lse2 = sLse[l32];
-      const float dl = sDl[l32];
-      float pq[16];
-      float amax = 0.0f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = kw0 + 16 * h + v;
-        const bool ok = qj < nq && key < nkv && (!a.causal || key <= qj);
-        const float p = ok ? fast_exp2(s[v] * sl2 - lse2) : 0.0f;
-        s[v] = p * (dp[v] - dl);  // dS
-        pq[v] = p * psc;
-        amax = fmaxf(amax, pq[v]);
-      }
-      const float sc = e4m3_scale_from_amax(amax);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kr = (16 * h + v) * SP + l32;
-        myPt[kr] = (uint16_t)f32_to_bf16_bits(e2m1_dequant(pq[v], sc));
-        mySt[kr] = (uint16_t)f32_to_bf16_bits(s[v]);
-      }
+      const bool mask = (q0 + BM > nq) || (kw0 + 32 > nkv) || (CAUSAL && q0 < kw0 + 31);
+      if (mask)
+        dkdv_tile<D, CAUSAL, true>(kf, vf, dk, dv, sQ[buf], sdO[buf], sLse[buf], sDl[buf],
+                                   sPF[wave], sDS[wave], q0, kw0, nq, nkv, sl2, psc, lane);
+      else
+        dkdv_tile<D, CAUSAL, false>(kf, vf, dk, dv, sQ[buf], sdO[buf], sLse[buf], sDl[buf],
+                                    sPF[wave], sDS[wave], q0, kw0, nq, nkv, sl2, psc, lane);
     }
+    if (has_next) store_tile(buf ^ 1);
     __syncthreads();
-    if (active) {
-#pragma unroll
-      for (int kq = 0; kq < BM / 16; ++kq) {
-        const bf16x8 ap = ld_bf16x8(&myPt[l32 * SP + 16 * kq + 8 * h]);
-        const bf16x8 as = ld_bf16x8(&mySt[l32 * SP + 16 * kq + 8 * h]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int off = (32 * db + l32) * SQT + 16 * kq + 8 * h;
-          dv[db] = mfma32x32x16(ap, ld_bf16x8(&sdOt[off]), dv[db]);
-          dk[db] = mfma32x32x16(as, ld_bf16x8(&sQt[off]), dk[db]);
-        }
-      }
-    }
   }
 
   // dK / dV accumulators: lane -> d = 32*db + l32, VGPR v -> key kw0 + 8*(v/4) + 4h + v%4
@@ -328,19 +406,33 @@ __global__ __launch_bounds__(256) void k_dkdv(AttnArgs a) {
 
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid((a.nq + kDqBM - 1) / kDqBM, a.bh);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(k_dq<128>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_dq<64>, grid, dim3(256), 0, stream, a);
+  if (head_dim == 128) {
+    if (a.causal)
+      hipLaunchKernelGGL((k_dq<128, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_dq<128, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (a.causal)
+      hipLaunchKernelGGL((k_dq<64, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_dq<64, false>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid((a.nkv + kDkvBN - 1) / kDkvBN, a.bh);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(k_dkdv<128>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_dkdv<64>, grid, dim3(256), 0, stream, a);
+  if (head_dim == 128) {
+    if (a.causal)
+      hipLaunchKernelGGL((k_dkdv<128, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_dkdv<128, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (a.causal)
+      hipLaunchKernelGGL((k_dkdv<64, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_dkdv<64, false>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

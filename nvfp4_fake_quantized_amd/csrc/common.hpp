@@ -84,6 +84,77 @@ __device__ __forceinline__ float e2m1_dequant(float x, float s) {
   return __builtin_copysignf(c * s, x);
 }
 
+// Faster exact path for non-negative fp32 values (the probabilities P), used
+// where the scale is shared by the 16 values one lane holds:
+//   q  = |x|/s refined from q0 = x * rcp(s) by one FMA residual step
+//        (q0 + (x - q0*s) * rcp(s)),
+//   c  = RNE_E2M1(q) by the hardware FP4 conversion (scale 1: no scaling;
+//        ties to even, saturating at 6), converted back to fp32,
+//   x^ = c * s.
+// For every E4M3 scale s and every fp32 x in [0.2 s, 8 s) the code c equals
+// the exact comparison result of e2m1_dequant (checked exhaustively on gfx950;
+// below 0.2 s both give 0 and at or above 8 s both saturate at 6).  s == 0
+// uses rcp 0 and yields 0.
+struct FastP {
+  float s, r;
+  __device__ __forceinline__ explicit FastP(float scale)
+      : s(scale), r(scale > 0.0f ? __builtin_amdgcn_rcpf(scale) : 0.0f) {}
+  // quantize-dequantize a pair (x0, x1 >= 0)
+  __device__ __forceinline__ void pair(float x0, float x1, float& y0, float& y1) const {
+    const float a0 = x0 * r, a1 = x1 * r;
+    const float q0 = __builtin_fmaf(__builtin_fmaf(-a0, s, x0), r, a0);
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-a1, s, x1), r, a1);
+    const uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q0, q1, 1.0f, 0);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 0);
+    y0 = c[0] * s;
+    y1 = c[1] * s;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// LDS transpose reads (ds_read_b64_tr_b16).
+//
+// Within each group of 16 lanes, source lane j supplies the address of 4
+// consecutive 16-bit elements; result lane i receives element (i % 4) of
+// source lanes 4e + i/4 for e = 0..3.  When source lane j points at row
+// r0 + j/4, columns c0 + 4*(j%4) .. +3 of a row-major tile, lane i receives
+// column c0 + i of rows r0 .. r0+3: a column read.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// A 32x32x16 MFMA operand whose lanes index columns of a row-major LDS tile:
+// lane l gets column col0 + l%32 of rows r0 + 0..3 (elements 0..3) and
+// r1 + 0..3 (elements 4..7), where r0, r1 may depend on h = l/32.
+__device__ __forceinline__ bf16x8 lds_operand_cols(const uint16_t* tile, int ld, int col0, int r0,
+                                                   int r1, int lane) {
+  const int j = lane & 15;
+  const int col = col0 + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
+  const u32x2 lo = lds_read_tr16(tile + (r0 + (j >> 2)) * ld + col);
+  const u32x2 hi = lds_read_tr16(tile + (r1 + (j >> 2)) * ld + col);
+  const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// bf16 pair from two floats (round to nearest even), packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Compiler-level ordering point for LDS traffic exchanged between the lanes
+// of one wave (LDS operations of a wave complete in issue order).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
 // MFMA (bf16 in, fp32 accumulate).
 //

