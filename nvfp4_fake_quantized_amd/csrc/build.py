@@ -52,13 +52,14 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False, extra_flags=(), out_dir: str | None = None) -> str:
     """Compiles every HIP source and links ``libattnqat.so`` into the package
-    directory; returns its path.  Always rebuilds."""
+    directory (or ``out_dir``); returns its path.  Always rebuilds.
+    ``extra_flags`` are passed to every compile (e.g. -DATTNQAT_FWD_BN=64)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    out = os.path.join(PKG, LIB_NAME)
+    out = os.path.join(out_dir or PKG, LIB_NAME)
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

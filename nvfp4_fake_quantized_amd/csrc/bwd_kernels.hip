@@ -15,8 +15,9 @@
 //  * k_dq: each wave owns 32 queries (Q^ and dO rows in registers as B
 //    operands).  S^T and dP^T accumulators hold one query per lane, so dS^T
 //    feeds the B operand of dQ^T = K^T dS^T from registers; K^ and V^ tiles
-//    are staged row-major in double-buffered LDS (prefetched one tile ahead
-//    through registers) and the K^T operand is read with LDS transpose reads.
+//    are staged row-major in double-buffered, XOR-swizzled LDS (prefetched
+//    one tile ahead through registers) and the K^T operand is read with LDS
+//    transpose reads.
 //  * k_dkdv: each wave owns 32 keys.  Its K^ and V^ rows sit in registers as
 //    A operands with the row order permuted so that, in the S^T accumulator,
 //    each lane holds one query and 16 *consecutive* keys: exactly one P
@@ -41,31 +42,33 @@ namespace attnqat {
 
 namespace {
 
-constexpr int kDqBM = 128;    // queries per workgroup (k_dq)
-constexpr int kDqBN = 32;     // keys per tile (k_dq)
-constexpr int kDkvBN = 128;   // keys per workgroup (k_dkdv)
-constexpr int kDkvBM = 32;    // queries per tile (k_dkdv)
+constexpr int kDqBM = 128;              // queries per workgroup (k_dq)
+constexpr int kDqBN = ATTNQAT_DQ_BN;      // keys per staged tile (k_dq; 32-key sub-tiles)
+constexpr int kDkvBN = 128;             // keys per workgroup (k_dkdv)
+constexpr int kDkvBM = ATTNQAT_DKDV_BM;   // queries per staged tile (k_dkdv; 32-query sub-tiles)
 
 __device__ __forceinline__ u32x4 ld_u32x4(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// One 32-key tile of k_dq for one wave (32 queries).
+// ---------------------------------------------------------------------------
+// dQ
+
+// One 32-key sub-tile of k_dq for one wave (32 queries).
 template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dq_tile(const bf16x8* qf, const bf16x8* df, f32x16* acc,
-                                        const uint16_t* sKb, const uint16_t* sVb, int k0, int qi,
-                                        bool qok, int nkv, float lse2, float dl, float sl2,
-                                        int lane) {
+                                        const uint16_t* sKb, const uint16_t* sVb,
+                                        const RowOffsets<D>& ro, const ColOffsets<D>& co, int k0,
+                                        int qi, bool qok, int nkv, float lse2, float dl,
+                                        float sl2, int lane) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
-  constexpr int SK = D + 8;
   const int h = lane >> 5, l32 = lane & 31;
   f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    const int off = l32 * SK + 16 * kb + 8 * h;
-    s = mfma32x32x16(ld_bf16x8(sKb + off), qf[kb], s);
-    dp = mfma32x32x16(ld_bf16x8(sVb + off), df[kb], dp);
+    s = mfma32x32x16(ld_bf16x8(sKb + ro.o[kb]), qf[kb], s);
+    dp = mfma32x32x16(ld_bf16x8(sVb + ro.o[kb]), df[kb], dp);
   }
   float ds[16];
 #pragma unroll
@@ -87,23 +90,24 @@ __device__ __forceinline__ void dq_tile(const bf16x8* qf, const bf16x8* df, f32x
                       pack_bf16x2(ds[8 * kh + 4], ds[8 * kh + 5]),
                       pack_bf16x2(ds[8 * kh + 6], ds[8 * kh + 7])};
     const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-    const int r0 = 16 * kh + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      acc[db] = mfma32x32x16(lds_operand_cols(sKb, SK, 32 * db, r0, r0 + 8, lane), b, acc[db]);
+      acc[db] = mfma32x32x16(lds_operand_cols_at(sKb + 16 * kh * D, co.a[db], co.b[db]), b,
+                             acc[db]);
   }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void k_dq(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_DQ_WAVES, 8)))
+void k_dq(AttnArgs a) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int BN = kDqBN;
-  constexpr int SK = D + 8;          // row stride of sK / sV
-  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int CH = BN * CPR / 256;  // chunks per thread per tensor per tile
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * SK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * SK];
+  static_assert(BN % 32 == 0 && CH >= 1, "key tile must be whole 32-key sub-tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];  // swizzled rows
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -128,6 +132,9 @@ __global__ __launch_bounds__(256) void k_dq(AttnArgs a) {
   const float lse2 = qok ? a.lse[(size_t)bh * nq + qi] * kLog2e : 0.0f;
   const float dl = qok ? a.delta[(size_t)bh * nq + qi] : 0.0f;
   const float sl2 = a.softmax_scale * kLog2e;
+  // LDS offsets: row reads of K^/V^ and K^T column reads (k-block rows 4h.., 4h+8..)
+  const RowOffsets<D> ro(lane);
+  const ColOffsets<D> co(4 * h, 4 * h + 8, lane);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -153,8 +160,8 @@ __global__ __launch_bounds__(256) void k_dq(AttnArgs a) {
     for (int c = 0; c < CH; ++c) {
       const int idx = tid + 256 * c;
       const int r = idx / CPR, col = (idx % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&sK[buf][r * SK + col]) = rk[c];
-      *reinterpret_cast<u32x4*>(&sV[buf][r * SK + col]) = rv[c];
+      *reinterpret_cast<u32x4*>(&sK[buf][swz<D>(r, col)]) = rk[c];
+      *reinterpret_cast<u32x4*>(&sV[buf][swz<D>(r, col)]) = rv[c];
     }
   };
 
@@ -168,15 +175,21 @@ __global__ __launch_bounds__(256) void k_dq(AttnArgs a) {
     const int k0 = it * BN;
     const bool has_next = it + 1 < ntiles;
     if (has_next) load_tile(k0 + BN);
-    const bool active = !(CAUSAL && qw0 + 31 < k0);  // every key above every row
-    if (active) {
-      const bool mask = (k0 + BN > nkv) || (qw0 + 32 > nq) || (CAUSAL && k0 + BN - 1 > qw0);
-      if (mask)
-        dq_tile<D, CAUSAL, true>(qf, df, acc, sK[buf], sV[buf], k0, qi, qok, nkv, lse2, dl,
-                                 sl2, lane);
-      else
-        dq_tile<D, CAUSAL, false>(qf, df, acc, sK[buf], sV[buf], k0, qi, qok, nkv, lse2, dl,
-                                  sl2, lane);
+#pragma unroll
+    for (int sub = 0; sub < BN / 32; ++sub) {
+      const int ks = k0 + 32 * sub;
+      const bool active = !(CAUSAL && qw0 + 31 < ks);  // every key above every row
+      if (active) {
+        const uint16_t* kb = sK[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
+        const uint16_t* vb = sV[buf] + 32 * sub * D;
+        const bool mask = (ks + 32 > nkv) || (qw0 + 32 > nq) || (CAUSAL && ks + 31 > qw0);
+        if (mask)
+          dq_tile<D, CAUSAL, true>(qf, df, acc, kb, vb, ro, co, ks, qi, qok, nkv, lse2, dl, sl2,
+                                   lane);
+        else
+          dq_tile<D, CAUSAL, false>(qf, df, acc, kb, vb, ro, co, ks, qi, qok, nkv, lse2, dl, sl2,
+                                    lane);
+      }
     }
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
@@ -197,6 +210,9 @@ __global__ __launch_bounds__(256) void k_dq(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK / dV
+
 // Row r of a wave's 32-key MFMA A operand holds key pi(r) so that the S^T
 // accumulator (rows 8*(v/4) + 4h + v%4 in VGPR v of lane half h) holds key
 // 16h + v: one contiguous 16-key group per lane.
@@ -204,25 +220,24 @@ __device__ __forceinline__ int key_perm(int r) {
   return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 }
 
-// One 32-query tile of k_dkdv for one wave (32 keys).  MASK selects the
+// One 32-query sub-tile of k_dkdv for one wave (32 keys).  MASK selects the
 // boundary version (tails, causal diagonal); interior tiles skip all masking.
 template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkdv_tile(const bf16x8* kf, const bf16x8* vf, f32x16* dk,
                                           f32x16* dv, const uint16_t* sQb, const uint16_t* sdOb,
                                           const float* sLseb, const float* sDlb, uint16_t* myPF,
-                                          uint16_t* myDS, int q0, int kw0, int nq, int nkv,
+                                          uint16_t* myDS, const RowOffsets<D>& ro,
+                                          const ColOffsets<D>& co, const ColOffsets<32>& cp,
+                                          int pw0, int pw1, int q0, int kw0, int nq, int nkv,
                                           float sl2, float psc, int lane) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
-  constexpr int SQ = D + 8;
-  constexpr int SP = 40;
   const int h = lane >> 5, l32 = lane & 31;
   f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    const int off = l32 * SQ + 16 * kb + 8 * h;
-    s = mfma32x32x16(kf[kb], ld_bf16x8(sQb + off), s);
-    dp = mfma32x32x16(vf[kb], ld_bf16x8(sdOb + off), dp);
+    s = mfma32x32x16(kf[kb], ld_bf16x8(sQb + ro.o[kb]), s);
+    dp = mfma32x32x16(vf[kb], ld_bf16x8(sdOb + ro.o[kb]), dp);
   }
   // this lane: query q0 + l32, keys kw0 + 16h + v (v = 0..15)
   const int qj = q0 + l32;
@@ -252,41 +267,43 @@ __device__ __forceinline__ void dkdv_tile(const bf16x8* kf, const bf16x8* vf, f3
     pf[i >> 2][i & 3] = pack_bf16x2(y0, y1);
     dsb[i >> 2][i & 3] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
   }
-  // P^F and dS as rows [query][key] of this wave's transposition tiles
-  *reinterpret_cast<u32x4*>(myPF + l32 * SP + 16 * h) = pf[0];
-  *reinterpret_cast<u32x4*>(myPF + l32 * SP + 16 * h + 8) = pf[1];
-  *reinterpret_cast<u32x4*>(myDS + l32 * SP + 16 * h) = dsb[0];
-  *reinterpret_cast<u32x4*>(myDS + l32 * SP + 16 * h + 8) = dsb[1];
+  // P^F and dS as rows [query][key] of this wave's (swizzled) tiles
+  *reinterpret_cast<u32x4*>(myPF + pw0) = pf[0];
+  *reinterpret_cast<u32x4*>(myPF + pw1) = pf[1];
+  *reinterpret_cast<u32x4*>(myDS + pw0) = dsb[0];
+  *reinterpret_cast<u32x4*>(myDS + pw1) = dsb[1];
   wave_lds_fence();
   // dV += P^F^T dO and dK += dS^T Q^: A operands are key columns of the
   // [query][key] tiles, B operands are d columns of the [query][d] tiles.
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq) {
-    const int r0 = 16 * kq + 8 * h;
-    const bf16x8 ap = lds_operand_cols(myPF, SP, 0, r0, r0 + 4, lane);
-    const bf16x8 as = lds_operand_cols(myDS, SP, 0, r0, r0 + 4, lane);
+    const bf16x8 ap = lds_operand_cols_at(myPF + 16 * kq * 32, cp.a[0], cp.b[0]);
+    const bf16x8 as = lds_operand_cols_at(myDS + 16 * kq * 32, cp.a[0], cp.b[0]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      dv[db] = mfma32x32x16(ap, lds_operand_cols(sdOb, SQ, 32 * db, r0, r0 + 4, lane), dv[db]);
-      dk[db] = mfma32x32x16(as, lds_operand_cols(sQb, SQ, 32 * db, r0, r0 + 4, lane), dk[db]);
+      dv[db] = mfma32x32x16(ap, lds_operand_cols_at(sdOb + 16 * kq * D, co.a[db], co.b[db]),
+                            dv[db]);
+      dk[db] = mfma32x32x16(as, lds_operand_cols_at(sQb + 16 * kq * D, co.a[db], co.b[db]),
+                            dk[db]);
     }
   }
   wave_lds_fence();
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void k_dkdv(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_DKDV_WAVES, 8)))
+void k_dkdv(AttnArgs a) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int BM = kDkvBM;
-  constexpr int SQ = D + 8;         // row stride of sQ / sdO
-  constexpr int SP = 40;            // row stride of the per-wave [query][key] tiles
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int CH = BM * CPR / 256;  // chunks per thread per tensor per tile
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BM * SQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BM * SQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sPF[4][BM * SP];
-  __shared__ __attribute__((aligned(16))) uint16_t sDS[4][BM * SP];
+  static_assert(BM % 32 == 0 && CH >= 1 && kDkvBN % BM == 0,
+                "query tile must be whole 32-query sub-tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BM * D];  // swizzled rows
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sPF[4][32 * 32];  // per wave [query][key]
+  __shared__ __attribute__((aligned(16))) uint16_t sDS[4][32 * 32];
   __shared__ float sLse[2][BM];
   __shared__ float sDl[2][BM];
 
@@ -322,6 +339,12 @@ __global__ __launch_bounds__(256) void k_dkdv(AttnArgs a) {
   }
   const float sl2 = a.softmax_scale * kLog2e;
   const float psc = a.p_scale;
+  // LDS offsets: Q^/dO row reads, their column reads (k-block rows 8h.., 8h+4..),
+  // and the per-wave [query][key] tiles (column reads and this lane's row writes)
+  const RowOffsets<D> ro(lane);
+  const ColOffsets<D> co(8 * h, 8 * h + 4, lane);
+  const ColOffsets<32> cp(8 * h, 8 * h + 4, lane);
+  const int pw0 = swz<32>(l32, 16 * h), pw1 = swz<32>(l32, 16 * h + 8);
 
   // query tiles: below the workgroup's first key everything is masked (causal)
   const int qfirst = CAUSAL ? kblk0 : 0;
@@ -350,8 +373,8 @@ __global__ __launch_bounds__(256) void k_dkdv(AttnArgs a) {
     for (int c = 0; c < CH; ++c) {
       const int idx = tid + 256 * c;
       const int r = idx / CPR, col = (idx % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&sQ[buf][r * SQ + col]) = rq[c];
-      *reinterpret_cast<u32x4*>(&sdO[buf][r * SQ + col]) = rd[c];
+      *reinterpret_cast<u32x4*>(&sQ[buf][swz<D>(r, col)]) = rq[c];
+      *reinterpret_cast<u32x4*>(&sdO[buf][swz<D>(r, col)]) = rd[c];
     }
     if (tid < BM) {
       sLse[buf][tid] = rl;
@@ -369,16 +392,26 @@ __global__ __launch_bounds__(256) void k_dkdv(AttnArgs a) {
     const int q0 = qfirst + it * BM;
     const bool has_next = it + 1 < ntiles;
     if (has_next) load_tile(q0 + BM);
-    // every query of the tile below this wave's first key: nothing to do
-    const bool active = !(CAUSAL && q0 + BM - 1 < kw0);
-    if (active) {
-      const bool mask = (q0 + BM > nq) || (kw0 + 32 > nkv) || (CAUSAL && q0 < kw0 + 31);
-      if (mask)
-        dkdv_tile<D, CAUSAL, true>(kf, vf, dk, dv, sQ[buf], sdO[buf], sLse[buf], sDl[buf],
-                                   sPF[wave], sDS[wave], q0, kw0, nq, nkv, sl2, psc, lane);
-      else
-        dkdv_tile<D, CAUSAL, false>(kf, vf, dk, dv, sQ[buf], sdO[buf], sLse[buf], sDl[buf],
-                                    sPF[wave], sDS[wave], q0, kw0, nq, nkv, sl2, psc, lane);
+#pragma unroll
+    for (int sub = 0; sub < BM / 32; ++sub) {
+      const int qs = q0 + 32 * sub;
+      // every query of the sub-tile below this wave's first key: nothing to do
+      const bool active = !(CAUSAL && qs + 31 < kw0);
+      if (active) {
+        const uint16_t* qb = sQ[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
+        const uint16_t* ob = sdO[buf] + 32 * sub * D;
+        const float* lb = sLse[buf] + 32 * sub;
+        const float* db = sDl[buf] + 32 * sub;
+        const bool mask = (qs + 32 > nq) || (kw0 + 32 > nkv) || (CAUSAL && qs < kw0 + 31);
+        if (mask)
+          dkdv_tile<D, CAUSAL, true>(kf, vf, dk, dv, qb, ob, lb, db, sPF[wave], sDS[wave],
+                                            ro, co, cp, pw0, pw1, qs, kw0, nq, nkv, sl2, psc,
+                                            lane);
+        else
+          dkdv_tile<D, CAUSAL, false>(kf, vf, dk, dv, qb, ob, lb, db, sPF[wave],
+                                             sDS[wave], ro, co, cp, pw0, pw1, qs, kw0, nq, nkv,
+                                             sl2, psc, lane);
+      }
     }
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();

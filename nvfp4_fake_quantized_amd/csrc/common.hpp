@@ -18,6 +18,27 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Build-time tiling knobs (defaults are the tuned values).
+#ifndef ATTNQAT_FWD_BN
+#define ATTNQAT_FWD_BN 32  // keys per staged tile in the forward (32 or 64)
+#endif
+#ifndef ATTNQAT_DQ_BN
+#define ATTNQAT_DQ_BN 32  // keys per staged tile in the dQ kernel (32 or 64)
+#endif
+#ifndef ATTNQAT_DKDV_BM
+#define ATTNQAT_DKDV_BM 64  // queries per staged tile in the dK/dV kernel (32 or 64)
+#endif
+// Waves per SIMD the register allocation of each attention kernel targets.
+#ifndef ATTNQAT_FWD_WAVES
+#define ATTNQAT_FWD_WAVES 2
+#endif
+#ifndef ATTNQAT_DQ_WAVES
+#define ATTNQAT_DQ_WAVES 2
+#endif
+#ifndef ATTNQAT_DKDV_WAVES
+#define ATTNQAT_DKDV_WAVES 1
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -127,18 +148,83 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// A 32x32x16 MFMA operand whose lanes index columns of a row-major LDS tile:
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles.
+//
+// Tiles of bf16 rows of W elements are stored unpadded; the 16-byte chunk c
+// of row r sits at chunk position c ^ f(r).  The two access patterns of the
+// kernels are (a) 16-byte row reads by 32 lanes over 32 consecutive rows and
+// (b) transpose reads of 4 consecutive rows by each 16-lane group.  On
+// gfx950's 64-bank LDS, f below makes both conflict-free (measured: 16-byte
+// row reads at 128 B/clk, transpose reads at 256 B/clk):
+//   W = 128: f(r) = ((r >> 2) & 3) ^ ((r & 3) << 2)
+//   W = 64:  f(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
+//   W = 32:  f(r) = (r >> 2) & 3
+template <int W>
+__device__ __forceinline__ int swz_chunk(int r, int c) {
+  if constexpr (W == 128) return c ^ (((r >> 2) & 3) ^ ((r & 3) << 2));
+  else if constexpr (W == 64) return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  else return c ^ ((r >> 2) & 3);
+}
+
+// Element offset of (row r, column col) in a swizzled tile of width W.
+template <int W>
+__device__ __forceinline__ int swz(int r, int col) {
+  return r * W + 8 * swz_chunk<W>(r, col >> 3) + (col & 7);
+}
+
+// A 32x32x16 MFMA operand whose lanes index columns of a swizzled tile:
 // lane l gets column col0 + l%32 of rows r0 + 0..3 (elements 0..3) and
 // r1 + 0..3 (elements 4..7), where r0, r1 may depend on h = l/32.
-__device__ __forceinline__ bf16x8 lds_operand_cols(const uint16_t* tile, int ld, int col0, int r0,
-                                                   int r1, int lane) {
+template <int W>
+__device__ __forceinline__ bf16x8 lds_operand_cols(const uint16_t* tile, int col0, int r0, int r1,
+                                                   int lane) {
   const int j = lane & 15;
   const int col = col0 + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
-  const u32x2 lo = lds_read_tr16(tile + (r0 + (j >> 2)) * ld + col);
-  const u32x2 hi = lds_read_tr16(tile + (r1 + (j >> 2)) * ld + col);
+  const u32x2 lo = lds_read_tr16(tile + swz<W>(r0 + (j >> 2), col));
+  const u32x2 hi = lds_read_tr16(tile + swz<W>(r1 + (j >> 2), col));
   const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
   return __builtin_bit_cast(bf16x8, v);
 }
+
+// The same read from two precomputed per-lane element offsets (see
+// ColOffsets); `tile` may carry compile-time row offsets.
+__device__ __forceinline__ bf16x8 lds_operand_cols_at(const uint16_t* tile, int off0, int off1) {
+  const u32x2 lo = lds_read_tr16(tile + off0);
+  const u32x2 hi = lds_read_tr16(tile + off1);
+  const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Per-lane offsets of the column reads of lds_operand_cols<W> for the
+// column blocks col0 = 32*db and first rows r0 = RA(h), r1 = RB(h).  The
+// swizzle phase of a row depends only on bits of the row index that a
+// k-block shift by a multiple of 16 rows does not change, so the offsets for
+// k-block kb are these plus 16*kb*W (a compile-time constant).
+template <int W>
+struct ColOffsets {
+  int a[W / 32], b[W / 32];
+  __device__ __forceinline__ ColOffsets(int ra, int rb, int lane) {
+    const int j = lane & 15;
+#pragma unroll
+    for (int db = 0; db < W / 32; ++db) {
+      const int col = 32 * db + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
+      a[db] = swz<W>(ra + (j >> 2), col);
+      b[db] = swz<W>(rb + (j >> 2), col);
+    }
+  }
+};
+
+// Per-lane offsets of the 16-byte row reads (row l32, column 16*kb + 8h).
+template <int W>
+struct RowOffsets {
+  int o[W / 16];
+  __device__ __forceinline__ explicit RowOffsets(int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int kb = 0; kb < W / 16; ++kb) o[kb] = swz<W>(l32, 16 * kb + 8 * h);
+  }
+};
 
 // bf16 pair from two floats (round to nearest even), packed low/high.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -6,9 +6,9 @@
 // Work decomposition (gfx950, wave64, bf16 MFMA 32x32x16, fp32 accumulate):
 //  * a workgroup of 4 waves owns 128 queries; each wave owns 32 queries and
 //    keeps its Q^ rows in registers as the B operand of S^T = K^ Q^T;
-//  * the key loop stages 32-key tiles of K^ and V^ row-major in
-//    double-buffered LDS, prefetched one tile ahead through registers; the
-//    V^T operand is read with LDS transpose reads;
+//  * the key loop stages 32-key tiles of K^ and V^ row-major (XOR-swizzled
+//    16-byte chunks) in double-buffered LDS, prefetched one tile ahead
+//    through registers; the V^T operand is read with LDS transpose reads;
 //  * S^T's accumulator layout puts one query per lane (and 16 of its keys in
 //    VGPRs), so the online-softmax row statistics are per lane (plus one
 //    exchange with the lane 32 away), and P^T feeds the B operand of
@@ -30,7 +30,7 @@ namespace attnqat {
 namespace {
 
 constexpr int kFwdBM = 128;  // queries per workgroup
-constexpr int kFwdBN = 32;   // keys per tile
+constexpr int kFwdBN = ATTNQAT_FWD_BN;  // keys per staged tile (32-key sub-tiles)
 
 __device__ __forceinline__ u32x4 ld_u32x4(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -40,16 +40,16 @@ __device__ __forceinline__ u32x4 ld_u32x4(const uint16_t* p) {
 // (m, l, O^T).  m is the running row max in log2 units.
 template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void fwd_tile(const bf16x8* qf, f32x16* o, float& m, float& l,
-                                         const uint16_t* sKb, const uint16_t* sVb, int k0, int qi,
-                                         int nkv, float sl2, int lane) {
+                                         const uint16_t* sKb, const uint16_t* sVb,
+                                         const RowOffsets<D>& ro, const ColOffsets<D>& co, int k0,
+                                         int qi, int nkv, float sl2, int lane) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
-  constexpr int SK = D + 8;
   const int h = lane >> 5, l32 = lane & 31;
   f32x16 s = zero_f32x16();
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
-    s = mfma32x32x16(ld_bf16x8(sKb + l32 * SK + 16 * kb + 8 * h), qf[kb], s);
+    s = mfma32x32x16(ld_bf16x8(sKb + ro.o[kb]), qf[kb], s);
   float tmax = -INFINITY;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -88,23 +88,23 @@ __device__ __forceinline__ void fwd_tile(const bf16x8* qf, f32x16* o, float& m, 
                       pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]),
                       pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7])};
     const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-    const int r0 = 16 * kh + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      o[db] = mfma32x32x16(lds_operand_cols(sVb, SK, 32 * db, r0, r0 + 8, lane), b, o[db]);
+      o[db] = mfma32x32x16(lds_operand_cols_at(sVb + 16 * kh * D, co.a[db], co.b[db]), b, o[db]);
   }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void k_fwd(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_FWD_WAVES, 8)))
+void k_fwd(AttnArgs a) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int BN = kFwdBN;
-  constexpr int SK = D + 8;           // row stride of sK / sV (elements)
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int CH = BN * CPR / 256;  // chunks per thread per tensor per tile
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * SK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * SK];
+  static_assert(BN % 32 == 0 && CH >= 1, "key tile must be whole 32-key sub-tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];  // swizzled rows
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -128,6 +128,9 @@ __global__ __launch_bounds__(256) void k_fwd(AttnArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = zero_f32x16();
   float m = -INFINITY, l = 0.0f;
   const float sl2 = a.softmax_scale * kLog2e;
+  // LDS offsets: K^ row reads and V^T column reads (k-block rows 4h.., 4h+8..)
+  const RowOffsets<D> ro(lane);
+  const ColOffsets<D> co(4 * h, 4 * h + 8, lane);
   const int kend = CAUSAL ? min(nkv, qblk0 + kFwdBM) : nkv;
   const int ntiles = (kend + BN - 1) / BN;
 
@@ -148,8 +151,8 @@ __global__ __launch_bounds__(256) void k_fwd(AttnArgs a) {
     for (int c = 0; c < CH; ++c) {
       const int idx = tid + 256 * c;
       const int r = idx / CPR, col = (idx % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&sK[buf][r * SK + col]) = rk[c];
-      *reinterpret_cast<u32x4*>(&sV[buf][r * SK + col]) = rv[c];
+      *reinterpret_cast<u32x4*>(&sK[buf][swz<D>(r, col)]) = rk[c];
+      *reinterpret_cast<u32x4*>(&sV[buf][swz<D>(r, col)]) = rv[c];
     }
   };
 
@@ -163,13 +166,19 @@ __global__ __launch_bounds__(256) void k_fwd(AttnArgs a) {
     const int k0 = it * BN;
     const bool has_next = it + 1 < ntiles;
     if (has_next) load_tile(k0 + BN);
-    const bool active = !(CAUSAL && qw0 + 31 < k0);  // every key above every row
-    if (active) {
-      const bool mask = (k0 + BN > nkv) || (CAUSAL && k0 + BN - 1 > qw0);
-      if (mask)
-        fwd_tile<D, CAUSAL, true>(qf, o, m, l, sK[buf], sV[buf], k0, qi, nkv, sl2, lane);
-      else
-        fwd_tile<D, CAUSAL, false>(qf, o, m, l, sK[buf], sV[buf], k0, qi, nkv, sl2, lane);
+#pragma unroll
+    for (int sub = 0; sub < BN / 32; ++sub) {
+      const int ks = k0 + 32 * sub;
+      const bool active = !(CAUSAL && qw0 + 31 < ks);  // every key above every row
+      if (active) {
+        const uint16_t* kb = sK[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
+        const uint16_t* vb = sV[buf] + 32 * sub * D;
+        const bool mask = (ks + 32 > nkv) || (CAUSAL && ks + 31 > qw0);
+        if (mask)
+          fwd_tile<D, CAUSAL, true>(qf, o, m, l, kb, vb, ro, co, ks, qi, nkv, sl2, lane);
+        else
+          fwd_tile<D, CAUSAL, false>(qf, o, m, l, kb, vb, ro, co, ks, qi, nkv, sl2, lane);
+      }
     }
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
