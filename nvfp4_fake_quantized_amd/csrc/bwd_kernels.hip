@@ -45,7 +45,7 @@ namespace {
 constexpr int kDqBM = 128;              // queries per workgroup (k_dq)
 constexpr int kDqBN = ATTNQAT_DQ_BN;      // keys per staged tile (k_dq; 32-key sub-tiles)
 constexpr int kDkvBN = 128;             // keys per workgroup (k_dkdv)
-constexpr int kDkvBM = ATTNQAT_DKDV_BM;   // queries per staged tile (k_dkdv; 32-query sub-tiles)
+constexpr int kDkvBM = 64;              // queries per staged tile (k_dkdv; two 32-query sub-tiles)
 
 __device__ __forceinline__ u32x4 ld_u32x4(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -144,7 +144,7 @@ void k_dq(AttnArgs a) {
   const int ntiles = (kend + BN - 1) / BN;
 
   u32x4 rk[CH], rv[CH];
-  auto load_tile = [&](int k0) {
+  auto load_tile = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int idx = tid + 256 * c;
@@ -155,7 +155,7 @@ void k_dq(AttnArgs a) {
       rv[c] = key < nkv ? ld_u32x4(V + (size_t)key * D + col) : z;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int idx = tid + 256 * c;
@@ -165,12 +165,8 @@ void k_dq(AttnArgs a) {
     }
   };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+  auto step = [&](int it, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = it & 1;
     const int k0 = it * BN;
     const bool has_next = it + 1 < ntiles;
@@ -178,22 +174,28 @@ void k_dq(AttnArgs a) {
 #pragma unroll
     for (int sub = 0; sub < BN / 32; ++sub) {
       const int ks = k0 + 32 * sub;
-      const bool active = !(CAUSAL && qw0 + 31 < ks);  // every key above every row
-      if (active) {
-        const uint16_t* kb = sK[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
-        const uint16_t* vb = sV[buf] + 32 * sub * D;
-        const bool mask = (ks + 32 > nkv) || (qw0 + 32 > nq) || (CAUSAL && ks + 31 > qw0);
-        if (mask)
-          dq_tile<D, CAUSAL, true>(qf, df, acc, kb, vb, ro, co, ks, qi, qok, nkv, lse2, dl, sl2,
-                                   lane);
-        else
-          dq_tile<D, CAUSAL, false>(qf, df, acc, kb, vb, ro, co, ks, qi, qok, nkv, lse2, dl, sl2,
-                                    lane);
-      }
+      const uint16_t* kb = sK[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
+      const uint16_t* vb = sV[buf] + 32 * sub * D;
+      // (boundary tiles only) every key above every row of this wave: skip
+      if (!MASK || !(CAUSAL && qw0 + 31 < ks))
+        dq_tile<D, CAUSAL, MASK>(qf, df, acc, kb, vb, ro, co, ks, qi, qok, nkv, lse2, dl, sl2,
+                                 lane);
     }
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
+  };
+  // Leading tiles are interior (branch-free); masks start at the first tile
+  // that reaches past nkv or above the workgroup's first query (causal).
+  int it_hi = min(ntiles, nkv / BN);
+  if (CAUSAL) it_hi = min(it_hi, (qblk0 + 1) / BN);
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
   }
+  __syncthreads();
+  for (int it = 0; it < it_hi; ++it) step(it, BoolTag<false>());
+  for (int it = it_hi; it < ntiles; ++it) step(it, BoolTag<true>());
 
   if (qok) {
     const float sc = a.softmax_scale;
@@ -290,6 +292,148 @@ __device__ __forceinline__ void dkdv_tile(const bf16x8* kf, const bf16x8* vf, f3
   wave_lds_fence();
 }
 
+// One slot of the interior software pipeline of k_dkdv (one wave, 32 keys).
+// It runs the VALU work of sub-tile i (softmax recompute from lse, dS, the
+// P fake-quant, the P^F/dS rows written to LDS) and, interleaved with it,
+// the dV/dK MFMAs of sub-tile i-1 (from its P^F/dS tiles) and the S^T/dP^T
+// MFMAs of sub-tile i+1.  The three streams are independent, so the MFMA
+// pipe and the VALU overlap; scheduling fences keep the interleave and the
+// LDS operands of each MFMA are read one step ahead.
+template <int D>
+__device__ __forceinline__ void dkdv_slot(
+    // sub-tile i: S^T/dP^T accumulators, lse (log2 units) and delta of this
+    // lane's query, destination P^F/dS tiles
+    const f32x16& s, const f32x16& dp, float lse2, float dl, uint16_t* pfB, uint16_t* dsB,
+    // sub-tile i-1: its P^F/dS tiles and its staged Q^/dO rows
+    const uint16_t* pfC, const uint16_t* dsC, const uint16_t* sQC, const uint16_t* sdOC,
+    // sub-tile i+1: its staged Q^/dO rows and the S^T/dP^T results
+    const uint16_t* sQA, const uint16_t* sdOA, f32x16& sA, f32x16& dA,
+    const bf16x8* kf, const bf16x8* vf, f32x16* dk, f32x16* dv, const RowOffsets<D>& ro,
+    const ColOffsets<D>& co, const ColOffsets<32>& cp, int pw0, int pw1, float sl2, float psc) {
+  constexpr int KB = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NC = 4 * DB;  // dV/dK MFMAs (2 k-blocks of 16 queries x DB x {dV, dK})
+  constexpr int NA = 2 * KB;  // S^T/dP^T MFMAs
+  constexpr int NS = 16;      // steps (VALU: 8 softmax steps, 8 quant steps)
+  static_assert(NC <= NS && NA <= NS, "MFMA streams must fit the VALU steps");
+  // B operands of the C stream (column reads) and of the A stream (row reads)
+  auto opC = [&](int k) __attribute__((always_inline)) {
+    const int kq = k / (2 * DB), db = (k / 2) % DB;
+    return (k & 1) ? lds_operand_cols_at(sQC + 16 * kq * D, co.a[db], co.b[db])
+                   : lds_operand_cols_at(sdOC + 16 * kq * D, co.a[db], co.b[db]);
+  };
+  auto opA = [&](int k) __attribute__((always_inline)) {
+    return ld_bf16x8(((k & 1) ? sdOA : sQA) + ro.o[k / 2]);
+  };
+  bf16x8 apC[2], asC[2], bC[NS + 1], bA[NS + 1];
+  apC[0] = lds_operand_cols_at(pfC, cp.a[0], cp.b[0]);
+  asC[0] = lds_operand_cols_at(dsC, cp.a[0], cp.b[0]);
+  bC[0] = opC(0);
+  bA[0] = opA(0);
+  sA = zero_f32x16();
+  dA = zero_f32x16();
+  float p[16], ds[16], amax = 0.0f, sc = 0.0f;
+  u32x4 pf[2], dsb[2];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    // operands of the next step
+    if (k + 1 < NC) bC[k + 1] = opC(k + 1);
+    if (k + 1 < NA) bA[k + 1] = opA(k + 1);
+    if (k + 1 == 2 * DB) {
+      apC[1] = lds_operand_cols_at(pfC + 16 * 32, cp.a[0], cp.b[0]);
+      asC[1] = lds_operand_cols_at(dsC + 16 * 32, cp.a[0], cp.b[0]);
+    }
+    if (k < NC) {
+      const int kq = k / (2 * DB), db = (k / 2) % DB;
+      if (k & 1)
+        dk[db] = mfma32x32x16(asC[kq], bC[k], dk[db]);
+      else
+        dv[db] = mfma32x32x16(apC[kq], bC[k], dv[db]);
+    }
+    if (k < NA) {
+      if (k & 1)
+        dA = mfma32x32x16(vf[k / 2], bA[k], dA);
+      else
+        sA = mfma32x32x16(kf[k / 2], bA[k], sA);
+    }
+    if (k < 8) {
+#pragma unroll
+      for (int e = 2 * k; e < 2 * k + 2; ++e) {
+        const float pv = fast_exp2(__builtin_fmaf(s[e], sl2, -lse2));
+        ds[e] = pv * (dp[e] - dl);
+        p[e] = pv * psc;
+        amax = fmaxf(amax, p[e]);
+      }
+      if (k == 7) sc = e4m3_scale_from_amax(amax);
+    } else {
+      const int i = k - 8;
+      const FastP fq(sc);
+      float y0, y1;
+      fq.pair(p[2 * i], p[2 * i + 1], y0, y1);
+      pf[i >> 2][i & 3] = pin_vgpr(pack_bf16x2(y0, y1));
+      dsb[i >> 2][i & 3] = pin_vgpr(pack_bf16x2(ds[2 * i], ds[2 * i + 1]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  *reinterpret_cast<u32x4*>(pfB + pw0) = pf[0];
+  *reinterpret_cast<u32x4*>(pfB + pw1) = pf[1];
+  *reinterpret_cast<u32x4*>(dsB + pw0) = dsb[0];
+  *reinterpret_cast<u32x4*>(dsB + pw1) = dsb[1];
+  wave_lds_fence();
+}
+
+// S^T/dP^T MFMAs of one sub-tile alone (fills the pipeline).
+template <int D>
+__device__ __forceinline__ void dkdv_fill(const uint16_t* sQA, const uint16_t* sdOA, f32x16& sA,
+                                          f32x16& dA, const bf16x8* kf, const bf16x8* vf,
+                                          const RowOffsets<D>& ro) {
+  constexpr int KB = D / 16;
+  sA = zero_f32x16();
+  dA = zero_f32x16();
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    sA = mfma32x32x16(kf[kb], ld_bf16x8(sQA + ro.o[kb]), sA);
+    dA = mfma32x32x16(vf[kb], ld_bf16x8(sdOA + ro.o[kb]), dA);
+  }
+}
+
+// dV/dK MFMAs of one sub-tile alone (drains the pipeline).
+template <int D>
+__device__ __forceinline__ void dkdv_drain(const uint16_t* pfC, const uint16_t* dsC,
+                                           const uint16_t* sQC, const uint16_t* sdOC, f32x16* dk,
+                                           f32x16* dv, const ColOffsets<D>& co,
+                                           const ColOffsets<32>& cp) {
+  constexpr int DB = D / 32;
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq) {
+    const bf16x8 ap = lds_operand_cols_at(pfC + 16 * kq * 32, cp.a[0], cp.b[0]);
+    const bf16x8 as = lds_operand_cols_at(dsC + 16 * kq * 32, cp.a[0], cp.b[0]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dv[db] = mfma32x32x16(ap, lds_operand_cols_at(sdOC + 16 * kq * D, co.a[db], co.b[db]),
+                            dv[db]);
+      dk[db] = mfma32x32x16(as, lds_operand_cols_at(sQC + 16 * kq * D, co.a[db], co.b[db]),
+                            dk[db]);
+    }
+  }
+  wave_lds_fence();
+}
+
+// Workgroup: 4 waves x 32 keys.  Each wave keeps its K^/V^ rows in registers
+// (A operands of S^T = K^ Q^T and dP^T = V dO^T, rows in key_perm order) and
+// its dK/dV accumulators.  Query tiles of 64 rows (two 32-query sub-tiles)
+// are staged in a ring of three LDS buffers: tile t+1 is written after
+// sub-tile 0 of tile t and published by the one barrier per tile, and tile
+// t+2 is then fetched into registers.  A tile's buffer is read from the
+// second half of the tile before it to the first half of the tile after it;
+// the third buffer lets the single barrier separate those reads from the
+// next write of the same buffer.
+//
+// Interior tiles (no masks) run the slot pipeline over the sub-tile
+// sequence; boundary tiles (causal diagonal first, a partial query tile
+// last, everything when the workgroup's keys pass nkv) run self-contained
+// masked sub-tiles, and the pipeline is filled and drained around the
+// interior run.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_DKDV_WAVES, 8)))
 void k_dkdv(AttnArgs a) {
@@ -298,14 +442,15 @@ void k_dkdv(AttnArgs a) {
   constexpr int BM = kDkvBM;
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int CH = BM * CPR / 256;  // chunks per thread per tensor per tile
-  static_assert(BM % 32 == 0 && CH >= 1 && kDkvBN % BM == 0,
-                "query tile must be whole 32-query sub-tiles");
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BM * D];  // swizzled rows
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BM * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sPF[4][32 * 32];  // per wave [query][key]
-  __shared__ __attribute__((aligned(16))) uint16_t sDS[4][32 * 32];
-  __shared__ float sLse[2][BM];
-  __shared__ float sDl[2][BM];
+  constexpr int NBUF = 3;
+  static_assert(BM == 64 && CH >= 1 && kDkvBN % BM == 0, "two 32-query sub-tiles per tile");
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[NBUF][BM * D];  // swizzled rows
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[NBUF][BM * D];
+  // per wave [query][key] tiles of P^F and dS, indexed by sub-tile parity
+  __shared__ __attribute__((aligned(16))) uint16_t sPF[4][2][32 * 32];
+  __shared__ __attribute__((aligned(16))) uint16_t sDS[4][2][32 * 32];
+  __shared__ float sLse[NBUF][BM];
+  __shared__ float sDl[NBUF][BM];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -345,6 +490,10 @@ void k_dkdv(AttnArgs a) {
   const ColOffsets<D> co(8 * h, 8 * h + 4, lane);
   const ColOffsets<32> cp(8 * h, 8 * h + 4, lane);
   const int pw0 = swz<32>(l32, 16 * h), pw1 = swz<32>(l32, 16 * h + 8);
+  uint16_t* const pf0 = sPF[wave][0];
+  uint16_t* const pf1 = sPF[wave][1];
+  uint16_t* const ds0 = sDS[wave][0];
+  uint16_t* const ds1 = sDS[wave][1];
 
   // query tiles: below the workgroup's first key everything is masked (causal)
   const int qfirst = CAUSAL ? kblk0 : 0;
@@ -352,7 +501,8 @@ void k_dkdv(AttnArgs a) {
 
   u32x4 rq[CH], rd[CH];
   float rl = 0.0f, rdl = 0.0f;
-  auto load_tile = [&](int q0) {
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const int q0 = qfirst + t * BM;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int idx = tid + 256 * c;
@@ -368,7 +518,7 @@ void k_dkdv(AttnArgs a) {
       rdl = qq < nq ? DL[qq] : 0.0f;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int idx = tid + 256 * c;
@@ -381,40 +531,85 @@ void k_dkdv(AttnArgs a) {
       sDl[buf][tid] = rdl;
     }
   };
+  // between the two sub-tiles of tile t: publish tile t+1, fetch tile t+2
+  auto advance = [&](int t, int nbuf) __attribute__((always_inline)) {
+    if (t + 1 < ntiles) store_tile(nbuf);
+    __syncthreads();
+    if (t + 2 < ntiles) load_tile(t + 2);
+  };
+  // self-contained masked sub-tile (skipped when every query is below the
+  // wave's first key)
+  auto masked_sub = [&](int t, int buf, int sub) __attribute__((always_inline)) {
+    const int qs = qfirst + t * BM + 32 * sub;
+    if (!(CAUSAL && qs + 31 < kw0))
+      dkdv_tile<D, CAUSAL, true>(kf, vf, dk, dv, sQ[buf] + 32 * sub * D, sdO[buf] + 32 * sub * D,
+                                 sLse[buf] + 32 * sub, sDl[buf] + 32 * sub, pf0, ds0, ro, co, cp,
+                                 pw0, pw1, qs, kw0, nq, nkv, sl2, psc, lane);
+  };
+  auto masked_step = [&](int t, int buf, int nbuf) __attribute__((always_inline)) {
+    masked_sub(t, buf, 0);
+    advance(t, nbuf);
+    masked_sub(t, buf, 1);
+  };
+
+  // Tiles needing masks: the causal diagonal (queries below the workgroup's
+  // last key) at the start, a partial query tile at the end, or all tiles
+  // when the workgroup's keys run past nkv.
+  int it_lo = 0, it_hi = ntiles;
+  if (kblk0 + kDkvBN > nkv) {
+    it_lo = ntiles;
+  } else {
+    if (CAUSAL) it_lo = min(ntiles, (kblk0 + kDkvBN - 1 - qfirst + BM - 1) / BM);
+    if (nq % BM != 0) it_hi = max(it_lo, ntiles - 1);
+  }
 
   if (ntiles > 0) {
-    load_tile(qfirst);
+    load_tile(0);
     store_tile(0);
   }
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int q0 = qfirst + it * BM;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(q0 + BM);
-#pragma unroll
-    for (int sub = 0; sub < BM / 32; ++sub) {
-      const int qs = q0 + 32 * sub;
-      // every query of the sub-tile below this wave's first key: nothing to do
-      const bool active = !(CAUSAL && qs + 31 < kw0);
-      if (active) {
-        const uint16_t* qb = sQ[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
-        const uint16_t* ob = sdO[buf] + 32 * sub * D;
-        const float* lb = sLse[buf] + 32 * sub;
-        const float* db = sDl[buf] + 32 * sub;
-        const bool mask = (qs + 32 > nq) || (kw0 + 32 > nkv) || (CAUSAL && qs < kw0 + 31);
-        if (mask)
-          dkdv_tile<D, CAUSAL, true>(kf, vf, dk, dv, qb, ob, lb, db, sPF[wave], sDS[wave],
-                                            ro, co, cp, pw0, pw1, qs, kw0, nq, nkv, sl2, psc,
-                                            lane);
-        else
-          dkdv_tile<D, CAUSAL, false>(kf, vf, dk, dv, qb, ob, lb, db, sPF[wave],
-                                             sDS[wave], ro, co, cp, pw0, pw1, qs, kw0, nq, nkv,
-                                             sl2, psc, lane);
-      }
+  if (ntiles > 1) load_tile(1);
+  int buf = 0;  // t % NBUF
+  int t = 0;
+  for (; t < it_lo; ++t) {
+    const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+    masked_step(t, buf, nbuf);
+    buf = nbuf;
+  }
+  if (it_lo < it_hi) {
+    // The first slot's dV/dK stream has no previous sub-tile: give it zero
+    // P^F/dS tiles (with the current tile's finite Q^/dO as the other operand)
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(pf1 + pw0) = z;
+    *reinterpret_cast<u32x4*>(pf1 + pw1) = z;
+    *reinterpret_cast<u32x4*>(ds1 + pw0) = z;
+    *reinterpret_cast<u32x4*>(ds1 + pw1) = z;
+    wave_lds_fence();
+    f32x16 s0, dp0, s1, dp1;
+    dkdv_fill<D>(sQ[buf], sdO[buf], s0, dp0, kf, vf, ro);
+    int pbuf = buf;  // buffer of the previous tile (the current one at first)
+    for (; t < it_hi; ++t) {
+      const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+      const uint16_t* q = sQ[buf];
+      const uint16_t* o = sdO[buf];
+      // sub-tile 0: C = sub-tile 1 of the previous tile, A = sub-tile 1
+      dkdv_slot<D>(s0, dp0, sLse[buf][l32], sDl[buf][l32], pf0, ds0, pf1, ds1,
+                   sQ[pbuf] + 32 * D, sdO[pbuf] + 32 * D, q + 32 * D, o + 32 * D, s1, dp1, kf,
+                   vf, dk, dv, ro, co, cp, pw0, pw1, sl2, psc);
+      advance(t, nbuf);
+      // sub-tile 1: C = sub-tile 0, A = sub-tile 0 of the next tile (its
+      // result is unused after the last interior tile)
+      dkdv_slot<D>(s1, dp1, sLse[buf][32 + l32], sDl[buf][32 + l32], pf1, ds1, pf0, ds0, q, o,
+                   sQ[nbuf], sdO[nbuf], s0, dp0, kf, vf, dk, dv, ro, co, cp, pw0, pw1, sl2, psc);
+      pbuf = buf;
+      buf = nbuf;
     }
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    dkdv_drain<D>(pf1, ds1, sQ[pbuf] + 32 * D, sdO[pbuf] + 32 * D, dk, dv, co, cp);
+  }
+  for (; t < ntiles; ++t) {
+    const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+    masked_step(t, buf, nbuf);
+    buf = nbuf;
   }
 
   // dK / dV accumulators: lane -> d = 32*db + l32, VGPR v -> key kw0 + 8*(v/4) + 4h + v%4

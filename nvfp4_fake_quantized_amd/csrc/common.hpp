@@ -25,9 +25,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef ATTNQAT_DQ_BN
 #define ATTNQAT_DQ_BN 32  // keys per staged tile in the dQ kernel (32 or 64)
 #endif
-#ifndef ATTNQAT_DKDV_BM
-#define ATTNQAT_DKDV_BM 64  // queries per staged tile in the dK/dV kernel (32 or 64)
-#endif
 // Waves per SIMD the register allocation of each attention kernel targets.
 #ifndef ATTNQAT_FWD_WAVES
 #define ATTNQAT_FWD_WAVES 2
@@ -40,6 +37,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Compile-time boolean carried through generic lambdas.
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
@@ -235,6 +238,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Compiler-level ordering point for LDS traffic exchanged between the lanes
 // of one wave (LDS operations of a wave complete in issue order).
+// Returns x unchanged but makes the compiler materialize it here: the value
+// is computed before this point and not sunk towards its later uses (keeps a
+// hand-interleaved VALU stream where it was placed between scheduling fences).
+__device__ __forceinline__ uint32_t pin_vgpr(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -15,7 +15,8 @@
 //    O^T = V^T P^T straight from registers;
 //  * the running max only triggers a rescale of the accumulator when it
 //    moved for some row of the wave (otherwise the factor is exactly 1);
-//  * only boundary tiles evaluate masks;
+//  * only boundary tiles (the last key tiles: tail, causal diagonal) evaluate
+//    masks; the leading tiles run a branch-free loop;
 //  * causal: tiles with every key above the wave's last query are skipped
 //    (and the key loop ends at the workgroup's last query); the diagonal
 //    tile keeps the elementwise key <= query mask; keys >= Nkv are masked
@@ -156,12 +157,8 @@ void k_fwd(AttnArgs a) {
     }
   };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+  auto step = [&](int it, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = it & 1;
     const int k0 = it * BN;
     const bool has_next = it + 1 < ntiles;
@@ -169,20 +166,27 @@ void k_fwd(AttnArgs a) {
 #pragma unroll
     for (int sub = 0; sub < BN / 32; ++sub) {
       const int ks = k0 + 32 * sub;
-      const bool active = !(CAUSAL && qw0 + 31 < ks);  // every key above every row
-      if (active) {
-        const uint16_t* kb = sK[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
-        const uint16_t* vb = sV[buf] + 32 * sub * D;
-        const bool mask = (ks + 32 > nkv) || (CAUSAL && ks + 31 > qw0);
-        if (mask)
-          fwd_tile<D, CAUSAL, true>(qf, o, m, l, kb, vb, ro, co, ks, qi, nkv, sl2, lane);
-        else
-          fwd_tile<D, CAUSAL, false>(qf, o, m, l, kb, vb, ro, co, ks, qi, nkv, sl2, lane);
-      }
+      const uint16_t* kb = sK[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
+      const uint16_t* vb = sV[buf] + 32 * sub * D;
+      // (boundary tiles only) every key above every row of this wave: skip
+      if (!MASK || !(CAUSAL && qw0 + 31 < ks))
+        fwd_tile<D, CAUSAL, MASK>(qf, o, m, l, kb, vb, ro, co, ks, qi, nkv, sl2, lane);
     }
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
+  };
+  // Leading tiles are interior (branch-free); masks start at the first tile
+  // that reaches past nkv or above the workgroup's first query (causal).
+  int it_hi = min(ntiles, nkv / BN);
+  if (CAUSAL) it_hi = min(it_hi, (qblk0 + 1) / BN);
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
   }
+  __syncthreads();
+  for (int it = 0; it < it_hi; ++it) step(it, BoolTag<false>());
+  for (int it = it_hi; it < ntiles; ++it) step(it, BoolTag<true>());
 
   const float lt = l + xor32(l);
   if (qi < nq) {
