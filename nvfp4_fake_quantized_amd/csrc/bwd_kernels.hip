@@ -47,10 +47,6 @@ constexpr int kDqBN = ATTNQAT_DQ_BN;      // keys per staged tile (k_dq; 32-key 
 constexpr int kDkvBN = 128;             // keys per workgroup (k_dkdv)
 constexpr int kDkvBM = 64;              // queries per staged tile (k_dkdv; two 32-query sub-tiles)
 
-__device__ __forceinline__ u32x4 ld_u32x4(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
 // ---------------------------------------------------------------------------
 // dQ
 
@@ -144,15 +140,21 @@ void k_dq(AttnArgs a) {
   const int ntiles = (kend + BN - 1) / BN;
 
   u32x4 rk[CH], rv[CH];
+  uint32_t voff[CH];  // byte offset of this thread's chunks within a tile
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = tid + 256 * c;
+    voff[c] = (uint32_t)((idx / CPR) * D + (idx % CPR) * 8) * 2u;
+  }
   auto load_tile = [&](int k0) __attribute__((always_inline)) {
+    // rows past nkv read as zeros (masked out later)
+    const uint32_t bytes = (uint32_t)(min(nkv - k0, BN) * D) * 2u;
+    const auto rsk = make_rsrc(K + (size_t)k0 * D, bytes);
+    const auto rsv = make_rsrc(V + (size_t)k0 * D, bytes);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / CPR, col = (idx % CPR) * 8;
-      const int key = k0 + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      rk[c] = key < nkv ? ld_u32x4(K + (size_t)key * D + col) : z;
-      rv[c] = key < nkv ? ld_u32x4(V + (size_t)key * D + col) : z;
+      rk[c] = buf_ld16(rsk, voff[c]);
+      rv[c] = buf_ld16(rsv, voff[c]);
     }
   };
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
@@ -193,6 +195,7 @@ void k_dq(AttnArgs a) {
     load_tile(0);
     store_tile(0);
   }
+  vmem_wait_all();
   __syncthreads();
   for (int it = 0; it < it_hi; ++it) step(it, BoolTag<false>());
   for (int it = it_hi; it < ntiles; ++it) step(it, BoolTag<true>());
@@ -501,21 +504,28 @@ void k_dkdv(AttnArgs a) {
 
   u32x4 rq[CH], rd[CH];
   float rl = 0.0f, rdl = 0.0f;
+  uint32_t voff[CH];  // byte offset of this thread's chunks within a tile
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = tid + 256 * c;
+    voff[c] = (uint32_t)((idx / CPR) * D + (idx % CPR) * 8) * 2u;
+  }
   auto load_tile = [&](int t) __attribute__((always_inline)) {
+    // rows past nq read as zeros (masked out later); lse/delta are only
+    // scaled when stored, so nothing waits for these loads here
     const int q0 = qfirst + t * BM;
+    const int rows = min(nq - q0, BM);
+    const uint32_t bytes = (uint32_t)(rows * D) * 2u;
+    const auto rsq = make_rsrc(Q + (size_t)q0 * D, bytes);
+    const auto rsd = make_rsrc(dO + (size_t)q0 * D, bytes);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / CPR, col = (idx % CPR) * 8;
-      const int qq = q0 + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      rq[c] = qq < nq ? ld_u32x4(Q + (size_t)qq * D + col) : z;
-      rd[c] = qq < nq ? ld_u32x4(dO + (size_t)qq * D + col) : z;
+      rq[c] = buf_ld16(rsq, voff[c]);
+      rd[c] = buf_ld16(rsd, voff[c]);
     }
     if (tid < BM) {
-      const int qq = q0 + tid;
-      rl = qq < nq ? LSE[qq] * kLog2e : 0.0f;
-      rdl = qq < nq ? DL[qq] : 0.0f;
+      rl = buf_ldf(make_rsrc(LSE + q0, (uint32_t)rows * 4u), (uint32_t)tid * 4u);
+      rdl = buf_ldf(make_rsrc(DL + q0, (uint32_t)rows * 4u), (uint32_t)tid * 4u);
     }
   };
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
@@ -527,7 +537,7 @@ void k_dkdv(AttnArgs a) {
       *reinterpret_cast<u32x4*>(&sdO[buf][swz<D>(r, col)]) = rd[c];
     }
     if (tid < BM) {
-      sLse[buf][tid] = rl;
+      sLse[buf][tid] = rl * kLog2e;
       sDl[buf][tid] = rdl;
     }
   };
@@ -567,6 +577,7 @@ void k_dkdv(AttnArgs a) {
     load_tile(0);
     store_tile(0);
   }
+  vmem_wait_all();
   __syncthreads();
   if (ntiles > 1) load_tile(1);
   int buf = 0;  // t % NBUF

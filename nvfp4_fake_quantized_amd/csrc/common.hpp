@@ -246,6 +246,12 @@ __device__ __forceinline__ uint32_t pin_vgpr(uint32_t x) {
   return x;
 }
 
+// Waits for every outstanding vector-memory load of this wave (s_waitcnt
+// vmcnt(0); expcnt and lgkmcnt left at their maximum).  Used once before a
+// main loop whose MFMAs read registers loaded earlier, so that the compiler's
+// wait placement inside the loop only has to track the loop's own prefetches.
+__device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -281,6 +287,23 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* f) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = (__bf16)f[e];
   return r;
+}
+
+// Buffer resource over `bytes` bytes starting at p (raw, unswizzled, 32-bit
+// dword format).  Buffer loads past `bytes` return zeros (hardware range
+// check), so a tile that runs past the end of a tensor is zero-filled without
+// a select on the loaded data, and the per-lane offsets stay loop-invariant.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
+__device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const void* p) {

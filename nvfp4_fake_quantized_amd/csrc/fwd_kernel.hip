@@ -33,10 +33,6 @@ namespace {
 constexpr int kFwdBM = 128;  // queries per workgroup
 constexpr int kFwdBN = ATTNQAT_FWD_BN;  // keys per staged tile (32-key sub-tiles)
 
-__device__ __forceinline__ u32x4 ld_u32x4(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
 // One 32-key tile for one wave (32 queries): online-softmax update of
 // (m, l, O^T).  m is the running row max in log2 units.
 template <int D, bool CAUSAL, bool MASK>
@@ -136,15 +132,21 @@ void k_fwd(AttnArgs a) {
   const int ntiles = (kend + BN - 1) / BN;
 
   u32x4 rk[CH], rv[CH];
-  auto load_tile = [&](int k0) {
+  uint32_t voff[CH];  // byte offset of this thread's chunks within a tile
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = tid + 256 * c;
+    voff[c] = (uint32_t)((idx / CPR) * D + (idx % CPR) * 8) * 2u;
+  }
+  auto load_tile = [&](int k0) __attribute__((always_inline)) {
+    // rows past nkv read as zeros (masked out later)
+    const uint32_t bytes = (uint32_t)(min(nkv - k0, BN) * D) * 2u;
+    const auto rsk = make_rsrc(K + (size_t)k0 * D, bytes);
+    const auto rsv = make_rsrc(V + (size_t)k0 * D, bytes);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / CPR, col = (idx % CPR) * 8;
-      const int key = k0 + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      rk[c] = key < nkv ? ld_u32x4(K + (size_t)key * D + col) : z;
-      rv[c] = key < nkv ? ld_u32x4(V + (size_t)key * D + col) : z;
+      rk[c] = buf_ld16(rsk, voff[c]);
+      rv[c] = buf_ld16(rsv, voff[c]);
     }
   };
   auto store_tile = [&](int buf) {
@@ -184,6 +186,7 @@ void k_fwd(AttnArgs a) {
     load_tile(0);
     store_tile(0);
   }
+  vmem_wait_all();
   __syncthreads();
   for (int it = 0; it < it_hi; ++it) step(it, BoolTag<false>());
   for (int it = it_hi; it < ntiles; ++it) step(it, BoolTag<true>());
