@@ -225,24 +225,55 @@ __device__ __forceinline__ int key_perm(int r) {
   return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 }
 
-// One 32-query sub-tile of k_dkdv for one wave (32 keys).  MASK selects the
-// boundary version (tails, causal diagonal); interior tiles skip all masking.
-template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void dkdv_tile(const bf16x8* kf, const bf16x8* vf, f32x16* dk,
-                                          f32x16* dv, const uint16_t* sQb, const uint16_t* sdOb,
-                                          const float* sLseb, const float* sDlb, uint16_t* myPF,
-                                          uint16_t* myDS, const RowOffsets<D>& ro,
-                                          const ColOffsets<D>& co, const ColOffsets<32>& cp,
-                                          int pw0, int pw1, int q0, int kw0, int nq, int nkv,
-                                          float sl2, float psc, int lane) {
+// Q^ and dO staging of k_dkdv: each ring buffer holds a BM-row tile of Q^
+// followed by the same rows of dO, as bf16 rows of D elements at a pitch of
+// D + 8 (16 bytes of padding keep both the 16-byte row reads and the
+// transpose reads free of bank conflicts on the 64-bank LDS).  With a
+// linear layout every k-block, d-block, sub-tile and tensor offset is a
+// compile-time immediate of the LDS instruction: a lane needs one address
+// register per access pattern and buffer.
+template <int D>
+struct DkdvStage {
+  static constexpr int P = D + 8;             // row pitch (elements)
+  static constexpr int DO = kDkvBM * P;       // dO rows after the Q^ rows
+  static constexpr int BUF = 2 * kDkvBM * P;  // one ring buffer
+  static constexpr int SUB = 32 * P;          // second 32-row sub-tile
+  // lane offsets: row reads (row l32, columns 8h..) and column reads (rows
+  // 8h + (l%16)/4, columns 16*((l/16)%2) + 4*(l%4)); the second half of a
+  // column operand is 4 rows further
+  __device__ static int row_off(int lane) { return (lane & 31) * P + 8 * (lane >> 5); }
+  __device__ static int col_off(int lane) {
+    const int j = lane & 15;
+    return (8 * (lane >> 5) + (j >> 2)) * P + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
+  }
+  // B operand of S^T / dP^T: Q^ (or dO) row block kb of the sub-tile at p
+  __device__ static bf16x8 rows(const uint16_t* p, int kb) { return ld_bf16x8(p + 16 * kb); }
+  // B operand of dK / dV: columns 32*db.. of query block kq of the sub-tile at p
+  __device__ static bf16x8 cols(const uint16_t* p, int kq, int db) {
+    return lds_operand_cols_at(p + 16 * kq * P + 32 * db, 0, 4 * P);
+  }
+};
+
+// One 32-query sub-tile of k_dkdv for one wave (32 keys), self-contained and
+// masked: the boundary tiles (causal diagonal, query tail, keys past nkv).
+// qa / qc: the sub-tile's Q^ rows at this lane's row / column read offsets.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dkdv_tile_masked(const bf16x8* kf, const bf16x8* vf, f32x16* dk,
+                                                 f32x16* dv, const uint16_t* qa,
+                                                 const uint16_t* qc, const float* sLseb,
+                                                 const float* sDlb, uint16_t* myPF, uint16_t* myDS,
+                                                 const ColOffsets<32>& cp, int pw0, int pw1,
+                                                 int q0, int kw0, int nq, int nkv, float sl2,
+                                                 float psc, int lane) {
+  using S = DkdvStage<D>;
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   const int h = lane >> 5, l32 = lane & 31;
   f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    s = mfma32x32x16(kf[kb], ld_bf16x8(sQb + ro.o[kb]), s);
-    dp = mfma32x32x16(vf[kb], ld_bf16x8(sdOb + ro.o[kb]), dp);
+    s = mfma32x32x16(kf[kb], S::rows(qa, kb), s);
+    dp = mfma32x32x16(vf[kb], S::rows(qa + S::DO, kb), dp);
   }
   // this lane: query q0 + l32, keys kw0 + 16h + v (v = 0..15)
   const int qj = q0 + l32;
@@ -252,13 +283,9 @@ __device__ __forceinline__ void dkdv_tile(const bf16x8* kf, const bf16x8* vf, f3
   float amax = 0.0f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    float x = __builtin_fmaf(s[v], sl2, -lse2);
-    if (MASK) {
-      const int key = kw0 + 16 * h + v;
-      const bool ok = qj < nq && key < nkv && (!CAUSAL || key <= qj);
-      x = ok ? x : -INFINITY;
-    }
-    const float pv = fast_exp2(x);
+    const int key = kw0 + 16 * h + v;
+    const bool ok = qj < nq && key < nkv && (!CAUSAL || key <= qj);
+    const float pv = fast_exp2(ok ? __builtin_fmaf(s[v], sl2, -lse2) : -INFINITY);
     ds[v] = pv * (dp[v] - dl);
     p[v] = pv * psc;
     amax = fmaxf(amax, p[v]);
@@ -286,10 +313,8 @@ __device__ __forceinline__ void dkdv_tile(const bf16x8* kf, const bf16x8* vf, f3
     const bf16x8 as = lds_operand_cols_at(myDS + 16 * kq * 32, cp.a[0], cp.b[0]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      dv[db] = mfma32x32x16(ap, lds_operand_cols_at(sdOb + 16 * kq * D, co.a[db], co.b[db]),
-                            dv[db]);
-      dk[db] = mfma32x32x16(as, lds_operand_cols_at(sQb + 16 * kq * D, co.a[db], co.b[db]),
-                            dk[db]);
+      dv[db] = mfma32x32x16(ap, S::cols(qc + S::DO, kq, db), dv[db]);
+      dk[db] = mfma32x32x16(as, S::cols(qc, kq, db), dk[db]);
     }
   }
   wave_lds_fence();
@@ -307,12 +332,13 @@ __device__ __forceinline__ void dkdv_slot(
     // sub-tile i: S^T/dP^T accumulators, lse (log2 units) and delta of this
     // lane's query, destination P^F/dS tiles
     const f32x16& s, const f32x16& dp, float lse2, float dl, uint16_t* pfB, uint16_t* dsB,
-    // sub-tile i-1: its P^F/dS tiles and its staged Q^/dO rows
-    const uint16_t* pfC, const uint16_t* dsC, const uint16_t* sQC, const uint16_t* sdOC,
-    // sub-tile i+1: its staged Q^/dO rows and the S^T/dP^T results
-    const uint16_t* sQA, const uint16_t* sdOA, f32x16& sA, f32x16& dA,
-    const bf16x8* kf, const bf16x8* vf, f32x16* dk, f32x16* dv, const RowOffsets<D>& ro,
-    const ColOffsets<D>& co, const ColOffsets<32>& cp, int pw0, int pw1, float sl2, float psc) {
+    // sub-tile i-1: its P^F/dS tiles and its staged Q^ rows (column reads)
+    const uint16_t* pfC, const uint16_t* dsC, const uint16_t* qc,
+    // sub-tile i+1: its staged Q^ rows (row reads) and the S^T/dP^T results
+    const uint16_t* qa, f32x16& sA, f32x16& dA,
+    const bf16x8* kf, const bf16x8* vf, f32x16* dk, f32x16* dv, const ColOffsets<32>& cp,
+    int pw0, int pw1, float sl2, float psc) {
+  using S = DkdvStage<D>;
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int NC = 4 * DB;  // dV/dK MFMAs (2 k-blocks of 16 queries x DB x {dV, dK})
@@ -321,28 +347,30 @@ __device__ __forceinline__ void dkdv_slot(
   static_assert(NC <= NS && NA <= NS, "MFMA streams must fit the VALU steps");
   // B operands of the C stream (column reads) and of the A stream (row reads)
   auto opC = [&](int k) __attribute__((always_inline)) {
-    const int kq = k / (2 * DB), db = (k / 2) % DB;
-    return (k & 1) ? lds_operand_cols_at(sQC + 16 * kq * D, co.a[db], co.b[db])
-                   : lds_operand_cols_at(sdOC + 16 * kq * D, co.a[db], co.b[db]);
+    return S::cols((k & 1) ? qc : qc + S::DO, k / (2 * DB), (k / 2) % DB);
   };
   auto opA = [&](int k) __attribute__((always_inline)) {
-    return ld_bf16x8(((k & 1) ? sdOA : sQA) + ro.o[k / 2]);
+    return S::rows((k & 1) ? qa + S::DO : qa, k / 2);
   };
-  bf16x8 apC[2], asC[2], bC[NS + 1], bA[NS + 1];
+  constexpr int PD = ATTNQAT_DKDV_PREFETCH;  // LDS operand reads run PD steps ahead
+  bf16x8 apC[2], asC[2], bC[NS + PD], bA[NS + PD];
   apC[0] = lds_operand_cols_at(pfC, cp.a[0], cp.b[0]);
   asC[0] = lds_operand_cols_at(dsC, cp.a[0], cp.b[0]);
-  bC[0] = opC(0);
-  bA[0] = opA(0);
+#pragma unroll
+  for (int k = 0; k < PD; ++k) {
+    if (k < NC) bC[k] = opC(k);
+    if (k < NA) bA[k] = opA(k);
+  }
   sA = zero_f32x16();
   dA = zero_f32x16();
   float p[16], ds[16], amax = 0.0f, sc = 0.0f;
   u32x4 pf[2], dsb[2];
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    // operands of the next step
-    if (k + 1 < NC) bC[k + 1] = opC(k + 1);
-    if (k + 1 < NA) bA[k + 1] = opA(k + 1);
-    if (k + 1 == 2 * DB) {
+    // operands PD steps ahead
+    if (k + PD < NC) bC[k + PD] = opC(k + PD);
+    if (k + PD < NA) bA[k + PD] = opA(k + PD);
+    if (k + PD == 2 * DB) {
       apC[1] = lds_operand_cols_at(pfC + 16 * 32, cp.a[0], cp.b[0]);
       asC[1] = lds_operand_cols_at(dsC + 16 * 32, cp.a[0], cp.b[0]);
     }
@@ -387,25 +415,25 @@ __device__ __forceinline__ void dkdv_slot(
 
 // S^T/dP^T MFMAs of one sub-tile alone (fills the pipeline).
 template <int D>
-__device__ __forceinline__ void dkdv_fill(const uint16_t* sQA, const uint16_t* sdOA, f32x16& sA,
-                                          f32x16& dA, const bf16x8* kf, const bf16x8* vf,
-                                          const RowOffsets<D>& ro) {
+__device__ __forceinline__ void dkdv_fill(const uint16_t* qa, f32x16& sA, f32x16& dA,
+                                          const bf16x8* kf, const bf16x8* vf) {
+  using S = DkdvStage<D>;
   constexpr int KB = D / 16;
   sA = zero_f32x16();
   dA = zero_f32x16();
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    sA = mfma32x32x16(kf[kb], ld_bf16x8(sQA + ro.o[kb]), sA);
-    dA = mfma32x32x16(vf[kb], ld_bf16x8(sdOA + ro.o[kb]), dA);
+    sA = mfma32x32x16(kf[kb], S::rows(qa, kb), sA);
+    dA = mfma32x32x16(vf[kb], S::rows(qa + S::DO, kb), dA);
   }
 }
 
 // dV/dK MFMAs of one sub-tile alone (drains the pipeline).
 template <int D>
 __device__ __forceinline__ void dkdv_drain(const uint16_t* pfC, const uint16_t* dsC,
-                                           const uint16_t* sQC, const uint16_t* sdOC, f32x16* dk,
-                                           f32x16* dv, const ColOffsets<D>& co,
+                                           const uint16_t* qc, f32x16* dk, f32x16* dv,
                                            const ColOffsets<32>& cp) {
+  using S = DkdvStage<D>;
   constexpr int DB = D / 32;
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq) {
@@ -413,10 +441,8 @@ __device__ __forceinline__ void dkdv_drain(const uint16_t* pfC, const uint16_t* 
     const bf16x8 as = lds_operand_cols_at(dsC + 16 * kq * 32, cp.a[0], cp.b[0]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      dv[db] = mfma32x32x16(ap, lds_operand_cols_at(sdOC + 16 * kq * D, co.a[db], co.b[db]),
-                            dv[db]);
-      dk[db] = mfma32x32x16(as, lds_operand_cols_at(sQC + 16 * kq * D, co.a[db], co.b[db]),
-                            dk[db]);
+      dv[db] = mfma32x32x16(ap, S::cols(qc + S::DO, kq, db), dv[db]);
+      dk[db] = mfma32x32x16(as, S::cols(qc, kq, db), dk[db]);
     }
   }
   wave_lds_fence();
@@ -440,6 +466,7 @@ __device__ __forceinline__ void dkdv_drain(const uint16_t* pfC, const uint16_t* 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_DKDV_WAVES, 8)))
 void k_dkdv(AttnArgs a) {
+  using S = DkdvStage<D>;
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int BM = kDkvBM;
@@ -447,8 +474,7 @@ void k_dkdv(AttnArgs a) {
   constexpr int CH = BM * CPR / 256;  // chunks per thread per tensor per tile
   constexpr int NBUF = 3;
   static_assert(BM == 64 && CH >= 1 && kDkvBN % BM == 0, "two 32-query sub-tiles per tile");
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[NBUF][BM * D];  // swizzled rows
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[NBUF][BM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sQO[NBUF * S::BUF];
   // per wave [query][key] tiles of P^F and dS, indexed by sub-tile parity
   __shared__ __attribute__((aligned(16))) uint16_t sPF[4][2][32 * 32];
   __shared__ __attribute__((aligned(16))) uint16_t sDS[4][2][32 * 32];
@@ -487,10 +513,10 @@ void k_dkdv(AttnArgs a) {
   }
   const float sl2 = a.softmax_scale * kLog2e;
   const float psc = a.p_scale;
-  // LDS offsets: Q^/dO row reads, their column reads (k-block rows 8h.., 8h+4..),
-  // and the per-wave [query][key] tiles (column reads and this lane's row writes)
-  const RowOffsets<D> ro(lane);
-  const ColOffsets<D> co(8 * h, 8 * h + 4, lane);
+  // LDS: this lane's row / column read positions in a staged tile, and its
+  // column reads and row writes of the per-wave [query][key] tiles
+  const uint16_t* const qrow = sQO + S::row_off(lane);
+  const uint16_t* const qcol = sQO + S::col_off(lane);
   const ColOffsets<32> cp(8 * h, 8 * h + 4, lane);
   const int pw0 = swz<32>(l32, 16 * h), pw1 = swz<32>(l32, 16 * h + 8);
   uint16_t* const pf0 = sPF[wave][0];
@@ -505,10 +531,12 @@ void k_dkdv(AttnArgs a) {
   u32x4 rq[CH], rd[CH];
   float rl = 0.0f, rdl = 0.0f;
   uint32_t voff[CH];  // byte offset of this thread's chunks within a tile
+  int soff[CH];       // their element offset in a staged buffer
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int idx = tid + 256 * c;
     voff[c] = (uint32_t)((idx / CPR) * D + (idx % CPR) * 8) * 2u;
+    soff[c] = (idx / CPR) * S::P + (idx % CPR) * 8;
   }
   auto load_tile = [&](int t) __attribute__((always_inline)) {
     // rows past nq read as zeros (masked out later); lse/delta are only
@@ -529,12 +557,11 @@ void k_dkdv(AttnArgs a) {
     }
   };
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    uint16_t* const b = sQO + buf * S::BUF;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / CPR, col = (idx % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&sQ[buf][swz<D>(r, col)]) = rq[c];
-      *reinterpret_cast<u32x4*>(&sdO[buf][swz<D>(r, col)]) = rd[c];
+      *reinterpret_cast<u32x4*>(b + soff[c]) = rq[c];
+      *reinterpret_cast<u32x4*>(b + S::DO + soff[c]) = rd[c];
     }
     if (tid < BM) {
       sLse[buf][tid] = rl * kLog2e;
@@ -551,10 +578,11 @@ void k_dkdv(AttnArgs a) {
   // wave's first key)
   auto masked_sub = [&](int t, int buf, int sub) __attribute__((always_inline)) {
     const int qs = qfirst + t * BM + 32 * sub;
+    const int o = buf * S::BUF + sub * S::SUB;
     if (!(CAUSAL && qs + 31 < kw0))
-      dkdv_tile<D, CAUSAL, true>(kf, vf, dk, dv, sQ[buf] + 32 * sub * D, sdO[buf] + 32 * sub * D,
-                                 sLse[buf] + 32 * sub, sDl[buf] + 32 * sub, pf0, ds0, ro, co, cp,
-                                 pw0, pw1, qs, kw0, nq, nkv, sl2, psc, lane);
+      dkdv_tile_masked<D, CAUSAL>(kf, vf, dk, dv, qrow + o, qcol + o, sLse[buf] + 32 * sub,
+                                  sDl[buf] + 32 * sub, pf0, ds0, cp, pw0, pw1, qs, kw0, nq, nkv,
+                                  sl2, psc, lane);
   };
   auto masked_step = [&](int t, int buf, int nbuf) __attribute__((always_inline)) {
     masked_sub(t, buf, 0);
@@ -597,25 +625,26 @@ void k_dkdv(AttnArgs a) {
     *reinterpret_cast<u32x4*>(ds1 + pw1) = z;
     wave_lds_fence();
     f32x16 s0, dp0, s1, dp1;
-    dkdv_fill<D>(sQ[buf], sdO[buf], s0, dp0, kf, vf, ro);
-    int pbuf = buf;  // buffer of the previous tile (the current one at first)
+    dkdv_fill<D>(qrow + buf * S::BUF, s0, dp0, kf, vf);
+    // column-read position in the previous tile's buffer (the current one at first)
+    const uint16_t* cprev = qcol + buf * S::BUF;
     for (; t < it_hi; ++t) {
       const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
-      const uint16_t* q = sQ[buf];
-      const uint16_t* o = sdO[buf];
+      const uint16_t* const rcur = qrow + buf * S::BUF;
+      const uint16_t* const rnext = qrow + nbuf * S::BUF;
+      const uint16_t* const ccur = qcol + buf * S::BUF;
       // sub-tile 0: C = sub-tile 1 of the previous tile, A = sub-tile 1
-      dkdv_slot<D>(s0, dp0, sLse[buf][l32], sDl[buf][l32], pf0, ds0, pf1, ds1,
-                   sQ[pbuf] + 32 * D, sdO[pbuf] + 32 * D, q + 32 * D, o + 32 * D, s1, dp1, kf,
-                   vf, dk, dv, ro, co, cp, pw0, pw1, sl2, psc);
+      dkdv_slot<D>(s0, dp0, sLse[buf][l32], sDl[buf][l32], pf0, ds0, pf1, ds1, cprev + S::SUB,
+                   rcur + S::SUB, s1, dp1, kf, vf, dk, dv, cp, pw0, pw1, sl2, psc);
       advance(t, nbuf);
       // sub-tile 1: C = sub-tile 0, A = sub-tile 0 of the next tile (its
       // result is unused after the last interior tile)
-      dkdv_slot<D>(s1, dp1, sLse[buf][32 + l32], sDl[buf][32 + l32], pf1, ds1, pf0, ds0, q, o,
-                   sQ[nbuf], sdO[nbuf], s0, dp0, kf, vf, dk, dv, ro, co, cp, pw0, pw1, sl2, psc);
-      pbuf = buf;
+      dkdv_slot<D>(s1, dp1, sLse[buf][32 + l32], sDl[buf][32 + l32], pf1, ds1, pf0, ds0, ccur,
+                   rnext, s0, dp0, kf, vf, dk, dv, cp, pw0, pw1, sl2, psc);
+      cprev = ccur;
       buf = nbuf;
     }
-    dkdv_drain<D>(pf1, ds1, sQ[pbuf] + 32 * D, sdO[pbuf] + 32 * D, dk, dv, co, cp);
+    dkdv_drain<D>(pf1, ds1, cprev + S::SUB, dk, dv, cp);
   }
   for (; t < ntiles; ++t) {
     const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;

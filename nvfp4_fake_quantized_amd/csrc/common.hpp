@@ -35,6 +35,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef ATTNQAT_DKDV_WAVES
 #define ATTNQAT_DKDV_WAVES 1
 #endif
+// Steps by which the dK/dV pipeline reads its LDS MFMA operands ahead.
+#ifndef ATTNQAT_DKDV_PREFETCH
+#define ATTNQAT_DKDV_PREFETCH 2
+#endif
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -236,8 +240,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Compiler-level ordering point for LDS traffic exchanged between the lanes
-// of one wave (LDS operations of a wave complete in issue order).
 // Returns x unchanged but makes the compiler materialize it here: the value
 // is computed before this point and not sunk towards its later uses (keeps a
 // hand-interleaved VALU stream where it was placed between scheduling fences).
@@ -252,6 +254,8 @@ __device__ __forceinline__ uint32_t pin_vgpr(uint32_t x) {
 // wait placement inside the loop only has to track the loop's own prefetches.
 __device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Compiler-level ordering point for LDS traffic exchanged between the lanes
+// of one wave (LDS operations of a wave complete in issue order).
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
