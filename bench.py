@@ -97,32 +97,46 @@ def read_traffic(kernel: str, workload: str, digest: str):
         return None
 
 
-def cpu_baseline(w, q, k, v, do):
-    """The oracle (fp64 NumPy) on one head of the same workload."""
+def cpu_baseline(w, q, k, v, do, min_seconds: float = 10.0):
+    """The oracle (fp64 NumPy, as it stands) on whole heads of the same
+    workload, head after head until its backward has run for ``min_seconds``
+    (or every head is done).  Each head's backward takes that head's oracle
+    forward outputs as stored (O_hp in bf16, lse in fp32)."""
+    import torch
+
     from oracle.attention import qat_backward_full_head, qat_forward_head
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # threadpoolctl missing or failing: fall back to the affinity set
         threads = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    o64, l64 = qat_forward_head(q[0, 0], k[0, 0], v[0, 0], w.softmax_scale, w.causal)
-    t1 = time.perf_counter()
-    import torch  # the backward's inputs as stored: O_hp in bf16, lse in fp32
-    o_in = torch.from_numpy(o64).to(torch.bfloat16)
-    l_in = torch.from_numpy(l64).float()
-    qat_backward_full_head(q[0, 0], k[0, 0], v[0, 0], o_in, do[0, 0], l_in, w.softmax_scale,
-                           w.causal)
-    t2 = time.perf_counter()
+    heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    t_fwd = t_bwd = 0.0
+    done = 0
+    for b, h in heads:
+        t0 = time.perf_counter()
+        o64, l64 = qat_forward_head(q[b, h], k[b, h], v[b, h], w.softmax_scale, w.causal)
+        t1 = time.perf_counter()
+        o_in = torch.from_numpy(o64).to(torch.bfloat16)
+        l_in = torch.from_numpy(l64).float()
+        t2 = time.perf_counter()
+        qat_backward_full_head(q[b, h], k[b, h], v[b, h], o_in, do[b, h], l_in,
+                               w.softmax_scale, w.causal)
+        t3 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_bwd += t3 - t2
+        done += 1
+        if t_bwd >= min_seconds:
+            break
     head_bwd_flops = w.bwd_flops() / (w.batch * w.heads)
     return {
-        "value": head_bwd_flops / (t2 - t1) / 1e12,
+        "value": done * head_bwd_flops / t_bwd / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"one head (b=0,h=0) of {w.name} (N={w.seqlen}, D={w.head_dim}); oracle "
-                   f"backward {t2 - t1:.2f} s (after its forward, {t1 - t0:.2f} s), counted "
-                   f"{head_bwd_flops / 1e9:.1f} GFLOP; host has "
+        "sample": (f"{done} of {len(heads)} heads of {w.name} (N={w.seqlen}, D={w.head_dim}), "
+                   f"whole heads; oracle backward {t_bwd:.2f} s (its forward {t_fwd:.2f} s), "
+                   f"counted {done * head_bwd_flops / 1e9:.1f} GFLOP; host has "
                    f"{len(os.sched_getaffinity(0))} usable cores"),
     }
 
