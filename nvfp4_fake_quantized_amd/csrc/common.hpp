@@ -15,6 +15,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -64,13 +65,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 // E4M3FN block scale of a group with max magnitude `amax` (finite, >= 0):
 // the E4M3FN value nearest to amax/6, ties to the even mantissa, saturating
-// at 448.  amax/6 is the correctly rounded fp32 quotient; for bf16 and fp32
-// amax it never lands on an E4M3 midpoint unless the exact quotient is that
-// midpoint (E4M3 midpoints have 5 significant bits; a non-exact quotient
-// stays more than half an fp32 ulp away from them), so rounding it again is
-// the exact rounding of amax/6.
+// at 448.  y approximates amax/6 by a product with the fp32 reciprocal of 6
+// and one FMA residual correction; rounding y to E4M3 as below gives the
+// exact rounding of amax/6 for every finite non-negative fp32 amax (checked
+// exhaustively over all 2^31 - 2^23 such values against exact comparisons
+// with 6 times the E4M3 midpoints).  The plain product alone does not.
 __device__ __forceinline__ float e4m3_scale_from_amax(float amax) {
-  const float y = amax / 6.0f;  // IEEE division (no fast-math in this library)
+  constexpr float kSixth = 1.0f / 6.0f;
+  const float y0 = amax * kSixth;
+  const float y = __builtin_fmaf(__builtin_fmaf(-y0, 6.0f, amax), kSixth, y0);
   float s;
   if (y < 0x1p-6f) {
     // subnormal E4M3 range: multiples of 2^-9 (y * 512 is exact)
@@ -127,15 +130,43 @@ struct FastP {
   float s, r;
   __device__ __forceinline__ explicit FastP(float scale)
       : s(scale), r(scale > 0.0f ? __builtin_amdgcn_rcpf(scale) : 0.0f) {}
-  // quantize-dequantize a pair (x0, x1 >= 0)
-  __device__ __forceinline__ void pair(float x0, float x1, float& y0, float& y1) const {
-    const float a0 = x0 * r, a1 = x1 * r;
-    const float q0 = __builtin_fmaf(__builtin_fmaf(-a0, s, x0), r, a0);
-    const float q1 = __builtin_fmaf(__builtin_fmaf(-a1, s, x1), r, a1);
+  // the refined quotient x / s (x >= 0)
+  __device__ __forceinline__ float quotient(float x) const {
+    const float a = x * r;
+    return __builtin_fmaf(__builtin_fmaf(-a, s, x), r, a);
+  }
+  // E2M1-rounded quotients q0, q1 times the scale s
+  __device__ __forceinline__ static void dequant_pair(float q0, float q1, float s, float& y0,
+                                                      float& y1) {
     const uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q0, q1, 1.0f, 0);
     const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 0);
     y0 = c[0] * s;
     y1 = c[1] * s;
+  }
+  // E2M1 codes (RNE, saturating) of 8 quotients, packed 4 bits each: byte b
+  // holds the codes of elements 2b and 2b+1
+  __device__ __forceinline__ static uint32_t codes8(f32x4 lo, f32x4 hi) {
+    uint32_t p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, lo[0], lo[1], 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, lo[2], lo[3], 1.0f, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, hi[0], hi[1], 1.0f, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, hi[2], hi[3], 1.0f, 3);
+  }
+  // values of the two codes in byte `sel` of `codes`, times the scale s
+  __device__ __forceinline__ static void dequant_codes(uint32_t codes, int sel, float s,
+                                                       float& y0, float& y1) {
+    f32x2 c;
+    switch (sel) {  // the byte select is an instruction immediate
+      case 0: c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0); break;
+      case 1: c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1); break;
+      case 2: c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2); break;
+      default: c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3); break;
+    }
+    y0 = c[0] * s;
+    y1 = c[1] * s;
+  }
+  // quantize-dequantize a pair (x0, x1 >= 0)
+  __device__ __forceinline__ void pair(float x0, float x1, float& y0, float& y1) const {
+    dequant_pair(quotient(x0), quotient(x1), s, y0, y1);
   }
 };
 
