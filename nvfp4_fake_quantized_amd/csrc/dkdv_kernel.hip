@@ -10,36 +10,36 @@
 // gfx950 design (wave64, bf16 MFMA 32x32x16, fp32 accumulation).
 //
 // A workgroup of 8 waves owns 128 keys, as four pairs of waves that share a
-// SIMD (waves w and w+4).  The two waves of a pair split the work on their 32
-// keys by role, so that each issues the same number of MFMAs and a similar
-// VALU load (a lone wave issues VALU at only half of a SIMD's rate):
-//  * wave X (w < 4) keeps the pair's K^ rows and the dV accumulator.  Per
-//    32-query sub-tile j it computes S^T = K^ Q^T, P = exp2(S * s log2e -
-//    lse log2e), the group amax, the E4M3 scale and the refined quotients
-//    q = P / scale (q = P when the scale is 0), and hands q and the scale to
-//    Y through LDS.  Two steps later it reads P^F(j) back (from Y) and adds
-//    P^F^T dO to dV.
-//  * wave Y (w >= 4) keeps the V^ rows and the dK accumulator.  It computes
-//    dP^T = V^ dO^T for sub-tile j, and one step later (with q and the scale
-//    of sub-tile j) P ~ q * scale, dS = P (dP - delta), the E2M1 rounding of
-//    q (P^F = code * scale), writes P^F for X, and adds dS^T Q^ to dK.
-// One barrier per sub-tile orders the handovers.  P^F is exact: the E2M1
-// code comes from the FMA-refined quotient, which rounds like the exact
-// quotient (precise division).  P ~ q * scale differs from P by about one
-// fp32 ulp and only enters dS, which is rounded to bf16 for its MFMA.
+// SIMD (waves w and w+4).  A lone wave issues VALU at only half of a SIMD's
+// rate, so the two waves of a pair split the work on their 32 keys by role;
+// each issues 16 MFMAs per 32-query step and a similar VALU load, and their
+// instruction streams interleave on the SIMD:
+//  * wave X (w < 4) keeps the pair's K^ and V^ rows.  At step j it issues the
+//    MFMAs of S^T(j+1) = K^ Q^T and dP^T(j+1) = V^ dO^T (one step ahead, with
+//    operands read from LDS two MFMAs ahead) interleaved, element by element,
+//    with the VALU work on S^T(j) and dP^T(j) of the previous step:
+//    P = exp2(S s log2e - lse log2e), the group amax and E4M3 scale, and
+//    dS = P (dP - delta).  It hands P (fp32), the scale and the dS tile (bf16)
+//    to Y through LDS.
+//  * wave Y (w >= 4) keeps the dV and dK accumulators.  At step j it takes
+//    P, the scale and dS of sub-tile j-1, forms the refined quotients
+//    q = P / scale and their E2M1 codes (P^F = code * scale, exact: the code
+//    rounds like the exact quotient, i.e. precise division), and adds
+//    P^F^T dO to dV and dS^T Q^ to dK (operands prefetched from LDS).
+// One barrier per step orders the handover.
 //
 // In the S^T accumulator each lane holds one query and, because the K^/V^
 // rows are loaded in the permuted order pi, 16 *consecutive* keys: exactly
 // one P quantization group, so the amax and the scale are per-lane work.
 // The Q^/dO sub-tiles (32 queries) sit in a ring of four LDS slots
-// (XOR-swizzled rows; row reads for S/dP, transpose reads for dK/dV),
-// prefetched one step ahead through registers.  The step loops are unrolled
-// by the ring period, so every LDS address is a lane register plus an
-// immediate.  P^F and dS reach the A operands of dV and dK through per-pair
+// (XOR-swizzled rows; row reads for S/dP, transpose reads for dK/dV); X
+// waves stage them two steps ahead through registers.  The step loops are
+// unrolled by the ring period, so every LDS address is a lane register plus
+// an immediate.  P^F and dS reach the A operands of dV and dK through
 // [query][key] LDS tiles read back with transpose reads.
 //
 // Masks: only sub-tiles on a boundary (causal diagonal, query tail, keys past
-// nkv) evaluate them, in X (P = 0, hence q = 0, dS = 0 and P^F = 0); causal
+// nkv) evaluate them, in X (P = 0, hence dS = 0 and P^F = 0); causal
 // sub-tiles entirely above the diagonal are skipped by both waves.  Loads
 // beyond the ends read zeros and stores stop at the ends.
 #include <hip/hip_runtime.h>
@@ -54,7 +54,16 @@ namespace {
 constexpr int kKeys = 128;     // keys per workgroup
 constexpr int kSub = 32;       // queries per sub-tile
 constexpr int kThreads = 512;  // 4 X waves + 4 Y waves
+constexpr int kStagers = 256;  // the X waves stage the sub-tiles
 constexpr int kRing = 4;       // Q^/dO sub-tile slots (also the unroll factor)
+#ifndef ATTNQAT_DKDV_AHEAD
+#define ATTNQAT_DKDV_AHEAD 2
+#endif
+#ifndef ATTNQAT_DKDV_AHEAD_Y
+#define ATTNQAT_DKDV_AHEAD_Y 2
+#endif
+constexpr int kAhead = ATTNQAT_DKDV_AHEAD;     // X: MFMA operand reads issued this many MFMAs ahead
+constexpr int kAheadY = ATTNQAT_DKDV_AHEAD_Y;  // Y: the same
 
 template <int N>
 struct IntTag {
@@ -69,10 +78,10 @@ struct DkdvLds {
   static constexpr int RING = 0;                        // slot r: Q^ at 2r SUBT, dO at (2r+1) SUBT
   static constexpr int PAIR = RING + kRing * 2 * SUBT;  // per-pair buffers start here
   // offsets within the per-pair area
-  static constexpr int QB = 0;                       // q[pair][2][4 KB], [g][lane][4] floats
-  static constexpr int PF = QB + 4 * 2 * 4096;       // P^F[pair][2] 32x32 bf16 tiles
-  static constexpr int DS = PF + 4 * 2 * 2048;       // dS[pair] 32x32 bf16 tiles
-  static constexpr int SB = DS + 4 * 2048;           // scale[pair][2][64] floats
+  static constexpr int PB = 0;                       // P[pair][2][4 KB], [g][lane][4] floats
+  static constexpr int DS = PB + 4 * 2 * 4096;       // dS[pair][2] 32x32 bf16 tiles
+  static constexpr int PF = DS + 4 * 2 * 2048;       // P^F[pair] 32x32 bf16 tiles
+  static constexpr int SB = PF + 4 * 2048;           // scale[pair][2][64] floats
   static constexpr int LSE = SB + 4 * 2 * 256;       // lse[kRing][32] (raw)
   static constexpr int DL = LSE + kRing * kSub * 4;  // delta[kRing][32]
   static constexpr int TOTAL = PAIR + DL + kRing * kSub * 4;
@@ -91,8 +100,8 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
   constexpr int DB = D / 32;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int NCH = kSub * CPR;         // chunks per tensor per sub-tile
-  constexpr int CH = 2 * NCH / kThreads;  // chunks per thread per sub-tile
-  static_assert(CH >= 1 && (2 * NCH) % kThreads == 0 && NCH % 64 == 0,
+  constexpr int CH = 2 * NCH / kStagers;  // chunks per staging thread per sub-tile
+  static_assert(CH >= 1 && (2 * NCH) % kStagers == 0 && NCH % 64 == 0,
                 "sub-tile staging shape");
   static_assert(2 * kRing * L::SUBT <= 65536, "ring offsets fit LDS immediates");
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::TOTAL];
@@ -112,184 +121,211 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
   const float* LSE = a.lse + (size_t)bh * nq;
   const float* DL = a.delta + (size_t)bh * nq;
 
-  // X: K^ rows, Y: V^ rows of the pair's keys, in the order pi (A operands)
-  bf16x8 frag[KB];
-  {
-    const uint16_t* src = (is_x ? a.k_hat : a.v_hat) + ((size_t)bh * nkv + kblk0) * D;
-    const auto rs = make_rsrc(src, (uint32_t)(min(nkv - kblk0, kKeys) * D) * 2u);
-    const int row = 32 * kk + key_perm(l32);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      frag[kb] =
-          __builtin_bit_cast(bf16x8, buf_ld16(rs, (uint32_t)(row * D + 16 * kb + 8 * h) * 2u));
-  }
-
   // sub-tiles: queries below the workgroup's first key are masked (causal)
   const int qfirst = CAUSAL ? kblk0 : 0;
   const int nsub = qfirst < nq ? (nq - qfirst + kSub - 1) / kSub : 0;
-  const int nsteps = nsub > 0 ? nsub + 2 : 0;
+  const int nsteps = nsub > 0 ? nsub + 1 : 0;
   // a sub-tile entirely above the pair's keys (causal) is skipped by both waves
   auto skipped = [&](int j) __attribute__((always_inline)) {
     return CAUSAL && qfirst + kSub * j + kSub - 1 < kw0;
   };
-  const bool keys_tail = kw0 + 32 > nkv;
 
-  // ---- staging of sub-tile j (Q^ and dO rows, lse, delta) into slot j % kRing
-  u32x4 rst[CH];
-  float rl = 0.0f;
-  // this thread's chunk c: tensor (uniform per wave) and swizzled LDS offset
-  uint32_t goff[CH];
-  int loff[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int idx = tid + kThreads * c;
-    const int ch = idx % NCH;
-    goff[c] = (uint32_t)((ch / CPR) * D + (ch % CPR) * 8) * 2u;
-    loff[c] = 2 * swz<D>(ch / CPR, (ch % CPR) * 8);
-  }
-  auto load_sub = [&](int j) __attribute__((always_inline)) {
-    const int q0 = qfirst + kSub * j;
-    const int rows = min(nq - q0, kSub);
-    const uint32_t bytes = (uint32_t)(rows * D) * 2u;  // rows past nq read as zeros
-    const auto rsq = make_rsrc(Q + (size_t)q0 * D, bytes);
-    const auto rsd = make_rsrc(dO + (size_t)q0 * D, bytes);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const bool is_q = 64 * wave + kThreads * c < NCH;
-      rst[c] = buf_ld16(is_q ? rsq : rsd, goff[c]);
-    }
-    // wave 0 stages lse, wave 1 delta (lanes past the sub-tile read zeros)
-    if (wave < 2)
-      rl = buf_ldf(make_rsrc((wave == 0 ? LSE : DL) + q0, (uint32_t)rows * 4u),
-                   (uint32_t)lane * 4u);
-  };
-  auto store_sub = [&](auto rtag) __attribute__((always_inline)) {
-    constexpr int S = decltype(rtag)::value;  // ring slot
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const bool is_q = 64 * wave + kThreads * c < NCH;
-      *reinterpret_cast<u32x4*>(smem + L::RING + (2 * S + (is_q ? 0 : 1)) * L::SUBT + loff[c]) =
-          rst[c];
-    }
-    if (wave < 2 && lane < kSub)
-      reinterpret_cast<float*>(smem + L::PAIR + (wave == 0 ? L::LSE : L::DL))[S * kSub + lane] =
-          rl;
-  };
-
-  const float sl2 = a.softmax_scale * kLog2e;
-  const float psc = a.p_scale;
-  const RowOffsets<D> ro(lane);                     // row reads (S, dP B operands)
-  const ColOffsets<D> co(8 * h, 8 * h + 4, lane);   // column reads (dV, dK B operands)
-  const ColOffsets<32> cp(8 * h, 8 * h + 4, lane);  // key-column reads of P^F / dS tiles
-  const int pw0 = swz<32>(l32, 16 * h), pw1 = swz<32>(l32, 16 * h + 8);
-  uint8_t* const pair = smem + L::PAIR;
-  float* const qbuf = reinterpret_cast<float*>(pair + L::QB + kk * 2 * 4096);
-  float* const sbuf = reinterpret_cast<float*>(pair + L::SB + kk * 2 * 256);
-  uint16_t* const pftile = reinterpret_cast<uint16_t*>(pair + L::PF + kk * 2 * 2048);
-  uint16_t* const dstile = reinterpret_cast<uint16_t*>(pair + L::DS + kk * 2048);
-  const float* const slse = reinterpret_cast<const float*>(pair + L::LSE);
-  const float* const sdl = reinterpret_cast<const float*>(pair + L::DL);
   auto ring = [&](int slot, int tensor) __attribute__((always_inline)) {
     return reinterpret_cast<const uint16_t*>(smem + L::RING + (2 * slot + tensor) * L::SUBT);
   };
-
-  f32x16 acc[DB];  // X: dV, Y: dK (lane -> d, VGPR -> key)
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
-
-  if (nsub > 0) {
-    load_sub(0);
-    store_sub(IntTag<0>());
-  }
-  // the K^/V^ fragments have arrived: waits inside the step loops then only
-  // track the loops' own prefetches
-  vmem_wait_all();
-  __syncthreads();
-
-  // The stage prefetch and the barrier of a step are common to both roles.
-  auto step_common_begin = [&](int j) __attribute__((always_inline)) {
-    if (j + 1 < nsub) load_sub(j + 1);
-  };
-  auto step_common_end = [&](int j, auto rtag) __attribute__((always_inline)) {
-    constexpr int R = decltype(rtag)::value;
-    // slot (j+1) % kRing last held sub-tile j-3, whose last use (X, step
-    // j-1) is behind the previous barrier
-    if (j + 1 < nsub) store_sub(IntTag<(R + 1) % kRing>());
-    __syncthreads();
-  };
+  uint8_t* const pair = smem + L::PAIR;
+  float* const pbuf = reinterpret_cast<float*>(pair + L::PB + kk * 2 * 4096);
+  float* const sbuf = reinterpret_cast<float*>(pair + L::SB + kk * 2 * 256);
+  uint16_t* const dstile = reinterpret_cast<uint16_t*>(pair + L::DS + kk * 2 * 2048);
+  const int pw0 = swz<32>(l32, 16 * h), pw1 = swz<32>(l32, 16 * h + 8);  // tile row writes
 
   if (is_x) {
-    // ---- X, step j: S^T(j) -> P -> q(j), scale(j); dV += P^F(j-2)^T dO(j-2)
-    auto x_valu = [&](int j, const f32x16& s, auto rtag, auto mask_tag)
+    // K^ and V^ rows of the pair's keys, in the order pi (A operands)
+    bf16x8 kf[KB], vf[KB];
+    {
+      const size_t base = ((size_t)bh * nkv + kblk0) * D;
+      const uint32_t bytes = (uint32_t)(min(nkv - kblk0, kKeys) * D) * 2u;
+      const auto rk = make_rsrc(a.k_hat + base, bytes);
+      const auto rv = make_rsrc(a.v_hat + base, bytes);
+      const int row = 32 * kk + key_perm(l32);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint32_t off = (uint32_t)(row * D + 16 * kb + 8 * h) * 2u;
+        kf[kb] = __builtin_bit_cast(bf16x8, buf_ld16(rk, off));
+        vf[kb] = __builtin_bit_cast(bf16x8, buf_ld16(rv, off));
+      }
+    }
+    const bool keys_tail = kw0 + 32 > nkv;
+    const RowOffsets<D> ro(lane);  // row reads (S, dP B operands)
+
+    // ---- staging of sub-tile j (Q^ and dO rows, lse, delta) into slot j % kRing
+    u32x4 rst[CH];
+    float rl = 0.0f;
+    uint32_t goff[CH];
+    int loff[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + kStagers * c;
+      const int ch = idx % NCH;
+      goff[c] = (uint32_t)((ch / CPR) * D + (ch % CPR) * 8) * 2u;
+      loff[c] = 2 * swz<D>(ch / CPR, (ch % CPR) * 8);
+    }
+    auto load_sub = [&](int j) __attribute__((always_inline)) {
+      const int q0 = qfirst + kSub * j;
+      const int rows = min(nq - q0, kSub);
+      const uint32_t bytes = (uint32_t)(rows * D) * 2u;  // rows past nq read as zeros
+      const auto rsq = make_rsrc(Q + (size_t)q0 * D, bytes);
+      const auto rsd = make_rsrc(dO + (size_t)q0 * D, bytes);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const bool is_q = 64 * wave + kStagers * c < NCH;  // uniform per wave
+        rst[c] = buf_ld16(is_q ? rsq : rsd, goff[c]);
+      }
+      // wave 0 stages lse, wave 1 delta (lanes past the sub-tile read zeros)
+      if (wave < 2)
+        rl = buf_ldf(make_rsrc((wave == 0 ? LSE : DL) + q0, (uint32_t)rows * 4u),
+                     (uint32_t)lane * 4u);
+    };
+    auto store_sub = [&](auto rtag) __attribute__((always_inline)) {
+      constexpr int S = decltype(rtag)::value;  // ring slot
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const bool is_q = 64 * wave + kStagers * c < NCH;
+        *reinterpret_cast<u32x4*>(smem + L::RING + (2 * S + (is_q ? 0 : 1)) * L::SUBT +
+                                  loff[c]) = rst[c];
+      }
+      if (wave < 2 && lane < kSub)
+        reinterpret_cast<float*>(pair + (wave == 0 ? L::LSE : L::DL))[S * kSub + lane] = rl;
+    };
+
+    const float sl2 = a.softmax_scale * kLog2e;
+    const float psc = a.p_scale;
+    const float* const slse = reinterpret_cast<const float*>(pair + L::LSE);
+    const float* const sdl = reinterpret_cast<const float*>(pair + L::DL);
+    // MFMA k of a sub-tile (slot RN): S^T for even k, dP^T for odd k, over
+    // head-dim block k / 2
+    auto operand = [&](int k, auto rntag) __attribute__((always_inline)) {
+      constexpr int RN = decltype(rntag)::value;
+      return ld_bf16x8(ring(RN, k & 1) + ro.o[k >> 1]);
+    };
+
+    // One step: MFMAs of sub-tile j+1 (slot RN, when DO_M) interleaved with
+    // the VALU work on sub-tile j (slot R, when DO_V) from sc / dc.
+    auto x_step_body = [&](int j, auto rtag, auto dom_tag, auto dov_tag, auto mask_tag,
+                           const f32x16& sc, const f32x16& dc, f32x16& sn, f32x16& dn)
         __attribute__((always_inline)) {
       constexpr int R = decltype(rtag)::value;
+      constexpr int RN = (R + 1) % kRing;
+      constexpr bool DO_M = decltype(dom_tag)::value;
+      constexpr bool DO_V = decltype(dov_tag)::value;
       constexpr bool MASK = decltype(mask_tag)::value;
-      // this lane: query qj, keys kw0 + 16h + v; under MASK key v is valid
-      // when v < lim (below nkv, not above the query, query below nq)
-      const float lse2 = slse[R * kSub + l32] * kLog2e;
+      constexpr int NM = 2 * KB;  // MFMAs per sub-tile
+      bf16x8 b[NM];
+      if (DO_M) {
+#pragma unroll
+        for (int k = 0; k < kAhead; ++k) b[k] = operand(k, IntTag<RN>());
+      }
+      float lse2 = 0.0f, dl = 0.0f;
       int lim = 16;
-      if (MASK) {
-        const int qj = qfirst + kSub * j + l32;
-        lim = (CAUSAL ? min(nkv, qj + 1) : nkv) - (kw0 + 16 * h);
-        lim = qj < nq ? lim : 0;
-      }
-      float p[16];
-      float amax = 0.0f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = __builtin_fmaf(s[v], sl2, -lse2);
-        if (MASK) x = v < lim ? x : -INFINITY;
-        p[v] = UNIT_P ? fast_exp2(x) : fast_exp2(x) * psc;
-        amax = fmaxf(amax, p[v]);
-      }
-      // a zero scale (every P of the group underflows) divides by 1 instead:
-      // the handed-over value is then P itself, which Y still needs for dS
-      const float sc = e4m3_scale_from_amax(amax);
-      const FastP fq(sc > 0.0f ? sc : 1.0f);
-      float* qd = qbuf + (R & 1) * 1024;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 w = {fq.quotient(p[4 * g]), fq.quotient(p[4 * g + 1]),
-                         fq.quotient(p[4 * g + 2]), fq.quotient(p[4 * g + 3])};
-        *reinterpret_cast<f32x4*>(qd + (g * 64 + lane) * 4) = w;
-      }
-      sbuf[(R & 1) * 64 + lane] = sc;
-    };
-    auto x_step = [&](int j, auto rtag) __attribute__((always_inline)) {
-      constexpr int R = decltype(rtag)::value;
-      if (j >= nsteps) return;
-      step_common_begin(j);
-      const bool do_s = j < nsub && !skipped(j);
-      const bool do_v = j >= 2 && !skipped(j - 2);
-      f32x16 s;
-      if (do_s) {
-        const uint16_t* sQ = ring(R, 0);
-        s = mfma32x32x16(frag[0], ld_bf16x8(sQ + ro.o[0]), zero_f32x16());
-#pragma unroll
-        for (int kb = 1; kb < KB; ++kb) s = mfma32x32x16(frag[kb], ld_bf16x8(sQ + ro.o[kb]), s);
-      }
-      if (do_v) {
-        // P^F(j-2) was written by Y at step j-1 into tile (j-2) & 1 = R & 1
-        const uint16_t* pt = pftile + (R & 1) * 1024;
-        const uint16_t* sDO = ring((R + 2) % kRing, 1);
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-          const bf16x8 ap = lds_operand_cols_at(pt + 16 * kq * 32, cp.a[0], cp.b[0]);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            acc[db] = mfma32x32x16(
-                ap, lds_operand_cols_at(sDO + 16 * kq * D, co.a[db], co.b[db]), acc[db]);
+      if (DO_V) {
+        lse2 = slse[R * kSub + l32] * kLog2e;
+        dl = sdl[R * kSub + l32];
+        // this lane: query qj, keys kw0 + 16h + v; under MASK key v is valid
+        // when v < lim (below nkv, not above the query, query below nq)
+        if (MASK) {
+          const int qj = qfirst + kSub * j + l32;
+          lim = (CAUSAL ? min(nkv, qj + 1) : nkv) - (kw0 + 16 * h);
+          lim = qj < nq ? lim : 0;
         }
       }
-      if (do_s) {
-        const int q0 = qfirst + kSub * j;
-        // masks: keys past nkv, the query tail, the causal diagonal
-        if (keys_tail || q0 + kSub > nq || (CAUSAL && q0 < kw0 + 31))
-          x_valu(j, s, rtag, BoolTag<true>());
-        else
-          x_valu(j, s, rtag, BoolTag<false>());
+      float p[16], ds[16];
+      float amax = 0.0f;
+      constexpr int NSLOT = NM > 16 ? NM : 16;
+#pragma unroll
+      for (int k = 0; k < NSLOT; ++k) {
+        if (DO_M && k < NM) {
+          if (k + kAhead < NM) b[k + kAhead] = operand(k + kAhead, IntTag<RN>());
+          if (k & 1)
+            dn = mfma32x32x16(vf[k >> 1], b[k], k == 1 ? zero_f32x16() : dn);
+          else
+            sn = mfma32x32x16(kf[k >> 1], b[k], k == 0 ? zero_f32x16() : sn);
+        }
+        if (DO_V && k < 16) {  // element k of this lane's 16
+          float x = __builtin_fmaf(sc[k], sl2, -lse2);
+          if (MASK) x = k < lim ? x : -INFINITY;
+          const float pv = fast_exp2(x);
+          ds[k] = pv * (dc[k] - dl);
+          p[k] = UNIT_P ? pv : pv * psc;
+          amax = fmaxf(amax, p[k]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      step_common_end(j, rtag);
+      if (DO_V) {
+        // dS rows -> tile (j & 1); P and its group scale -> handover buffer
+        u32x4 dsb[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsb[i >> 2][i & 3] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+        uint16_t* dt = dstile + (R & 1) * 1024;
+        *reinterpret_cast<u32x4*>(dt + pw0) = dsb[0];
+        *reinterpret_cast<u32x4*>(dt + pw1) = dsb[1];
+        float* pd = pbuf + (R & 1) * 1024;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 w = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+          *reinterpret_cast<f32x4*>(pd + (g * 64 + lane) * 4) = w;
+        }
+        sbuf[(R & 1) * 64 + lane] = e4m3_scale_from_amax(amax);
+      }
+    };
+
+    // prologue: sub-tiles 0 and 1 staged, S^T(0) and dP^T(0)
+    if (nsub > 0) {
+      load_sub(0);
+      store_sub(IntTag<0>());
+    }
+    if (nsub > 1) {
+      load_sub(1);
+      store_sub(IntTag<1>());
+    }
+    vmem_wait_all();  // in-loop waits then only track the loop's own prefetches
+    __syncthreads();
+    f32x16 s_even, d_even, s_odd, d_odd;  // S^T / dP^T of even and odd sub-tiles
+    if (nsub > 0 && !skipped(0))
+      x_step_body(-1, IntTag<kRing - 1>(), BoolTag<true>(), BoolTag<false>(),
+                  BoolTag<false>(), s_odd, d_odd, s_even, d_even);
+
+    auto x_step = [&](int j, auto rtag) __attribute__((always_inline)) {
+      constexpr int R = decltype(rtag)::value;  // j % kRing
+      if (j >= nsteps) return;
+      f32x16& sc = (R & 1) ? s_odd : s_even;
+      f32x16& dc = (R & 1) ? d_odd : d_even;
+      f32x16& sn = (R & 1) ? s_even : s_odd;
+      f32x16& dn = (R & 1) ? d_even : d_odd;
+      if (j + 2 < nsub) load_sub(j + 2);
+      const bool do_m = j + 1 < nsub && !skipped(j + 1);
+      const bool do_v = j < nsub && !skipped(j);
+      const int q0 = qfirst + kSub * j;
+      // masks: keys past nkv, the query tail, the causal diagonal
+      const bool mask = keys_tail || q0 + kSub > nq || (CAUSAL && q0 < kw0 + 31);
+      if (do_m && do_v) {
+        if (mask)
+          x_step_body(j, rtag, BoolTag<true>(), BoolTag<true>(), BoolTag<true>(), sc, dc, sn, dn);
+        else
+          x_step_body(j, rtag, BoolTag<true>(), BoolTag<true>(), BoolTag<false>(), sc, dc, sn,
+                      dn);
+      } else if (do_m) {
+        x_step_body(j, rtag, BoolTag<true>(), BoolTag<false>(), BoolTag<false>(), sc, dc, sn, dn);
+      } else if (do_v) {
+        if (mask)
+          x_step_body(j, rtag, BoolTag<false>(), BoolTag<true>(), BoolTag<true>(), sc, dc, sn,
+                      dn);
+        else
+          x_step_body(j, rtag, BoolTag<false>(), BoolTag<true>(), BoolTag<false>(), sc, dc, sn,
+                      dn);
+      }
+      // slot (j+2) % kRing last held sub-tile j-2, last used by Y at step j-1
+      if (j + 2 < nsub) store_sub(IntTag<(R + 2) % kRing>());
+      __syncthreads();
     };
     for (int j0 = 0; j0 < nsteps; j0 += kRing) {
       x_step(j0, IntTag<0>());
@@ -298,66 +334,77 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       x_step(j0 + 3, IntTag<3>());
     }
   } else {
-    // ---- Y, step j: dS(j-1), P^F(j-1) -> LDS, dK += dS(j-1)^T Q^(j-1); dP^T(j)
-    f32x16 dp = zero_f32x16();  // dP^T of the sub-tile handled next step
+    // ---- Y, step j: P^F(j-1); dV += P^F^T dO(j-1), dK += dS^T Q^(j-1)
+    const float psc = a.p_scale;
+    const ColOffsets<D> co(8 * h, 8 * h + 4, lane);   // column reads (dV, dK B operands)
+    const ColOffsets<32> cp(8 * h, 8 * h + 4, lane);  // key-column reads of P^F / dS tiles
+    uint16_t* const pftile = reinterpret_cast<uint16_t*>(pair + L::PF + kk * 2048);
+    f32x16 dv[DB], dk[DB];  // lane -> d, VGPR -> key
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dv[db] = zero_f32x16();
+      dk[db] = zero_f32x16();
+    }
+    vmem_wait_all();
+    __syncthreads();  // the prologue barrier of the X waves
+
     auto y_step = [&](int j, auto rtag) __attribute__((always_inline)) {
-      constexpr int R = decltype(rtag)::value;
+      constexpr int R = decltype(rtag)::value;     // j % kRing
       constexpr int RP = (R + kRing - 1) % kRing;  // slot of sub-tile j-1
       if (j >= nsteps) return;
-      step_common_begin(j);
-      const bool do_k = j >= 1 && j - 1 < nsub && !skipped(j - 1);
-      const bool do_p = j < nsub && !skipped(j);
-      if (do_k) {
-        const float* qs = qbuf + (RP & 1) * 1024;
+      if (j >= 1 && !skipped(j - 1)) {  // j - 1 < nsub holds for j < nsteps
+        const float* ps = pbuf + (RP & 1) * 1024;
         const float sc = sbuf[(RP & 1) * 64 + lane];
-        // P = q * divisor / p_scale (the divisor is 1 for a zero scale);
-        // P^F = code * scale is then 0 for a zero scale
-        const float sdiv = sc > 0.0f ? sc : 1.0f;
-        const float sp = UNIT_P ? sdiv : sdiv / psc;
-        const float dl = sdl[RP * kSub + l32];
-        u32x4 pf[2], dsb[2];
+        // a zero scale divides by 1 instead (its codes are then multiplied by 0)
+        const FastP fq(sc > 0.0f ? sc : 1.0f);
         f32x4 q4[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          q4[g] = *reinterpret_cast<const f32x4*>(qs + (g * 64 + lane) * 4);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(ps + (g * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q4[g][e] = fq.quotient(p4[e]);
+        }
         // E2M1 codes of the 16 quotients, 8 to a dword
         const uint32_t codes[2] = {FastP::codes8(q4[0], q4[1]), FastP::codes8(q4[2], q4[3])};
+        u32x4 pf[2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float y[4], d[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) d[e] = q4[g][e] * sp * (dp[4 * g + e] - dl);
-          FastP::dequant_codes(codes[g >> 1], 2 * (g & 1), sc, y[0], y[1]);
-          FastP::dequant_codes(codes[g >> 1], 2 * (g & 1) + 1, sc, y[2], y[3]);
-          pf[g >> 1][2 * (g & 1)] = pack_bf16x2(y[0], y[1]);
-          pf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(y[2], y[3]);
-          dsb[g >> 1][2 * (g & 1)] = pack_bf16x2(d[0], d[1]);
-          dsb[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(d[2], d[3]);
+        for (int i = 0; i < 8; ++i) {
+          float y0, y1;
+          FastP::dequant_codes(codes[i >> 2], i & 3, sc, y0, y1);
+          pf[i >> 2][i & 3] = pack_bf16x2(y0, y1);
         }
-        uint16_t* pt = pftile + (RP & 1) * 1024;
-        *reinterpret_cast<u32x4*>(pt + pw0) = pf[0];
-        *reinterpret_cast<u32x4*>(pt + pw1) = pf[1];
-        *reinterpret_cast<u32x4*>(dstile + pw0) = dsb[0];
-        *reinterpret_cast<u32x4*>(dstile + pw1) = dsb[1];
+        *reinterpret_cast<u32x4*>(pftile + pw0) = pf[0];
+        *reinterpret_cast<u32x4*>(pftile + pw1) = pf[1];
         wave_lds_fence();
+        // MFMA k: kq = k / (2 DB), db = (k / 2) % DB; even k: dV, odd k: dK
+        const uint16_t* dt = dstile + (RP & 1) * 1024;
         const uint16_t* sQ = ring(RP, 0);
+        const uint16_t* sDO = ring(RP, 1);
+        constexpr int NM = 4 * DB;
+        const bf16x8 ap[2] = {lds_operand_cols_at(pftile, cp.a[0], cp.b[0]),
+                              lds_operand_cols_at(pftile + 16 * 32, cp.a[0], cp.b[0])};
+        const bf16x8 as[2] = {lds_operand_cols_at(dt, cp.a[0], cp.b[0]),
+                              lds_operand_cols_at(dt + 16 * 32, cp.a[0], cp.b[0])};
+        auto operand = [&](int k) __attribute__((always_inline)) {
+          const int kq = k / (2 * DB), db = (k / 2) % DB;
+          return lds_operand_cols_at(((k & 1) ? sQ : sDO) + 16 * kq * D, co.a[db], co.b[db]);
+        };
+        bf16x8 b[NM];
 #pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-          const bf16x8 as = lds_operand_cols_at(dstile + 16 * kq * 32, cp.a[0], cp.b[0]);
+        for (int k = 0; k < kAheadY; ++k) b[k] = operand(k);
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-            acc[db] = mfma32x32x16(
-                as, lds_operand_cols_at(sQ + 16 * kq * D, co.a[db], co.b[db]), acc[db]);
+        for (int k = 0; k < NM; ++k) {
+          if (k + kAheadY < NM) b[k + kAheadY] = operand(k + kAheadY);
+          const int kq = k / (2 * DB), db = (k / 2) % DB;
+          if (k & 1)
+            dk[db] = mfma32x32x16(as[kq], b[k], dk[db]);
+          else
+            dv[db] = mfma32x32x16(ap[kq], b[k], dv[db]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        wave_lds_fence();
       }
-      if (do_p) {
-        const uint16_t* sDO = ring(R, 1);
-        dp = mfma32x32x16(frag[0], ld_bf16x8(sDO + ro.o[0]), zero_f32x16());
-#pragma unroll
-        for (int kb = 1; kb < KB; ++kb) dp = mfma32x32x16(frag[kb], ld_bf16x8(sDO + ro.o[kb]), dp);
-      }
-      step_common_end(j, rtag);
+      (void)psc;
+      __syncthreads();
     };
     for (int j0 = 0; j0 < nsteps; j0 += kRing) {
       y_step(j0, IntTag<0>());
@@ -365,18 +412,22 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       y_step(j0 + 2, IntTag<2>());
       y_step(j0 + 3, IntTag<3>());
     }
-  }
 
-  // accumulators: lane -> d = 32*db + l32, VGPR v -> key kw0 + 8*(v/4) + 4h + v%4
-  const float osc = is_x ? (UNIT_P ? 1.0f : 1.0f / psc) : a.softmax_scale;
-  uint16_t* OUT = (is_x ? a.dv : a.dk) + (size_t)bh * nkv * D;
+    // accumulators: lane -> d = 32*db + l32, VGPR v -> key kw0 + 8*(v/4) + 4h + v%4
+    const float vsc = UNIT_P ? 1.0f : 1.0f / psc;
+    const float ksc = a.softmax_scale;
+    uint16_t* DV = a.dv + (size_t)bh * nkv * D;
+    uint16_t* DK = a.dk + (size_t)bh * nkv * D;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int key = kw0 + 8 * (v >> 2) + 4 * h + (v & 3);
-    if (key < nkv) {
+    for (int v = 0; v < 16; ++v) {
+      const int key = kw0 + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (key < nkv) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        OUT[(size_t)key * D + 32 * db + l32] = (uint16_t)f32_to_bf16_bits(acc[db][v] * osc);
+        for (int db = 0; db < DB; ++db) {
+          DV[(size_t)key * D + 32 * db + l32] = (uint16_t)f32_to_bf16_bits(dv[db][v] * vsc);
+          DK[(size_t)key * D + 32 * db + l32] = (uint16_t)f32_to_bf16_bits(dk[db][v] * ksc);
+        }
+      }
     }
   }
 }
