@@ -37,7 +37,8 @@
  *  - Limits (§Current support and limitations of the same page, plus
  *    head_dim 64): MHA only, head_dim in {64, 128}, causal is
  *    self-attention only (seqlen_q == seqlen_kv), no dropout, bias,
- *    padding masks or GQA.  NaN/Inf inputs are unsupported.
+ *    padding masks or GQA.  NaN/Inf inputs are unsupported.  At most 2^28
+ *    rows per tensor (batch * heads * max(seqlen_q, seqlen_kv)).
  */
 #ifndef ATTNQAT_H_
 #define ATTNQAT_H_
@@ -56,7 +57,7 @@ extern "C" {
 /* Status codes. */
 #define ATTNQAT_OK 0
 #define ATTNQAT_ERR_INVALID_ARGUMENT (-1) /* null pointer, size <= 0, non-finite or <= 0 scale */
-#define ATTNQAT_ERR_UNSUPPORTED (-2)      /* head_dim, causal cross-attention, device not gfx950 */
+#define ATTNQAT_ERR_UNSUPPORTED (-2)      /* head_dim, causal cross-attention, > 2^28 rows, device not gfx950 */
 #define ATTNQAT_ERR_MISALIGNED (-3)       /* a pointer is not 16-byte aligned */
 #define ATTNQAT_ERR_WORKSPACE_TOO_SMALL (-4)
 #define ATTNQAT_ERR_HIP (-5)              /* a HIP runtime call or kernel launch failed */

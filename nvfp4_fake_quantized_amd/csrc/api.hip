@@ -30,8 +30,11 @@ int validate_problem(const attnqat_problem* p) {
   if (p->causal != 0 && p->causal != 1) return ATTNQAT_ERR_INVALID_ARGUMENT;
   if (p->head_dim != 64 && p->head_dim != 128) return ATTNQAT_ERR_UNSUPPORTED;
   if (p->causal && p->seqlen_q != p->seqlen_kv) return ATTNQAT_ERR_UNSUPPORTED;
-  // batch*heads is the grid's y extent
-  if ((int64_t)p->batch * p->heads > 65535) return ATTNQAT_ERR_UNSUPPORTED;
+  // launch sizes: the codec launch has one thread per 16 values of a tensor
+  // (grid.x * block.x < 2^32); 2^28 rows is beyond what fits the device anyway
+  const int64_t rows = (int64_t)p->batch * p->heads *
+                       (p->seqlen_q > p->seqlen_kv ? p->seqlen_q : p->seqlen_kv);
+  if (rows > (int64_t)1 << 28) return ATTNQAT_ERR_UNSUPPORTED;
   return ATTNQAT_OK;
 }
 

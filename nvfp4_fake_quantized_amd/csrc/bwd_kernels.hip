@@ -32,6 +32,11 @@ constexpr int kDqBN = ATTNQAT_DQ_BN;      // keys per staged tile (k_dq; 32-key 
 // dQ
 
 // One 32-key sub-tile of k_dq for one wave (32 queries).
+#ifndef ATTNQAT_DQ_AHEAD
+#define ATTNQAT_DQ_AHEAD 2
+#endif
+constexpr int kDqAhead = ATTNQAT_DQ_AHEAD;  // MFMA operand reads issued this many MFMAs ahead
+
 template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dq_tile(const bf16x8* qf, const bf16x8* df, f32x16* acc,
                                         const uint16_t* sKb, const uint16_t* sVb,
@@ -40,13 +45,34 @@ __device__ __forceinline__ void dq_tile(const bf16x8* qf, const bf16x8* df, f32x
                                         float sl2, int lane) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
-  const int h = lane >> 5, l32 = lane & 31;
-  f32x16 s = zero_f32x16(), dp = zero_f32x16();
+  constexpr int NM = 2 * KB;  // S^T (even k) and dP^T (odd k) MFMAs
+  constexpr int NQ = 2 * DB;  // dQ^T MFMAs
+  const int h = lane >> 5;
+  // S^T = K^ Q^T and dP^T = V^ dO^T; A operands read from LDS kDqAhead MFMAs ahead
+  auto row_op = [&](int k) __attribute__((always_inline)) {
+    return ld_bf16x8(((k & 1) ? sVb : sKb) + ro.o[k >> 1]);
+  };
+  bf16x8 a[NM];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    s = mfma32x32x16(ld_bf16x8(sKb + ro.o[kb]), qf[kb], s);
-    dp = mfma32x32x16(ld_bf16x8(sVb + ro.o[kb]), df[kb], dp);
+  for (int k = 0; k < kDqAhead; ++k) a[k] = row_op(k);
+  f32x16 s, dp;
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    if (k + kDqAhead < NM) a[k + kDqAhead] = row_op(k + kDqAhead);
+    if (k & 1)
+      dp = mfma32x32x16(a[k], df[k >> 1], k == 1 ? zero_f32x16() : dp);
+    else
+      s = mfma32x32x16(a[k], qf[k >> 1], k == 0 ? zero_f32x16() : s);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // K^T operands of dQ^T = K^T dS^T (MFMA k: key block k / DB, d block k % DB),
+  // the first ones read while the VALU works
+  auto col_op = [&](int k) __attribute__((always_inline)) {
+    return lds_operand_cols_at(sKb + 16 * (k / DB) * D, co.a[k % DB], co.b[k % DB]);
+  };
+  bf16x8 c[NQ];
+#pragma unroll
+  for (int k = 0; k < kDqAhead; ++k) c[k] = col_op(k);
   float ds[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -60,17 +86,20 @@ __device__ __forceinline__ void dq_tile(const bf16x8* qf, const bf16x8* df, f32x
   }
   // dQ^T += K^T dS^T over two 16-key k-blocks: lane half h, element e of
   // k-block kh holds key 16*kh + 8*(e/4) + 4h + e%4 in both operands.
+  bf16x8 b[2];
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     const u32x4 bw = {pack_bf16x2(ds[8 * kh], ds[8 * kh + 1]),
                       pack_bf16x2(ds[8 * kh + 2], ds[8 * kh + 3]),
                       pack_bf16x2(ds[8 * kh + 4], ds[8 * kh + 5]),
                       pack_bf16x2(ds[8 * kh + 6], ds[8 * kh + 7])};
-    const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
+    b[kh] = __builtin_bit_cast(bf16x8, bw);
+  }
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      acc[db] = mfma32x32x16(lds_operand_cols_at(sKb + 16 * kh * D, co.a[db], co.b[db]), b,
-                             acc[db]);
+  for (int k = 0; k < NQ; ++k) {
+    if (k + kDqAhead < NQ) c[k + kDqAhead] = col_op(k + kDqAhead);
+    acc[k % DB] = mfma32x32x16(c[k], b[k / DB], acc[k % DB]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -89,9 +118,10 @@ void k_dq(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.y;
+  const TileId t = xcd_tile((a.nq + kDqBM - 1) / kDqBM);
+  const int bh = t.bh;
   const int nq = a.nq, nkv = a.nkv;
-  const int qblk0 = blockIdx.x * kDqBM;
+  const int qblk0 = t.tile * kDqBM;
   const int qw0 = qblk0 + wave * 32;
   const int qi = qw0 + l32;
   const bool qok = qi < nq;
@@ -199,7 +229,7 @@ void k_dq(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream) {
-  const dim3 grid((a.nq + kDqBM - 1) / kDqBM, a.bh);
+  const dim3 grid((unsigned)(((a.nq + kDqBM - 1) / kDqBM) * a.bh));
   if (head_dim == 128) {
     if (a.causal)
       hipLaunchKernelGGL((k_dq<128, true>), grid, dim3(256), 0, stream, a);

@@ -43,6 +43,31 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+#ifndef ATTNQAT_XCD_GROUP
+#define ATTNQAT_XCD_GROUP 1
+#endif
+constexpr int kNumXcd = 8;  // XCDs of an MI355X
+
+// Tile of a 1-D launch over (tiles per head) x (batch*heads). The dispatcher
+// deals workgroup ids out to the XCDs round-robin, so ids are renumbered to
+// give every XCD a contiguous run of logical ids, i.e. whole heads: the K/V
+// (or Q/dO) tiles that the workgroups of one head stream then hit that XCD's
+// own L2 instead of eight L2s each holding every head.
+struct TileId {
+  int tile, bh;
+};
+__device__ __forceinline__ TileId xcd_tile(int tiles_per_head) {
+  const int w = blockIdx.x;
+  int l = w;
+  if (ATTNQAT_XCD_GROUP) {
+    const int total = gridDim.x;
+    const int per = total / kNumXcd, rem = total % kNumXcd;
+    const int x = w % kNumXcd, slot = w / kNumXcd;
+    l = x < rem ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
+  }
+  return {l % tiles_per_head, l / tiles_per_head};
+}
+
 // Compile-time boolean carried through generic lambdas.
 template <bool B>
 struct BoolTag {

@@ -112,9 +112,10 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
   const int h = lane >> 5, l32 = lane & 31;
   const bool is_x = wave < 4;  // role
   const int kk = wave & 3;     // the pair's 32-key block
-  const int bh = blockIdx.y;
+  const TileId t = xcd_tile((a.nkv + kKeys - 1) / kKeys);
+  const int bh = t.bh;
   const int nq = a.nq, nkv = a.nkv;
-  const int kblk0 = blockIdx.x * kKeys;
+  const int kblk0 = t.tile * kKeys;
   const int kw0 = kblk0 + 32 * kk;
   const uint16_t* Q = a.q_hat + (size_t)bh * nq * D;
   const uint16_t* dO = a.d_o + (size_t)bh * nq * D;
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
 
 template <int D, bool CAUSAL>
 void launch_dkdv_d(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((a.nkv + kKeys - 1) / kKeys, a.bh);
+  const dim3 grid((unsigned)(((a.nkv + kKeys - 1) / kKeys) * a.bh));
   if (a.p_scale == 1.0f)
     hipLaunchKernelGGL((k_dkdv<D, CAUSAL, true>), grid, dim3(kThreads), 0, stream, a);
   else

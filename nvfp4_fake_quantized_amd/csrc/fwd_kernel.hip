@@ -106,9 +106,10 @@ void k_fwd(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.y;
+  const TileId t = xcd_tile((a.nq + kFwdBM - 1) / kFwdBM);
+  const int bh = t.bh;
   const int nq = a.nq, nkv = a.nkv;
-  const int qblk0 = blockIdx.x * kFwdBM;
+  const int qblk0 = t.tile * kFwdBM;
   const int qw0 = qblk0 + wave * 32;
   const int qi = qw0 + l32;
   const uint16_t* Q = a.q_hat + (size_t)bh * nq * D;
@@ -211,7 +212,7 @@ void k_fwd(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream) {
-  const dim3 grid((a.nq + kFwdBM - 1) / kFwdBM, a.bh);
+  const dim3 grid((unsigned)(((a.nq + kFwdBM - 1) / kFwdBM) * a.bh));
   if (head_dim == 128) {
     if (a.causal)
       hipLaunchKernelGGL((k_fwd<128, true>), grid, dim3(256), 0, stream, a);
