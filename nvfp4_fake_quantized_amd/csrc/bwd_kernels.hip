@@ -26,67 +26,51 @@ namespace attnqat {
 namespace {
 
 constexpr int kDqBM = 128;              // queries per workgroup (k_dq)
-constexpr int kDqBN = ATTNQAT_DQ_BN;      // keys per staged tile (k_dq; 32-key sub-tiles)
 
 // ---------------------------------------------------------------------------
 // dQ
 
-// One 32-key sub-tile of k_dq for one wave (32 queries).
 #ifndef ATTNQAT_DQ_AHEAD
 #define ATTNQAT_DQ_AHEAD 2
 #endif
 constexpr int kDqAhead = ATTNQAT_DQ_AHEAD;  // MFMA operand reads issued this many MFMAs ahead
 
-template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void dq_tile(const bf16x8* qf, const bf16x8* df, f32x16* acc,
-                                        const uint16_t* sKb, const uint16_t* sVb,
-                                        const RowOffsets<D>& ro, const ColOffsets<D>& co, int k0,
-                                        int qi, bool qok, int nkv, float lse2, float dl,
-                                        float sl2, int lane) {
-  constexpr int KB = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int NM = 2 * KB;  // S^T (even k) and dP^T (odd k) MFMAs
-  constexpr int NQ = 2 * DB;  // dQ^T MFMAs
-  const int h = lane >> 5;
-  // S^T = K^ Q^T and dP^T = V^ dO^T; A operands read from LDS kDqAhead MFMAs ahead
-  auto row_op = [&](int k) __attribute__((always_inline)) {
-    return ld_bf16x8(((k & 1) ? sVb : sKb) + ro.o[k >> 1]);
-  };
-  bf16x8 a[NM];
-#pragma unroll
-  for (int k = 0; k < kDqAhead; ++k) a[k] = row_op(k);
-  f32x16 s, dp;
-#pragma unroll
-  for (int k = 0; k < NM; ++k) {
-    if (k + kDqAhead < NM) a[k + kDqAhead] = row_op(k + kDqAhead);
-    if (k & 1)
-      dp = mfma32x32x16(a[k], df[k >> 1], k == 1 ? zero_f32x16() : dp);
-    else
-      s = mfma32x32x16(a[k], qf[k >> 1], k == 0 ? zero_f32x16() : s);
-    __builtin_amdgcn_sched_barrier(0);
+// Pieces of one wave's work on one 32-key block (32 queries x 32 keys).
+//
+// A operand of S^T/dP^T MFMA k (S^T = K^ Q^T for even k, dP^T = V^ dO^T for
+// odd k; d block k/2): rows of the K^ or V^ tile.
+template <int D>
+__device__ __forceinline__ bf16x8 dq_row_op(const uint16_t* sKb, const uint16_t* sVb,
+                                            const RowOffsets<D>& ro, int k) {
+  return ld_bf16x8(((k & 1) ? sVb : sKb) + ro.o[k >> 1]);
+}
+
+// S^T/dP^T MFMA k into s (even k) or dp (odd k).
+__device__ __forceinline__ void dq_sdp_mfma(int k, const bf16x8& a, const bf16x8* qf,
+                                            const bf16x8* df, f32x16& s, f32x16& dp) {
+  if (k & 1)
+    dp = mfma32x32x16(a, df[k >> 1], k == 1 ? zero_f32x16() : dp);
+  else
+    s = mfma32x32x16(a, qf[k >> 1], k == 0 ? zero_f32x16() : s);
+}
+
+// dS^T element v: lane half h holds key k0 + 8*(v/4) + 4h + v%4 of query qi.
+template <bool CAUSAL, bool MASK>
+__device__ __forceinline__ float dq_ds(float sv, float dpv, int v, int k0, int h, int qi, bool qok,
+                                       int nkv, float lse2, float dl, float sl2) {
+  float x = __builtin_fmaf(sv, sl2, -lse2);
+  if (MASK) {
+    const int key = k0 + 8 * (v >> 2) + 4 * h + (v & 3);
+    const bool ok = qok && key < nkv && (!CAUSAL || key <= qi);
+    x = ok ? x : -INFINITY;
   }
-  // K^T operands of dQ^T = K^T dS^T (MFMA k: key block k / DB, d block k % DB),
-  // the first ones read while the VALU works
-  auto col_op = [&](int k) __attribute__((always_inline)) {
-    return lds_operand_cols_at(sKb + 16 * (k / DB) * D, co.a[k % DB], co.b[k % DB]);
-  };
-  bf16x8 c[NQ];
-#pragma unroll
-  for (int k = 0; k < kDqAhead; ++k) c[k] = col_op(k);
-  float ds[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float x = __builtin_fmaf(s[v], sl2, -lse2);
-    if (MASK) {
-      const int key = k0 + 8 * (v >> 2) + 4 * h + (v & 3);
-      const bool ok = qok && key < nkv && (!CAUSAL || key <= qi);
-      x = ok ? x : -INFINITY;
-    }
-    ds[v] = fast_exp2(x) * (dp[v] - dl);
-  }
-  // dQ^T += K^T dS^T over two 16-key k-blocks: lane half h, element e of
-  // k-block kh holds key 16*kh + 8*(e/4) + 4h + e%4 in both operands.
-  bf16x8 b[2];
+  return fast_exp2(x) * (dpv - dl);
+}
+
+// dS^T as the two bf16 B operands of dQ^T = K^T dS^T (16-key k-blocks kh:
+// element e of k-block kh is key 16*kh + 8*(e/4) + 4h + e%4, matching the
+// K^T column reads).
+__device__ __forceinline__ void dq_pack(const float* ds, bf16x8* b) {
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     const u32x4 bw = {pack_bf16x2(ds[8 * kh], ds[8 * kh + 1]),
@@ -95,6 +79,79 @@ __device__ __forceinline__ void dq_tile(const bf16x8* qf, const bf16x8* df, f32x
                       pack_bf16x2(ds[8 * kh + 6], ds[8 * kh + 7])};
     b[kh] = __builtin_bit_cast(bf16x8, bw);
   }
+}
+
+// S^T and dP^T of one block, MFMAs only.
+template <int D>
+__device__ __forceinline__ void dq_sdp(const bf16x8* qf, const bf16x8* df, const uint16_t* sKb,
+                                       const uint16_t* sVb, const RowOffsets<D>& ro, f32x16& s,
+                                       f32x16& dp) {
+  constexpr int NM = D / 8;
+  bf16x8 a[NM];
+#pragma unroll
+  for (int k = 0; k < kDqAhead; ++k) a[k] = dq_row_op<D>(sKb, sVb, ro, k);
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    if (k + kDqAhead < NM) a[k + kDqAhead] = dq_row_op<D>(sKb, sVb, ro, k + kDqAhead);
+    dq_sdp_mfma(k, a[k], qf, df, s, dp);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// dS^T of the current block (VALU, into b) interleaved with dQ^T += K^T
+// dS^T of the previous block (MFMA, b_prev and that block's tile sKp): the
+// wave keeps the matrix pipe fed while it evaluates exp2.
+template <int D, bool CAUSAL, bool MASK, bool ACC>
+__device__ __forceinline__ void dq_ds_acc(const f32x16& s, const f32x16& dp, int k0, int h, int qi,
+                                          bool qok, int nkv, float lse2, float dl, float sl2,
+                                          bf16x8* b, f32x16* acc, const bf16x8* b_prev,
+                                          const uint16_t* sKp, const ColOffsets<D>& co) {
+  constexpr int DB = D / 32;
+  constexpr int NQ = 2 * DB;    // dQ^T MFMAs
+  constexpr int EPM = 16 / NQ;  // dS elements per MFMA
+  static_assert(EPM % 2 == 0, "elements are packed in pairs");
+  auto col_op = [&](int k) __attribute__((always_inline)) {
+    return lds_operand_cols_at(sKp + 16 * (k / DB) * D, co.a[k % DB], co.b[k % DB]);
+  };
+  bf16x8 c[NQ];
+  if (ACC) {
+#pragma unroll
+    for (int k = 0; k < kDqAhead; ++k) c[k] = col_op(k);
+  }
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    if (ACC) {
+      if (k + kDqAhead < NQ) c[k + kDqAhead] = col_op(k + kDqAhead);
+      acc[k % DB] = mfma32x32x16(c[k], b_prev[k / DB], acc[k % DB]);
+    }
+#pragma unroll
+    for (int e = 0; e < EPM; e += 2) {
+      const int v = EPM * k + e;
+      const float d0 = dq_ds<CAUSAL, MASK>(s[v], dp[v], v, k0, h, qi, qok, nkv, lse2, dl, sl2);
+      const float d1 =
+          dq_ds<CAUSAL, MASK>(s[v + 1], dp[v + 1], v + 1, k0, h, qi, qok, nkv, lse2, dl, sl2);
+      w[v >> 1] = pack_bf16x2(d0, d1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // element e of k-block kh is key 16*kh + 8*(e/4) + 4h + e%4 (dq_pack's order)
+  b[0] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+  b[1] = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
+}
+
+// dQ^T += K^T dS^T (MFMA k: 16-key k-block k / DB, d block k % DB).
+template <int D>
+__device__ __forceinline__ void dq_acc(f32x16* acc, const bf16x8* b, const uint16_t* sKb,
+                                       const ColOffsets<D>& co) {
+  constexpr int DB = D / 32;
+  constexpr int NQ = 2 * DB;
+  auto col_op = [&](int k) __attribute__((always_inline)) {
+    return lds_operand_cols_at(sKb + 16 * (k / DB) * D, co.a[k % DB], co.b[k % DB]);
+  };
+  bf16x8 c[NQ];
+#pragma unroll
+  for (int k = 0; k < kDqAhead; ++k) c[k] = col_op(k);
 #pragma unroll
   for (int k = 0; k < NQ; ++k) {
     if (k + kDqAhead < NQ) c[k + kDqAhead] = col_op(k + kDqAhead);
@@ -108,15 +165,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_DQ_
 void k_dq(AttnArgs a) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
-  constexpr int BN = kDqBN;
+  constexpr int BN = 32;              // keys per tile: one 32-key block
   constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int CH = BN * CPR / 256;  // chunks per thread per tensor per tile
-  static_assert(BN % 32 == 0 && CH >= 1, "key tile must be whole 32-key sub-tiles");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];  // swizzled rows
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
+  constexpr int CH = BN * CPR / 256;  // 16-byte chunks per lane per tensor per tile
+  constexpr int NB = 4;               // LDS ring: tiles it-1, it read while it+1, it+2 arrive
+  static_assert(CH >= 1, "tile copy needs at least one chunk per lane");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NB][BN * D];  // swizzled rows
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NB][BN * D];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const TileId t = xcd_tile((a.nq + kDqBM - 1) / kDqBM);
   const int bh = t.bh;
@@ -150,66 +208,84 @@ void k_dq(AttnArgs a) {
   const int kend = CAUSAL ? min(nkv, qblk0 + kDqBM) : nkv;
   const int ntiles = (kend + BN - 1) / BN;
 
-  u32x4 rk[CH], rv[CH];
-  uint32_t voff[CH];  // byte offset of this thread's chunks within a tile
+  // K^/V^ tiles go global -> LDS directly (no registers). Copy instruction c
+  // of this wave fills LDS chunk slots 64*(CH*wave + c) + lane; slot (row r,
+  // position j) of the XOR-swizzled layout holds column chunk swz(r, j), so
+  // each lane fetches that chunk (the swizzle is an involution).
+  uint32_t goff[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int idx = tid + 256 * c;
-    voff[c] = (uint32_t)((idx / CPR) * D + (idx % CPR) * 8) * 2u;
+    const int p = 64 * (CH * wave + c) + lane;
+    goff[c] = (uint32_t)swz<D>(p / CPR, 8 * (p % CPR)) * 2u;
   }
-  auto load_tile = [&](int k0) __attribute__((always_inline)) {
-    // rows past nkv read as zeros (masked out later)
+  auto issue_tile = [&](int it) __attribute__((always_inline)) {
+    const int k0 = it * BN;
+    const int buf = it % NB;
+    // rows past nkv arrive as zeros (masked out later)
     const uint32_t bytes = (uint32_t)(min(nkv - k0, BN) * D) * 2u;
-    const auto rsk = make_rsrc(K + (size_t)k0 * D, bytes);
-    const auto rsv = make_rsrc(V + (size_t)k0 * D, bytes);
+    const u32x4 dk = buf_desc(K + (size_t)k0 * D, bytes);
+    const u32x4 dv = buf_desc(V + (size_t)k0 * D, bytes);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      rk[c] = buf_ld16(rsk, voff[c]);
-      rv[c] = buf_ld16(rsv, voff[c]);
-    }
-  };
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / CPR, col = (idx % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&sK[buf][swz<D>(r, col)]) = rk[c];
-      *reinterpret_cast<u32x4*>(&sV[buf][swz<D>(r, col)]) = rv[c];
+      buf_ld16_lds(dk, goff[c],
+                   __builtin_amdgcn_readfirstlane(lds_addr(&sK[buf][512 * (CH * wave + c)])));
+      buf_ld16_lds(dv, goff[c],
+                   __builtin_amdgcn_readfirstlane(lds_addr(&sV[buf][512 * (CH * wave + c)])));
     }
   };
 
-  auto step = [&](int it, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = it & 1;
-    const int k0 = it * BN;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(k0 + BN);
-#pragma unroll
-    for (int sub = 0; sub < BN / 32; ++sub) {
-      const int ks = k0 + 32 * sub;
-      const uint16_t* kb = sK[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
-      const uint16_t* vb = sV[buf] + 32 * sub * D;
-      // (boundary tiles only) every key above every row of this wave: skip
-      if (!MASK || !(CAUSAL && qw0 + 31 < ks))
-        dq_tile<D, CAUSAL, MASK>(qf, df, acc, kb, vb, ro, co, ks, qi, qok, nkv, lse2, dl, sl2,
-                                 lane);
-    }
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-  };
   // Leading tiles are interior (branch-free); masks start at the first tile
   // that reaches past nkv or above the workgroup's first query (causal).
   int it_hi = min(ntiles, nkv / BN);
   if (CAUSAL) it_hi = min(it_hi, (qblk0 + 1) / BN);
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
   vmem_wait_all();
   __syncthreads();
-  for (int it = 0; it < it_hi; ++it) step(it, BoolTag<false>());
-  for (int it = it_hi; it < ntiles; ++it) step(it, BoolTag<true>());
+
+  // Software pipeline over tiles: step it runs the S^T/dP^T MFMAs of tile
+  // it, then its dS^T VALU work interleaved with the dQ^T MFMAs of tile it-1.
+  bf16x8 b_prev[2];
+  bool have_prev = false;
+  auto step = [&](int it, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int buf = it % NB;
+    const int pbuf = (it + NB - 1) % NB;
+    const int k0 = it * BN;
+    if (it + 2 < ntiles) issue_tile(it + 2);
+    // (boundary tiles only) every key above every query of this wave: skip;
+    // every later tile is then skipped too
+    if (!MASK || !(CAUSAL && qw0 + 31 < k0)) {
+      f32x16 s, dp;
+      dq_sdp<D>(qf, df, sK[buf], sV[buf], ro, s, dp);
+      bf16x8 b[2];
+      if (have_prev)
+        dq_ds_acc<D, CAUSAL, MASK, true>(s, dp, k0, h, qi, qok, nkv, lse2, dl, sl2, b, acc,
+                                         b_prev, sK[pbuf], co);
+      else
+        dq_ds_acc<D, CAUSAL, MASK, false>(s, dp, k0, h, qi, qok, nkv, lse2, dl, sl2, b, acc,
+                                          b_prev, sK[pbuf], co);
+      b_prev[0] = b[0];
+      b_prev[1] = b[1];
+      have_prev = true;
+    } else if (have_prev) {
+      dq_acc<D>(acc, b_prev, sK[pbuf], co);
+      have_prev = false;
+    }
+    // tile it+1 has landed (this wave's copies; the barrier covers the
+    // other waves'), tile it+2 may still be in flight
+    if (it + 2 < ntiles)
+      vmem_wait<2 * CH>();
+    else
+      vmem_wait<0>();
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it < it_hi; ++it) step(it, BoolTag<false>());
+  for (; it < ntiles; ++it) step(it, BoolTag<true>());
+  // the last block's dQ^T (its tile is still resident)
+  if (have_prev) dq_acc<D>(acc, b_prev, sK[(ntiles - 1) % NB], co);
 
   if (qok) {
     const float sc = a.softmax_scale;

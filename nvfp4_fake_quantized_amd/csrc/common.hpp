@@ -23,9 +23,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef ATTNQAT_FWD_BN
 #define ATTNQAT_FWD_BN 32  // keys per staged tile in the forward (32 or 64)
 #endif
-#ifndef ATTNQAT_DQ_BN
-#define ATTNQAT_DQ_BN 32  // keys per staged tile in the dQ kernel (32 or 64)
-#endif
 // Waves per SIMD the register allocation of each attention kernel targets.
 #ifndef ATTNQAT_FWD_WAVES
 #define ATTNQAT_FWD_WAVES 2
@@ -310,6 +307,14 @@ __device__ __forceinline__ uint32_t pin_vgpr(uint32_t x) {
 // wait placement inside the loop only has to track the loop's own prefetches.
 __device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations left
+// outstanding (they complete in issue order for loads).
+template <int N>
+__device__ __forceinline__ void vmem_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // Compiler-level ordering point for LDS traffic exchanged between the lanes
 // of one wave (LDS operations of a wave complete in issue order).
 __device__ __forceinline__ void wave_lds_fence() {
@@ -361,6 +366,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
+
+// Asynchronous copy of 16 bytes per lane straight into LDS
+// (buffer_load_dwordx4 ... lds): lane l's bytes land at LDS byte address
+// lds + 16*l, and lanes whose offset falls outside the descriptor's
+// num_records bytes write zeros.  `lds` must be wave-uniform.  Completion is
+// counted by vmcnt like any vector-memory load; the caller waits
+// (vmem_wait) and synchronizes before reading the destination.  Issued as
+// inline assembly so that the compiler does not add its own conservative
+// vmcnt waits in front of every later LDS read.
+__device__ __forceinline__ u32x4 buf_desc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p);
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; it is set right here
+__device__ __forceinline__ void buf_ld16_lds(const u32x4& desc, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(desc)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
