@@ -358,49 +358,68 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
         const float sc = sbuf[(RP & 1) * 64 + lane];
         // a zero scale divides by 1 instead (its codes are then multiplied by 0)
         const FastP fq(sc > 0.0f ? sc : 1.0f);
+        const uint16_t* dt = dstile + (RP & 1) * 1024;
+        const uint16_t* sQ = ring(RP, 0);
+        const uint16_t* sDO = ring(RP, 1);
+        constexpr int NH = 2 * DB;  // MFMAs per product (dK, dV)
+        // B operand of MFMA k of a product: 16-query k-block k / DB, d block k % DB
+        auto operand = [&](const uint16_t* tile, int k) __attribute__((always_inline)) {
+          return lds_operand_cols_at(tile + 16 * (k / DB) * D, co.a[k % DB], co.b[k % DB]);
+        };
+        // dK += dS^T Q^ first (dS arrived with the step), interleaved with the
+        // P^F VALU work: quotients, E2M1 codes, P^F = code * scale
+        const bf16x8 as[2] = {lds_operand_cols_at(dt, cp.a[0], cp.b[0]),
+                              lds_operand_cols_at(dt + 16 * 32, cp.a[0], cp.b[0])};
+        f32x4 p4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) p4[g] = *reinterpret_cast<const f32x4*>(ps + (g * 64 + lane) * 4);
+        bf16x8 b[NH];
+#pragma unroll
+        for (int k = 0; k < kAheadY; ++k) b[k] = operand(sQ, k);
         f32x4 q4[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(ps + (g * 64 + lane) * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q4[g][e] = fq.quotient(p4[e]);
-        }
-        // E2M1 codes of the 16 quotients, 8 to a dword
-        const uint32_t codes[2] = {FastP::codes8(q4[0], q4[1]), FastP::codes8(q4[2], q4[3])};
+        uint32_t codes[2];
         u32x4 pf[2];
+        // VALU share of dK MFMA k (NH = 8 for D = 128, 4 for D = 64)
+        auto valu_part = [&](int part, int nparts) __attribute__((always_inline)) {
+          // parts: quotient groups 0..3, then codes, then the 8 dequantized pairs
+          constexpr int NW = 4 + 1 + 8;  // work items
+          const int w0 = part * NW / nparts, w1 = (part + 1) * NW / nparts;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float y0, y1;
-          FastP::dequant_codes(codes[i >> 2], i & 3, sc, y0, y1);
-          pf[i >> 2][i & 3] = pack_bf16x2(y0, y1);
+          for (int w = 0; w < NW; ++w) {
+            if (w < w0 || w >= w1) continue;
+            if (w < 4) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) q4[w][e] = fq.quotient(p4[w][e]);
+            } else if (w == 4) {
+              codes[0] = FastP::codes8(q4[0], q4[1]);
+              codes[1] = FastP::codes8(q4[2], q4[3]);
+            } else {
+              const int i = w - 5;
+              float y0, y1;
+              FastP::dequant_codes(codes[i >> 2], i & 3, sc, y0, y1);
+              pf[i >> 2][i & 3] = pack_bf16x2(y0, y1);
+            }
+          }
+        };
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+          if (k + kAheadY < NH) b[k + kAheadY] = operand(sQ, k + kAheadY);
+          dk[k % DB] = mfma32x32x16(as[k / DB], b[k], dk[k % DB]);
+          valu_part(k, NH);
+          __builtin_amdgcn_sched_barrier(0);
         }
         *reinterpret_cast<u32x4*>(pftile + pw0) = pf[0];
         *reinterpret_cast<u32x4*>(pftile + pw1) = pf[1];
         wave_lds_fence();
-        // MFMA k: kq = k / (2 DB), db = (k / 2) % DB; even k: dV, odd k: dK
-        const uint16_t* dt = dstile + (RP & 1) * 1024;
-        const uint16_t* sQ = ring(RP, 0);
-        const uint16_t* sDO = ring(RP, 1);
-        constexpr int NM = 4 * DB;
+        // dV += P^F^T dO
         const bf16x8 ap[2] = {lds_operand_cols_at(pftile, cp.a[0], cp.b[0]),
                               lds_operand_cols_at(pftile + 16 * 32, cp.a[0], cp.b[0])};
-        const bf16x8 as[2] = {lds_operand_cols_at(dt, cp.a[0], cp.b[0]),
-                              lds_operand_cols_at(dt + 16 * 32, cp.a[0], cp.b[0])};
-        auto operand = [&](int k) __attribute__((always_inline)) {
-          const int kq = k / (2 * DB), db = (k / 2) % DB;
-          return lds_operand_cols_at(((k & 1) ? sQ : sDO) + 16 * kq * D, co.a[db], co.b[db]);
-        };
-        bf16x8 b[NM];
 #pragma unroll
-        for (int k = 0; k < kAheadY; ++k) b[k] = operand(k);
+        for (int k = 0; k < kAheadY; ++k) b[k] = operand(sDO, k);
 #pragma unroll
-        for (int k = 0; k < NM; ++k) {
-          if (k + kAheadY < NM) b[k + kAheadY] = operand(k + kAheadY);
-          const int kq = k / (2 * DB), db = (k / 2) % DB;
-          if (k & 1)
-            dk[db] = mfma32x32x16(as[kq], b[k], dk[db]);
-          else
-            dv[db] = mfma32x32x16(ap[kq], b[k], dv[db]);
+        for (int k = 0; k < NH; ++k) {
+          if (k + kAheadY < NH) b[k + kAheadY] = operand(sDO, k + kAheadY);
+          dv[k % DB] = mfma32x32x16(ap[k / DB], b[k], dv[k % DB]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
