@@ -55,7 +55,7 @@ def _compile(src: str, extra) -> str:
 def build(verbose: bool = False, extra_flags=(), out_dir: str | None = None) -> str:
     """Compiles every HIP source and links ``libattnqat.so`` into the package
     directory (or ``out_dir``); returns its path.  Always rebuilds.
-    ``extra_flags`` are passed to every compile (e.g. -DATTNQAT_FWD_BN=64)."""
+    ``extra_flags`` are passed to every compile (e.g. -DATTNQAT_DQ_AHEAD=3)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))

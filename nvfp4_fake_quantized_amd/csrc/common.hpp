@@ -20,9 +20,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Build-time tiling knobs (defaults are the tuned values).
-#ifndef ATTNQAT_FWD_BN
-#define ATTNQAT_FWD_BN 32  // keys per staged tile in the forward (32 or 64)
-#endif
 // Waves per SIMD the register allocation of each attention kernel targets.
 #ifndef ATTNQAT_FWD_WAVES
 #define ATTNQAT_FWD_WAVES 2

@@ -7,8 +7,10 @@
 //  * a workgroup of 4 waves owns 128 queries; each wave owns 32 queries and
 //    keeps its Q^ rows in registers as the B operand of S^T = K^ Q^T;
 //  * the key loop stages 32-key tiles of K^ and V^ row-major (XOR-swizzled
-//    16-byte chunks) in double-buffered LDS, prefetched one tile ahead
-//    through registers; the V^T operand is read with LDS transpose reads;
+//    16-byte chunks) in a 4-deep LDS ring, copied global -> LDS directly two
+//    tiles ahead; the V^T operand is read with LDS transpose reads;
+//  * software pipeline: step t issues the S^T MFMAs of tile t, then the
+//    softmax VALU work of tile t interleaved with the O^T MFMAs of tile t-1;
 //  * S^T's accumulator layout puts one query per lane (and 16 of its keys in
 //    VGPRs), so the online-softmax row statistics are per lane (plus one
 //    exchange with the lane 32 away), and P^T feeds the B operand of
@@ -31,64 +33,134 @@ namespace attnqat {
 namespace {
 
 constexpr int kFwdBM = 128;  // queries per workgroup
-constexpr int kFwdBN = ATTNQAT_FWD_BN;  // keys per staged tile (32-key sub-tiles)
+#ifndef ATTNQAT_FWD_AHEAD
+#define ATTNQAT_FWD_AHEAD 2
+#endif
+constexpr int kFwdAhead = ATTNQAT_FWD_AHEAD;  // MFMA operand reads issued this many MFMAs ahead
 
-// One 32-key tile for one wave (32 queries): online-softmax update of
-// (m, l, O^T).  m is the running row max in log2 units.
-template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void fwd_tile(const bf16x8* qf, f32x16* o, float& m, float& l,
-                                         const uint16_t* sKb, const uint16_t* sVb,
-                                         const RowOffsets<D>& ro, const ColOffsets<D>& co, int k0,
-                                         int qi, int nkv, float sl2, int lane) {
+// S^T = K^ Q^T of one 32-key tile (A operands read kFwdAhead MFMAs ahead).
+template <int D>
+__device__ __forceinline__ void fwd_s(const bf16x8* qf, const uint16_t* sKb,
+                                      const RowOffsets<D>& ro, f32x16& s) {
   constexpr int KB = D / 16;
-  constexpr int DB = D / 32;
-  const int h = lane >> 5, l32 = lane & 31;
-  f32x16 s = zero_f32x16();
+  bf16x8 a[KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-    s = mfma32x32x16(ld_bf16x8(sKb + ro.o[kb]), qf[kb], s);
-  float tmax = -INFINITY;
+  for (int k = 0; k < kFwdAhead; ++k) a[k] = ld_bf16x8(sKb + ro.o[k]);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float x = s[v] * sl2;
-    if (MASK) {
-      const int key = k0 + 8 * (v >> 2) + 4 * h + (v & 3);
-      const bool ok = key < nkv && (!CAUSAL || key <= qi);
-      x = ok ? x : -INFINITY;
-    }
-    s[v] = x;
-    tmax = fmaxf(tmax, x);
+  for (int k = 0; k < KB; ++k) {
+    if (k + kFwdAhead < KB) a[k + kFwdAhead] = ld_bf16x8(sKb + ro.o[k + kFwdAhead]);
+    s = mfma32x32x16(a[k], qf[k], k == 0 ? zero_f32x16() : s);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  tmax = fmaxf(tmax, xor32(tmax));
-  const float mnew = fmaxf(m, tmax);
-  // rescale only when some row's max moved; otherwise alpha would be exactly 1
-  if (__any(mnew > m)) {
-    const float alpha = fast_exp2(m - (mnew == -INFINITY ? 0.0f : mnew));
-    l *= alpha;
+}
+
+// O^T += V^T P^T of one tile (MFMA k: 16-key k-block k / DB, d block k % DB;
+// lane half h, element e of k-block kh holds key 16*kh + 8*(e/4) + 4h + e%4
+// in both operands).
+template <int D>
+__device__ __forceinline__ bf16x8 fwd_v_op(const uint16_t* sVb, const ColOffsets<D>& co, int k) {
+  constexpr int DB = D / 32;
+  return lds_operand_cols_at(sVb + 16 * (k / DB) * D, co.a[k % DB], co.b[k % DB]);
+}
+template <int D>
+__device__ __forceinline__ void fwd_pv(f32x16* o, const bf16x8* b, const uint16_t* sVb,
+                                       const ColOffsets<D>& co) {
+  constexpr int DB = D / 32;
+  constexpr int NQ = 2 * DB;
+  bf16x8 c[NQ];
+#pragma unroll
+  for (int k = 0; k < kFwdAhead; ++k) c[k] = fwd_v_op<D>(sVb, co, k);
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    if (k + kFwdAhead < NQ) c[k + kFwdAhead] = fwd_v_op<D>(sVb, co, k + kFwdAhead);
+    o[k % DB] = mfma32x32x16(c[k], b[k / DB], o[k % DB]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// O^T *= alpha when the row max moved at the previous tile (its pending
+// factor); the caller applies it before adding that tile's P^T V^.
+template <int D>
+__device__ __forceinline__ void fwd_rescale(f32x16* o, bool& pending, float alpha) {
+  constexpr int DB = D / 32;
+  if (pending) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    pending = false;
   }
+}
+
+// Online-softmax update of (m, l) with the S^T of one tile (m: running row
+// max in log2 units), producing P^T in bf16 (b), interleaved with the O^T
+// MFMAs of the previous tile (b_prev, sVp) when ACC.  O^T then holds every
+// earlier tile against the old max; when the max moved (for some row of the
+// wave), the factor exp2(m_old - m_new) is left pending in (pending, alpha)
+// and applied to O^T before this tile's P^T V^ is added.
+template <int D, bool CAUSAL, bool MASK, bool ACC>
+__device__ __forceinline__ void fwd_softmax_pv(const f32x16& s, float& m, float& l, bf16x8* b,
+                                               f32x16* o, const bf16x8* b_prev,
+                                               const uint16_t* sVp, const ColOffsets<D>& co,
+                                               bool& pending, float& alpha, int k0, int h,
+                                               int qi, int nkv, float sl2) {
+  constexpr int DB = D / 32;
+  constexpr int NQ = 2 * DB;
+  if (ACC) fwd_rescale<D>(o, pending, alpha);
+  // VALU work items: 16 scaled (and masked) scores with the running tile max,
+  // the row max across the lane pair, 16 exponentials with their sum, 8 packs
+  constexpr int NW = 16 + 1 + 16 + 8;
+  bf16x8 c[NQ];
+  if (ACC) {
+#pragma unroll
+    for (int k = 0; k < kFwdAhead; ++k) c[k] = fwd_v_op<D>(sVp, co, k);
+  }
+  float tmax = -INFINITY, mnew = m, base = 0.0f, psum = 0.0f;
+  float xs[16], pv[16];
+  uint32_t w[8];
+  auto item = [&](int i) __attribute__((always_inline)) {
+    if (i < 16) {
+      float x = s[i] * sl2;
+      if (MASK) {
+        const int key = k0 + 8 * (i >> 2) + 4 * h + (i & 3);
+        const bool ok = key < nkv && (!CAUSAL || key <= qi);
+        x = ok ? x : -INFINITY;
+      }
+      xs[i] = x;
+      tmax = fmaxf(tmax, x);
+    } else if (i == 16) {
+      tmax = fmaxf(tmax, xor32(tmax));
+      mnew = fmaxf(m, tmax);
+      base = (mnew == -INFINITY) ? 0.0f : mnew;
+    } else if (i < 33) {
+      const int e = i - 17;
+      pv[e] = fast_exp2(xs[e] - base);
+      psum += pv[e];
+    } else {
+      const int e = i - 33;
+      w[e] = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    if (ACC) {
+      if (k + kFwdAhead < NQ) c[k + kFwdAhead] = fwd_v_op<D>(sVp, co, k + kFwdAhead);
+      o[k % DB] = mfma32x32x16(c[k], b_prev[k / DB], o[k % DB]);
+    }
+    const int i0 = k * NW / NQ, i1 = (k + 1) * NW / NQ;
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      if (i >= i0 && i < i1) item(i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  b[0] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+  b[1] = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
+  // rescale only when some row's max moved; otherwise alpha would be exactly 1
+  if (__any(mnew > m)) {
+    alpha = fast_exp2(m - base);
+    l *= alpha;
+    pending = true;
+  }
+  l += psum;
   m = mnew;
-  const float base = (mnew == -INFINITY) ? 0.0f : mnew;
-  float pv[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    pv[v] = fast_exp2(s[v] - base);
-    l += pv[v];
-  }
-  // O^T += V^T P^T over two 16-key k-blocks: lane half h, element e of
-  // k-block kh holds key 16*kh + 8*(e/4) + 4h + e%4 in both operands.
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    const u32x4 bw = {pack_bf16x2(pv[8 * kh], pv[8 * kh + 1]),
-                      pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]),
-                      pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]),
-                      pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7])};
-    const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      o[db] = mfma32x32x16(lds_operand_cols_at(sVb + 16 * kh * D, co.a[db], co.b[db]), b, o[db]);
-  }
 }
 
 template <int D, bool CAUSAL>
@@ -96,15 +168,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_FWD
 void k_fwd(AttnArgs a) {
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
-  constexpr int BN = kFwdBN;
+  constexpr int BN = 32;              // keys per tile
   constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int CH = BN * CPR / 256;  // chunks per thread per tensor per tile
-  static_assert(BN % 32 == 0 && CH >= 1, "key tile must be whole 32-key sub-tiles");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];  // swizzled rows
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
+  constexpr int CH = BN * CPR / 256;  // 16-byte chunks per lane per tensor per tile
+  constexpr int NB = 4;               // LDS ring: tiles t-1, t read while t+1, t+2 arrive
+  static_assert(CH >= 1, "tile copy needs at least one chunk per lane");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NB][BN * D];  // swizzled rows
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NB][BN * D];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const TileId t = xcd_tile((a.nq + kFwdBM - 1) / kFwdBM);
   const int bh = t.bh;
@@ -132,65 +205,87 @@ void k_fwd(AttnArgs a) {
   const int kend = CAUSAL ? min(nkv, qblk0 + kFwdBM) : nkv;
   const int ntiles = (kend + BN - 1) / BN;
 
-  u32x4 rk[CH], rv[CH];
-  uint32_t voff[CH];  // byte offset of this thread's chunks within a tile
+  // K^/V^ tiles go global -> LDS directly. Copy instruction c of this wave
+  // fills LDS chunk slots 64*(CH*wave + c) + lane; slot (row r, position j)
+  // of the XOR-swizzled layout holds column chunk swz(r, j) (an involution).
+  uint32_t goff[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int idx = tid + 256 * c;
-    voff[c] = (uint32_t)((idx / CPR) * D + (idx % CPR) * 8) * 2u;
+    const int p = 64 * (CH * wave + c) + lane;
+    goff[c] = (uint32_t)swz<D>(p / CPR, 8 * (p % CPR)) * 2u;
   }
-  auto load_tile = [&](int k0) __attribute__((always_inline)) {
-    // rows past nkv read as zeros (masked out later)
+  auto issue_tile = [&](int it) __attribute__((always_inline)) {
+    const int k0 = it * BN;
+    const int buf = it % NB;
+    // rows past nkv arrive as zeros (masked out later)
     const uint32_t bytes = (uint32_t)(min(nkv - k0, BN) * D) * 2u;
-    const auto rsk = make_rsrc(K + (size_t)k0 * D, bytes);
-    const auto rsv = make_rsrc(V + (size_t)k0 * D, bytes);
+    const u32x4 dk = buf_desc(K + (size_t)k0 * D, bytes);
+    const u32x4 dv = buf_desc(V + (size_t)k0 * D, bytes);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      rk[c] = buf_ld16(rsk, voff[c]);
-      rv[c] = buf_ld16(rsv, voff[c]);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / CPR, col = (idx % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&sK[buf][swz<D>(r, col)]) = rk[c];
-      *reinterpret_cast<u32x4*>(&sV[buf][swz<D>(r, col)]) = rv[c];
+      buf_ld16_lds(dk, goff[c],
+                   __builtin_amdgcn_readfirstlane(lds_addr(&sK[buf][512 * (CH * wave + c)])));
+      buf_ld16_lds(dv, goff[c],
+                   __builtin_amdgcn_readfirstlane(lds_addr(&sV[buf][512 * (CH * wave + c)])));
     }
   };
 
-  auto step = [&](int it, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = it & 1;
-    const int k0 = it * BN;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(k0 + BN);
-#pragma unroll
-    for (int sub = 0; sub < BN / 32; ++sub) {
-      const int ks = k0 + 32 * sub;
-      const uint16_t* kb = sK[buf] + 32 * sub * D;  // 32-row blocks keep the swizzle phase
-      const uint16_t* vb = sV[buf] + 32 * sub * D;
-      // (boundary tiles only) every key above every row of this wave: skip
-      if (!MASK || !(CAUSAL && qw0 + 31 < ks))
-        fwd_tile<D, CAUSAL, MASK>(qf, o, m, l, kb, vb, ro, co, ks, qi, nkv, sl2, lane);
-    }
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-  };
   // Leading tiles are interior (branch-free); masks start at the first tile
   // that reaches past nkv or above the workgroup's first query (causal).
   int it_hi = min(ntiles, nkv / BN);
   if (CAUSAL) it_hi = min(it_hi, (qblk0 + 1) / BN);
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
   vmem_wait_all();
   __syncthreads();
-  for (int it = 0; it < it_hi; ++it) step(it, BoolTag<false>());
-  for (int it = it_hi; it < ntiles; ++it) step(it, BoolTag<true>());
+
+  bf16x8 b_prev[2];
+  bool have_prev = false;
+  bool pending = false;  // O^T rescale by alpha before the next P^T V^ (see fwd_softmax_pv)
+  float alpha = 1.0f;
+  auto step = [&](int it, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int buf = it % NB;
+    const int pbuf = (it + NB - 1) % NB;
+    const int k0 = it * BN;
+    if (it + 2 < ntiles) issue_tile(it + 2);
+    // (boundary tiles only) every key above every query of this wave: skip;
+    // every later tile is then skipped too
+    if (!MASK || !(CAUSAL && qw0 + 31 < k0)) {
+      f32x16 s;
+      fwd_s<D>(qf, sK[buf], ro, s);
+      bf16x8 b[2];
+      if (have_prev)
+        fwd_softmax_pv<D, CAUSAL, MASK, true>(s, m, l, b, o, b_prev, sV[pbuf], co, pending,
+                                              alpha, k0, h, qi, nkv, sl2);
+      else
+        fwd_softmax_pv<D, CAUSAL, MASK, false>(s, m, l, b, o, b_prev, sV[pbuf], co, pending,
+                                               alpha, k0, h, qi, nkv, sl2);
+      b_prev[0] = b[0];
+      b_prev[1] = b[1];
+      have_prev = true;
+    } else if (have_prev) {
+      fwd_rescale<D>(o, pending, alpha);
+      fwd_pv<D>(o, b_prev, sV[pbuf], co);
+      have_prev = false;
+    }
+    // tile it+1 has landed (this wave's copies; the barrier covers the
+    // other waves'), tile it+2 may still be in flight
+    if (it + 2 < ntiles)
+      vmem_wait<2 * CH>();
+    else
+      vmem_wait<0>();
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it < it_hi; ++it) step(it, BoolTag<false>());
+  for (; it < ntiles; ++it) step(it, BoolTag<true>());
+  // the last tile's O^T (its tile is still resident)
+  if (have_prev) {
+    fwd_rescale<D>(o, pending, alpha);
+    fwd_pv<D>(o, b_prev, sV[(ntiles - 1) % NB], co);
+  }
 
   const float lt = l + xor32(l);
   if (qi < nq) {
