@@ -13,6 +13,8 @@ block) and §High-level wrapper:
 * ``P = softmax(s * Q^ K^T)`` (unquantized), ``O_hp = P V^`` (the
   high-precision auxiliary saved before any probability quantization) and
   ``lse`` = the natural-log log-sum-exp of each row of ``s * Q^ K^T``;
+* the quantized user-visible output ``O = fake_nvfp4(P)  V^`` (Attn-QAT
+  summary, §Method; see :func:`qat_forward_quantized_head` for the reading);
 * backward: ``dS = P * (dO V^T - rowsum(O_hp * dO))``, ``dQ = s dS K^``,
   ``dK = s dS^T Q^`` (straight-through: the unquantized P), and
   ``dV = fake_nvfp4(P)^T dO`` with P grouped in 16s along the key index.
@@ -77,6 +79,39 @@ def qat_forward_head(q, k, v, softmax_scale: float, causal: bool, rows=None,
     lse = m[:, 0] + np.log(np.exp(S - m).sum(axis=1))
     P = np.exp(S - lse[:, None])
     return P @ vh, lse
+
+
+def qat_forward_quantized_head(q, k, v, softmax_scale: float, causal: bool,
+                               p_scale: float = 1.0, rows=None, quantize_p: bool = True):
+    """The quantized, user-visible QAT forward output of one head.
+
+    The Attn-QAT summary (§Method) forms the low-precision output from the
+    FP32 softmax probabilities fake-quantized to ``P^F`` and ``V^F``:
+    ``O = P^F V^``.  Reading taken here: ``P`` is the *normalized* softmax,
+    ``P = exp(s Q^ K^T - lse)`` with the row's natural-log lse, and ``P^F =
+    fake_nvfp4(p_scale P) / p_scale`` grouped in 16s along the key index from
+    key 0 -- exactly the ``P^F`` whose transpose the backward multiplies into
+    dO for dV, so dV is the straight-through gradient of this O.  (A one-pass
+    forward would instead quantize the unnormalized running-max ``p`` tile by
+    tile; that is not what is computed here.)
+
+    Returns ``O`` (len(rows), D) in fp64 for the query rows ``rows`` (all if
+    None).  ``quantize_p=False`` skips the quantization of P (then ``O`` is
+    ``O_hp``).
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    if causal and q.shape[0] != k.shape[0]:
+        raise ValueError("causal attention is self-attention only (Nq == Nk)")
+    r = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    _, lse = qat_forward_head(q, k, v, softmax_scale, causal, rows=r)
+    qh, kh, vh = quantize_qkv(q, k, v)
+    keys = np.arange(k.shape[0])
+    S = softmax_scale * (qh[r] @ kh.T)
+    P = np.exp(S - lse[:, None])
+    if causal:
+        P = np.where(_causal_mask(r, keys), 0.0, P)
+    PF = fake_nvfp4_values(p_scale * P, axis=1) / p_scale if quantize_p else P
+    return PF @ vh
 
 
 def _probabilities(qh, kh, lse, softmax_scale, causal, rows, keys):
@@ -170,6 +205,15 @@ def qat_forward(q, k, v, softmax_scale: float, causal: bool, heads=None, rows=No
     for b, h in _heads(B, H, heads):
         out[(b, h)] = qat_forward_head(q[b, h], k[b, h], v[b, h], softmax_scale, causal, rows)
     return out
+
+
+def qat_forward_quantized(q, k, v, softmax_scale: float, causal: bool, p_scale: float = 1.0,
+                          heads=None, rows=None):
+    """Batched quantized forward output; returns ``{(b, h): O}``."""
+    B, H = q.shape[0], q.shape[1]
+    return {(b, h): qat_forward_quantized_head(q[b, h], k[b, h], v[b, h], softmax_scale,
+                                               causal, p_scale, rows)
+            for b, h in _heads(B, H, heads)}
 
 
 def qat_backward(q, k, v, o_hp, do, lse, softmax_scale: float, causal: bool,

@@ -4,6 +4,9 @@ The oracle is checked against: torch's fp64 scaled-dot-product attention and
 autograd (a library routine) on the fake-quantized inputs, central finite
 differences, the FlashAttention row-sum identity that the high-precision
 auxiliary output keeps exact, and closed forms (causal row 0, uniform P).
+The quantized forward output O = P^F V^ is pinned by the same closed forms,
+by the adjoint identity <O, dO> = <V^, dV> with the backward's dV, and by
+reducing to O_hp without P quantization.
 """
 from __future__ import annotations
 
@@ -14,7 +17,8 @@ import pytest
 import torch
 
 from oracle.attention import (qat_backward, qat_backward_full_head, qat_backward_head,
-                              qat_forward, qat_forward_head, quantize_qkv)
+                              qat_forward, qat_forward_head, qat_forward_quantized_head,
+                              quantize_qkv)
 from oracle.nvfp4 import fake_nvfp4_values
 from workloads import make_inputs
 
@@ -232,3 +236,73 @@ def test_batched_wrappers_on_tiny_workload():
     dq, dk, dv = bw[(0, 0)]
     assert dq.shape == (128, 64) and dk.shape == (128, 64) and dv.shape == (128, 64)
     assert np.all(np.isfinite(dq)) and np.abs(dv).max() > 0
+
+
+# --- the quantized forward output O = P^F V^ --------------------------------
+
+def test_quantized_output_without_p_quant_is_o_hp():
+    q, k, v, _ = _heads_np(56, 64, seed=11)
+    for causal in (False, True):
+        o_hp, _ = qat_forward_head(q, k, v, 0.125, causal)
+        o = qat_forward_quantized_head(q, k, v, 0.125, causal, quantize_p=False)
+        np.testing.assert_allclose(o, o_hp, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("p_scale", [1.0, 2688.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_quantized_output_is_adjoint_of_backward_dv(causal, p_scale):
+    """<O, dO> = <V^, dV>: the forward's P^F is the one whose transpose the
+    backward multiplies into dO (dV is the straight-through gradient of O)."""
+    q, k, v, do = _heads_np(72, 64, seed=12)  # 72 keys: a short last group
+    o_hp, lse = qat_forward_head(q, k, v, 0.125, causal)
+    o = qat_forward_quantized_head(q, k, v, 0.125, causal, p_scale=p_scale)
+    _, _, dv = qat_backward_full_head(q, k, v, o_hp, do, lse, 0.125, causal, p_scale=p_scale)
+    _, _, vh = quantize_qkv(q, k, v)
+    lhs, rhs = float((o * do).sum()), float((vh * dv).sum())
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(rhs))
+    # and it differs from O_hp (the quantization is not a no-op here)
+    assert np.max(np.abs(o - o_hp)) > 1e-3 * np.max(np.abs(o_hp))
+
+
+@pytest.mark.parametrize("n,p_scale,expect", [(128, 1.0, "mean"), (4096, 1.0, "zero"),
+                                              (4096, 2688.0, "mean")])
+def test_quantized_output_uniform_p_closed_form(n, p_scale, expect):
+    """Q = 0 gives P = 1/N.  N=128: P^F = 2^-7 = P, so O = mean(V^); N=4096:
+    the scale underflows and O = 0; with p_scale = 2688, P^F = 2^-12 = P
+    again and O = mean(V^)."""
+    d = 64
+    g = torch.Generator().manual_seed(n + 1)
+    q = np.zeros((n, d))
+    k = torch.randn(n, d, generator=g).to(torch.bfloat16).double().numpy()
+    v = torch.randn(n, d, generator=g).to(torch.bfloat16).double().numpy()
+    rows = [0, 7, n - 1]
+    o = qat_forward_quantized_head(q, k, v, 0.125, False, p_scale=p_scale, rows=rows)
+    _, _, vh = quantize_qkv(q, k, v)
+    want = np.zeros((3, d)) if expect == "zero" else np.broadcast_to(vh.mean(0), (3, d))
+    np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-14)
+
+
+def test_quantized_output_causal_row_zero_closed_form():
+    """Causal query 0 sees only key 0 with P = 1: fq(1) = 1.03125 (scale
+    0.171875, code 6), so O[0] = 1.03125 v^_0; with p_scale = 2688 it is v^_0."""
+    q, k, v, _ = _heads_np(32, 64, seed=13)
+    _, _, vh = quantize_qkv(q, k, v)
+    o = qat_forward_quantized_head(q, k, v, 0.125, True, rows=[0])
+    assert np.array_equal(o[0], 1.03125 * vh[0])
+    o2 = qat_forward_quantized_head(q, k, v, 0.125, True, p_scale=2688.0, rows=[0])
+    assert np.array_equal(o2[0], vh[0])
+
+
+def test_quantized_output_groups_along_keys_with_zero_padded_tail():
+    q, k, v, _ = _heads_np(40, 64, seed=14, nk=40)
+    o_hp, lse = qat_forward_head(q, k, v, 0.125, False)
+    o = qat_forward_quantized_head(q, k, v, 0.125, False)
+    qh, kh, vh = quantize_qkv(q, k, v)
+    P = np.exp(0.125 * qh @ kh.T - lse[:, None])
+    Ppad = np.concatenate([P, np.zeros((40, 8))], axis=1)
+    PF = np.concatenate([fake_nvfp4_values(Ppad[:, 16 * g:16 * g + 16], axis=1)
+                         for g in range(3)], axis=1)[:, :40]
+    np.testing.assert_allclose(o, PF @ vh, rtol=1e-13, atol=1e-13)
+    # rows subset = full rows
+    o_rows = qat_forward_quantized_head(q, k, v, 0.125, False, rows=[3, 39])
+    np.testing.assert_allclose(o_rows, o[[3, 39]], rtol=1e-13, atol=1e-14)
