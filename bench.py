@@ -192,6 +192,20 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
+    # The full QAT forward with the quantized output O = fq(P) V^ (a second
+    # pass over the keys), timed on its own after the step loop.
+    o_q = torch.empty_like(qd)
+    KQ = max(min(K, 10), 1)
+    evq = [hip.array(4) for _ in range(KQ)]
+    for i in range(2):
+        B.attnqat_fwd_quantized_timed(p, qd, kd, vd, o, lse, o_q, wsf, evq[0], stream)
+    torch.cuda.synchronize()
+    for i in range(KQ):
+        B.attnqat_fwd_quantized_timed(p, qd, kd, vd, o, lse, o_q, wsf, evq[i], stream)
+    torch.cuda.synchronize()
+    fq_ms = sum(hip.ms(e[0], e[3]) for e in evq) / KQ
+    fq_pass_ms = sum(hip.ms(e[2], e[3]) for e in evq) / KQ
+
     names_f = ["fwd_quant_qkv", "fwd_attention"]
     names_b = ["bwd_quant_q_delta", "bwd_quant_kv", "bwd_dq", "bwd_dkdv"]
     per = {n: 0.0 for n in names_f + names_b}
@@ -250,6 +264,7 @@ def main():
         f"source={digest}")
     for n in names_f + names_b:
         log(f"  {n:20s} {per[n]:8.4f} ms")
+    log(f"  fwd with quantized output {fq_ms:.4f} ms (output pass {fq_pass_ms:.4f} ms)")
     log(f"  fwd {fwd_ms:.4f} ms ({fwd_tflops:.1f} TFLOP/s), bwd {bwd_ms:.4f} ms "
         f"({bwd_tflops:.1f} TFLOP/s = {100 * bwd_tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
 
@@ -275,6 +290,9 @@ def main():
         "fwd_tflops": round(fwd_tflops, 2),
         "kernels_ms": {n: round(per[n], 4) for n in names_f + names_b},
         "roofline": roofline,
+        "fwd_quantized": {"ms": round(fq_ms, 4), "output_pass_ms": round(fq_pass_ms, 4),
+                          "output_pass_tflops": round(w.fwd_flops() / (fq_pass_ms * 1e-3) / 1e12,
+                                                      2)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, do)

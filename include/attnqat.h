@@ -142,6 +142,21 @@ ATTNQAT_API int attnqat_fwd(const attnqat_problem* p, const void* q, const void*
                             const void* v, void* o_hp, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* The full QAT forward: attnqat_fwd's work plus the quantized, user-visible
+ * output O = P^F V^ (Attn-QAT summary, §Method: the FP32 softmax P is
+ * fake-quantized to P^F and combined with V^F).  P is the normalized
+ * softmax exp(scale Q^ K^T - lse) and P^F = fake_nvfp4(p_scale P) / p_scale
+ * in groups of 16 consecutive keys from key 0 (masked keys count as 0) --
+ * the P^F whose transpose attnqat_bwd multiplies into dO for dV.  Computed
+ * as a second pass over the keys after the first pass has produced lse.
+ * Arguments as attnqat_fwd, plus o (B,H,Nq,D) bf16 (16-byte aligned, not
+ * aliasing the other buffers).  Errors as attnqat_fwd; a NULL o is
+ * ATTNQAT_ERR_INVALID_ARGUMENT. */
+ATTNQAT_API int attnqat_fwd_quantized(const attnqat_problem* p, const void* q, const void* k,
+                                      const void* v, void* o_hp, float* lse, void* o,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
 /* QAT backward (page §Overview formula block and four-kernel structure:
  * Q fake-quant + delta, K/V fake-quant, dQ, dK/dV).
  * In: q, o_hp, d_o (B,H,Nq,D) bf16; k, v (B,H,Nkv,D) bf16; lse (B,H,Nq)
@@ -159,6 +174,8 @@ ATTNQAT_API int attnqat_bwd(const attnqat_problem* p, const void* q, const void*
  * without any synchronization inside the call.
  * attnqat_fwd_timed: events[0] before the Q/K/V fake-quant kernel,
  *   events[1] before the attention kernel, events[2] after it.
+ * attnqat_fwd_quantized_timed: as attnqat_fwd_timed, plus events[3] after
+ *   the second (quantized-output) pass.
  * attnqat_bwd_timed: events[0] before the Q fake-quant + delta kernel,
  *   events[1] before the K/V fake-quant kernel, events[2] before the dQ
  *   kernel, events[3] before the dK/dV kernel, events[4] after it.
@@ -167,6 +184,11 @@ ATTNQAT_API int attnqat_fwd_timed(const attnqat_problem* p, const void* q, const
                                   const void* v, void* o_hp, float* lse, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream,
                                   hipEvent_t* events);
+ATTNQAT_API int attnqat_fwd_quantized_timed(const attnqat_problem* p, const void* q,
+                                            const void* k, const void* v, void* o_hp,
+                                            float* lse, void* o, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream,
+                                            hipEvent_t* events);
 ATTNQAT_API int attnqat_bwd_timed(const attnqat_problem* p, const void* q, const void* k,
                                   const void* v, const void* o_hp, const void* d_o,
                                   const float* lse, void* dq, void* dk, void* dv,

@@ -69,7 +69,10 @@ _SIGS = {
     "attnqat_fwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "attnqat_bwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                    _vp]),
+    "attnqat_fwd_quantized": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "attnqat_fwd_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "attnqat_fwd_quantized_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                                   _vp, _vp]),
     "attnqat_bwd_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _sz, _vp, _vp]),
 }
@@ -182,6 +185,12 @@ def attnqat_fwd(p: attnqat_problem, q, k, v, o_hp, lse, workspace, stream=None):
                             _ptr(workspace), workspace.numel(), _stream(stream)), "attnqat_fwd")
 
 
+def attnqat_fwd_quantized(p: attnqat_problem, q, k, v, o_hp, lse, o, workspace, stream=None):
+    _check(_lib.attnqat_fwd_quantized(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),
+                                      _ptr(lse), _ptr(o), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)), "attnqat_fwd_quantized")
+
+
 def attnqat_bwd(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace, stream=None):
     _check(_lib.attnqat_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp), _ptr(d_o),
                             _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
@@ -193,6 +202,15 @@ def attnqat_fwd_timed(p: attnqat_problem, q, k, v, o_hp, lse, workspace, events,
     _check(_lib.attnqat_fwd_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),
                                   _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream),
                                   events), "attnqat_fwd_timed")
+
+
+def attnqat_fwd_quantized_timed(p: attnqat_problem, q, k, v, o_hp, lse, o, workspace, events,
+                                stream=None):
+    """``events``: a ctypes array of 4 hipEvent_t handles (see the header)."""
+    _check(_lib.attnqat_fwd_quantized_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(o_hp), _ptr(lse), _ptr(o), _ptr(workspace),
+                                            workspace.numel(), _stream(stream), events),
+           "attnqat_fwd_quantized_timed")
 
 
 def attnqat_bwd_timed(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace,
@@ -213,17 +231,23 @@ def _check_bhsd(*ts):
 
 
 def nvfp4_attention_qat_forward(q, k, v, is_causal=False, softmax_scale=None, p_scale=1.0,
-                                workspace=None, current_stream=None):
-    """Returns ``(high_precision_o, lse)`` of the QAT forward."""
+                                workspace=None, current_stream=None, quantized_output=False):
+    """Returns ``(high_precision_o, lse)`` of the QAT forward, or
+    ``(o, high_precision_o, lse)`` with ``quantized_output=True``, where ``o``
+    is the quantized user-visible output fake_nvfp4(P) V^."""
     _check_bhsd(q, k, v)
     p = problem_for(q, k, is_causal, softmax_scale, p_scale)
-    o = torch.empty_like(q)
+    o_hp = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = torch.empty(attnqat_fwd_workspace_bytes(p), dtype=torch.uint8,
                                 device=q.device)
-    attnqat_fwd(p, q, k, v, o, lse, workspace, current_stream)
-    return o, lse
+    if not quantized_output:
+        attnqat_fwd(p, q, k, v, o_hp, lse, workspace, current_stream)
+        return o_hp, lse
+    o = torch.empty_like(q)
+    attnqat_fwd_quantized(p, q, k, v, o_hp, lse, o, workspace, current_stream)
+    return o, o_hp, lse
 
 
 def nvfp4_attention_qat_backward(do, q, k, v, high_precision_o, lse, is_causal=False,

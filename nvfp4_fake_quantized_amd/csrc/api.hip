@@ -169,12 +169,13 @@ bool record(hipEvent_t* ev, int i, hipStream_t stream) {
   return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess;
 }
 
+// with_o: also the quantized output o (second pass)
 int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v, void* o_hp,
-            float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
-            hipEvent_t* ev) {
+            float* lse, bool with_o, void* o, void* workspace, size_t workspace_bytes,
+            hipStream_t stream, hipEvent_t* ev) {
   int st = validate_problem(p);
   if (st != ATTNQAT_OK) return st;
-  const void* ptrs[] = {q, k, v, o_hp, lse, workspace};
+  const void* ptrs[] = {q, k, v, o_hp, lse, workspace, with_o ? o : o_hp};
   for (const void* ptr : ptrs)
     if (ptr == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
   for (const void* ptr : ptrs)
@@ -213,6 +214,12 @@ int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   a.p_scale = p->p_scale;
   if (attnqat::launch_fwd(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
   if (!record(ev, 2, stream)) return ATTNQAT_ERR_HIP;
+  if (with_o) {
+    a.lse = lse;  // the first pass's output
+    a.o_q = static_cast<uint16_t*>(o);
+    if (attnqat::launch_fwd_out(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+    if (!record(ev, 3, stream)) return ATTNQAT_ERR_HIP;
+  }
   return ATTNQAT_OK;
 }
 
@@ -294,7 +301,13 @@ extern "C" {
 int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
                 void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
-  return run_fwd(p, q, k, v, o_hp, lse, workspace, workspace_bytes, stream, nullptr);
+  return run_fwd(p, q, k, v, o_hp, lse, false, nullptr, workspace, workspace_bytes, stream,
+                 nullptr);
+}
+int attnqat_fwd_quantized(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                          void* o_hp, float* lse, void* o, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return run_fwd(p, q, k, v, o_hp, lse, true, o, workspace, workspace_bytes, stream, nullptr);
 }
 
 int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
@@ -308,7 +321,15 @@ int attnqat_fwd_timed(const attnqat_problem* p, const void* q, const void* k, co
                       void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, hipEvent_t* events) {
   if (!events_ok(events, 3)) return ATTNQAT_ERR_INVALID_ARGUMENT;
-  return run_fwd(p, q, k, v, o_hp, lse, workspace, workspace_bytes, stream, events);
+  return run_fwd(p, q, k, v, o_hp, lse, false, nullptr, workspace, workspace_bytes, stream,
+                 events);
+}
+int attnqat_fwd_quantized_timed(const attnqat_problem* p, const void* q, const void* k,
+                                const void* v, void* o_hp, float* lse, void* o,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* events) {
+  if (!events_ok(events, 4)) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  return run_fwd(p, q, k, v, o_hp, lse, true, o, workspace, workspace_bytes, stream, events);
 }
 
 int attnqat_bwd_timed(const attnqat_problem* p, const void* q, const void* k, const void* v,

@@ -272,16 +272,26 @@ struct ColOffsets {
   }
 };
 
-// Per-lane offsets of the 16-byte row reads (row l32, column 16*kb + 8h).
+// Per-lane offsets of the 16-byte row reads (row l32, or the given row,
+// column 16*kb + 8h).
 template <int W>
 struct RowOffsets {
   int o[W / 16];
-  __device__ __forceinline__ explicit RowOffsets(int lane) {
-    const int h = lane >> 5, l32 = lane & 31;
+  __device__ __forceinline__ explicit RowOffsets(int lane) : RowOffsets(lane, lane & 31) {}
+  __device__ __forceinline__ RowOffsets(int lane, int row) {
+    const int h = lane >> 5;
 #pragma unroll
-    for (int kb = 0; kb < W / 16; ++kb) o[kb] = swz<W>(l32, 16 * kb + 8 * h);
+    for (int kb = 0; kb < W / 16; ++kb) o[kb] = swz<W>(row, 16 * kb + 8 * h);
   }
 };
+
+// Row r of a 32-row A operand taken from key pi(r) of a 32-key block: the
+// 32x32 accumulator row 8*(v/4) + 4h + v%4 of lane half h (VGPR v) is then
+// key 16h + v, so each lane holds 16 consecutive keys -- one P quantization
+// group -- of its column.
+__device__ __forceinline__ int key_perm(int r) {
+  return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
 
 // bf16 pair from two floats (round to nearest even), packed low/high.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -372,9 +382,12 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 // (vmem_wait) and synchronizes before reading the destination.  Issued as
 // inline assembly so that the compiler does not add its own conservative
 // vmcnt waits in front of every later LDS read.
+// (The descriptor must live in SGPRs: its fields are read as wave-uniform.)
 __device__ __forceinline__ u32x4 buf_desc(const void* p, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(p);
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu),
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p);

@@ -87,12 +87,6 @@ struct DkdvLds {
   static constexpr int TOTAL = PAIR + DL + kRing * kSub * 4;
 };
 
-// Row r of a wave's 32-row K^/V^ operand holds key pi(r): the S^T
-// accumulator row 8*(v/4) + 4h + v%4 of lane half h is then key 16h + v.
-__device__ __forceinline__ int key_perm(int r) {
-  return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
-}
-
 template <int D, bool CAUSAL, bool UNIT_P>
 __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
   using L = DkdvLds<D>;

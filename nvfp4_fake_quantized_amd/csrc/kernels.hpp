@@ -21,6 +21,7 @@ struct AttnArgs {
   uint16_t* dq;           // (BH, nq, D)
   uint16_t* dk;           // (BH, nkv, D)
   uint16_t* dv;           // (BH, nkv, D)
+  uint16_t* o_q;          // (BH, nq, D)       quantized forward output (second pass)
   int bh;                 // batch * heads
   int nq, nkv;
   int causal;
@@ -46,6 +47,8 @@ hipError_t launch_quant_q_delta(const uint16_t* q, const uint16_t* o_hp, const u
                                 int64_t rows, int head_dim, hipStream_t stream);
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream);
+// O = P^F V^ from Q^, K^, V^ and the forward's lse (a.lse), into a.o_q.
+hipError_t launch_fwd_out(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream);
 
