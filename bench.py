@@ -20,6 +20,7 @@ import ctypes
 import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -141,6 +142,87 @@ def cpu_baseline(w, q, k, v, do, min_seconds: float = 10.0):
     }
 
 
+def p_scale_study(p_scales=(1.0, 64.0, 512.0, 2688.0), reps=5):
+    """Gradient-quality diagnostic of the P pre-scale (the P^F = fq(p_scale P)
+    / p_scale reading): for every workload at full size and two of its heads,
+    cos(dV, dV_unquantized) where dV comes from the library and
+    dV_unquantized = P^T dO is formed here with torch fp32 matmuls from the
+    library's own Q^/K^ and lse; the fraction of P groups (16 keys, at least
+    one nonzero P) whose E4M3 scale underflows to 0; the backward's time.
+    Returns a list of dicts."""
+    import torch
+
+    from nvfp4_fake_quantized_amd import binding as B
+    from workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    hip = HipEvents()
+    out = []
+    for name in ("tiny", "small_causal", "ref_shape", "llm_causal", "video_dit"):
+        w = WORKLOADS[name]
+        log(f"[p_scale study] {name}")
+        q, k, v, do = (t.to(dev) for t in make_inputs(w))
+        p1 = B.problem_for(q, k, w.causal, w.softmax_scale, 1.0)
+        wsf = torch.empty(B.attnqat_fwd_workspace_bytes(p1), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        B.attnqat_fwd(p1, q, k, v, o, lse, wsf)
+        L = B.attnqat_workspace_layout(p1, B.WS_FWD)
+        n_el = q.numel()
+        qh = wsf[L["q_hat"]:L["q_hat"] + 2 * n_el].view(torch.bfloat16).view(q.shape)
+        kh = wsf[L["k_hat"]:L["k_hat"] + 2 * n_el].view(torch.bfloat16).view(k.shape)
+        heads = [(0, 0), (w.batch - 1, w.heads - 1)]
+        N = w.seqlen
+        G = -(-N // 16)
+        ref, amaxes = {}, {}
+        for b, h in heads:
+            dv_ref = torch.zeros(N, w.head_dim, dtype=torch.float32, device=dev)
+            am = []
+            kf = kh[b, h].float()
+            for r0 in range(0, N, 2048):
+                r1 = min(N, r0 + 2048)
+                S = (qh[b, h, r0:r1].float() @ kf.T) * w.softmax_scale
+                P = torch.exp(S - lse[b, h, r0:r1, None])
+                if w.causal:
+                    rows = torch.arange(r0, r1, device=dev)[:, None]
+                    P = torch.where(torch.arange(N, device=dev)[None, :] > rows, 0.0, P)
+                dv_ref += P.T @ do[b, h, r0:r1].float()
+                Pp = torch.nn.functional.pad(P, (0, 16 * G - N))
+                am.append(Pp.view(r1 - r0, G, 16).amax(-1).flatten())
+            ref[(b, h)] = dv_ref.double()
+            amaxes[(b, h)] = torch.cat(am)
+        for ps in p_scales:
+            p = B.problem_for(q, k, w.causal, w.softmax_scale, ps)
+            wsb = torch.empty(B.attnqat_bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            evs = [hip.array(5) for _ in range(reps)]
+            for i in range(2 + reps):
+                B.attnqat_bwd_timed(p, q, k, v, o, do, lse, dq, dk, dv, wsb, evs[max(i - 2, 0)])
+            torch.cuda.synchronize()
+            bwd_ms = sum(hip.ms(e[0], e[4]) for e in evs) / reps
+            num = den_a = den_b = 0.0
+            zero = total = 0
+            for b, h in heads:
+                a_, r_ = dv[b, h].double(), ref[(b, h)]
+                num += float((a_ * r_).sum())
+                den_a += float((a_ * a_).sum())
+                den_b += float((r_ * r_).sum())
+                am = amaxes[(b, h)]
+                live = am > 0
+                total += int(live.sum())
+                zero += int((live & (am.double() * ps / 6.0 <= 2.0 ** -10)).sum())
+            cos = num / max(math.sqrt(den_a * den_b), 1e-300)
+            out.append({"workload": name, "p_scale": ps, "cos_dv_vs_unquantized_p": round(cos, 4),
+                        "zero_scale_group_fraction": round(zero / max(total, 1), 4),
+                        "bwd_ms": round(bwd_ms, 4), "heads": heads})
+            log(f"  p_scale {ps:7.1f}: cos(dV) {cos:.4f}, zero-scale P groups "
+                f"{zero / max(total, 1):.4f}, bwd {bwd_ms:.4f} ms")
+        del q, k, v, do, o, lse, wsf
+        torch.cuda.empty_cache()
+    hip.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,11 +233,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
+    ap.add_argument("--p-scale-study", action="store_true",
+                    help="instead of the benchmark, print the p_scale gradient-quality study "
+                         "(one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on a single GPU; multi-GPU runs are not part of this "
               "build (the work shards over batch*heads with no exchange).", file=sys.stderr)
         sys.exit(2)
+
+    if args.p_scale_study:
+        print(json.dumps({"p_scale_study": p_scale_study()}), flush=True)
+        return
 
     import torch
 
