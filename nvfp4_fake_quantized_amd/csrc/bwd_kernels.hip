@@ -176,7 +176,7 @@ void k_dq(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const TileId t = xcd_tile((a.nq + kDqBM - 1) / kDqBM);
+  const TileId t = xcd_tile((a.nq + kDqBM - 1) / kDqBM, CAUSAL);
   const int bh = t.bh;
   const int nq = a.nq, nkv = a.nkv;
   const int qblk0 = t.tile * kDqBM;

@@ -50,7 +50,10 @@ constexpr int kNumXcd = 8;  // XCDs of an MI355X
 struct TileId {
   int tile, bh;
 };
-__device__ __forceinline__ TileId xcd_tile(int tiles_per_head) {
+// last_first: hand out each head's tiles from the last one down (causal
+// query tiles: the last one has the most keys, so the heavy work starts
+// first and the light tiles fill the tail).
+__device__ __forceinline__ TileId xcd_tile(int tiles_per_head, bool last_first = false) {
   const int w = blockIdx.x;
   int l = w;
   if (ATTNQAT_XCD_GROUP) {
@@ -59,7 +62,8 @@ __device__ __forceinline__ TileId xcd_tile(int tiles_per_head) {
     const int x = w % kNumXcd, slot = w / kNumXcd;
     l = x < rem ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
   }
-  return {l % tiles_per_head, l / tiles_per_head};
+  const int tile = l % tiles_per_head;
+  return {last_first ? tiles_per_head - 1 - tile : tile, l / tiles_per_head};
 }
 
 // Compile-time boolean carried through generic lambdas.

@@ -161,7 +161,7 @@ void k_fwd_out(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const TileId t = xcd_tile((a.nq + kOutBM - 1) / kOutBM);
+  const TileId t = xcd_tile((a.nq + kOutBM - 1) / kOutBM, CAUSAL);
   const int bh = t.bh;
   const int nq = a.nq, nkv = a.nkv;
   const int qblk0 = t.tile * kOutBM;
