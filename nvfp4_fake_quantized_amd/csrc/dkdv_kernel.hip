@@ -12,20 +12,20 @@
 // A workgroup of 8 waves owns 128 keys, as four pairs of waves that share a
 // SIMD (waves w and w+4).  A lone wave issues VALU at only half of a SIMD's
 // rate, so the two waves of a pair split the work on their 32 keys by role;
-// each issues 16 MFMAs per 32-query step and a similar VALU load, and their
-// instruction streams interleave on the SIMD:
+// each issues 16 MFMAs per 32-query step, and their instruction streams
+// interleave on the SIMD:
 //  * wave X (w < 4) keeps the pair's K^ and V^ rows.  At step j it issues the
 //    MFMAs of S^T(j+1) = K^ Q^T and dP^T(j+1) = V^ dO^T (one step ahead, with
 //    operands read from LDS two MFMAs ahead) interleaved, element by element,
 //    with the VALU work on S^T(j) and dP^T(j) of the previous step:
-//    P = exp2(S s log2e - lse log2e), the group amax and E4M3 scale, and
-//    dS = P (dP - delta).  It hands P (fp32), the scale and the dS tile (bf16)
-//    to Y through LDS.
-//  * wave Y (w >= 4) keeps the dV and dK accumulators.  At step j it takes
-//    P, the scale and dS of sub-tile j-1, forms the refined quotients
-//    q = P / scale and their E2M1 codes (P^F = code * scale, exact: the code
-//    rounds like the exact quotient, i.e. precise division), and adds
-//    P^F^T dO to dV and dS^T Q^ to dK (operands prefetched from LDS).
+//    P = exp2(S s log2e - lse log2e), the group amax and E4M3 scale,
+//    dS = P (dP - delta), then the refined quotients q = P / scale and their
+//    E2M1 codes (the code rounds like the exact quotient, i.e. precise
+//    division).  It hands the 4-bit codes, the scale and the dS tile (bf16)
+//    to Y through LDS: 8 bytes of codes per lane instead of 64 bytes of P.
+//  * wave Y (w >= 4) keeps the dV and dK accumulators.  At step j it adds
+//    dS^T Q^ of sub-tile j-1 to dK while it forms P^F = code * scale (exact
+//    in bf16), then adds P^F^T dO to dV (operands prefetched from LDS).
 // One barrier per step orders the handover.
 //
 // In the S^T accumulator each lane holds one query and, because the K^/V^
@@ -65,6 +65,7 @@ constexpr int kRing = 4;       // Q^/dO sub-tile slots (also the unroll factor)
 constexpr int kAhead = ATTNQAT_DKDV_AHEAD;     // X: MFMA operand reads issued this many MFMAs ahead
 constexpr int kAheadY = ATTNQAT_DKDV_AHEAD_Y;  // Y: the same
 
+
 template <int N>
 struct IntTag {
   static constexpr int value = N;
@@ -78,8 +79,8 @@ struct DkdvLds {
   static constexpr int RING = 0;                        // slot r: Q^ at 2r SUBT, dO at (2r+1) SUBT
   static constexpr int PAIR = RING + kRing * 2 * SUBT;  // per-pair buffers start here
   // offsets within the per-pair area
-  static constexpr int PB = 0;                       // P[pair][2][4 KB], [g][lane][4] floats
-  static constexpr int DS = PB + 4 * 2 * 4096;       // dS[pair][2] 32x32 bf16 tiles
+  static constexpr int CB = 0;                       // E2M1 codes[pair][2][64 lanes] (8 B)
+  static constexpr int DS = CB + 4 * 2 * 512;        // dS[pair][2] 32x32 bf16 tiles
   static constexpr int PF = DS + 4 * 2 * 2048;       // P^F[pair] 32x32 bf16 tiles
   static constexpr int SB = PF + 4 * 2048;           // scale[pair][2][64] floats
   static constexpr int LSE = SB + 4 * 2 * 256;       // lse[kRing][32] (raw)
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
     return reinterpret_cast<const uint16_t*>(smem + L::RING + (2 * slot + tensor) * L::SUBT);
   };
   uint8_t* const pair = smem + L::PAIR;
-  float* const pbuf = reinterpret_cast<float*>(pair + L::PB + kk * 2 * 4096);
+  u32x2* const cbuf = reinterpret_cast<u32x2*>(pair + L::CB + kk * 2 * 512);
   float* const sbuf = reinterpret_cast<float*>(pair + L::SB + kk * 2 * 256);
   uint16_t* const dstile = reinterpret_cast<uint16_t*>(pair + L::DS + kk * 2 * 2048);
   const int pw0 = swz<32>(l32, 16 * h), pw1 = swz<32>(l32, 16 * h + 8);  // tile row writes
@@ -263,13 +264,18 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
         uint16_t* dt = dstile + (R & 1) * 1024;
         *reinterpret_cast<u32x4*>(dt + pw0) = dsb[0];
         *reinterpret_cast<u32x4*>(dt + pw1) = dsb[1];
-        float* pd = pbuf + (R & 1) * 1024;
+        // the group's E2M1 codes (refined quotients, hardware RNE) go to Y
+        const float sc = e4m3_scale_from_amax(amax);
+        // a zero scale divides by 1 instead (its codes are then multiplied by 0)
+        const FastP fq(sc > 0.0f ? sc : 1.0f);
+        f32x4 q4[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 w = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
-          *reinterpret_cast<f32x4*>(pd + (g * 64 + lane) * 4) = w;
-        }
-        sbuf[(R & 1) * 64 + lane] = e4m3_scale_from_amax(amax);
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q4[g][e] = fq.quotient(p[4 * g + e]);
+        cbuf[(R & 1) * 64 + lane] = u32x2{FastP::codes8(q4[0], q4[1]),
+                                          FastP::codes8(q4[2], q4[3])};
+        sbuf[(R & 1) * 64 + lane] = sc;
       }
     };
 
@@ -348,10 +354,8 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       constexpr int RP = (R + kRing - 1) % kRing;  // slot of sub-tile j-1
       if (j >= nsteps) return;
       if (j >= 1 && !skipped(j - 1)) {  // j - 1 < nsub holds for j < nsteps
-        const float* ps = pbuf + (RP & 1) * 1024;
         const float sc = sbuf[(RP & 1) * 64 + lane];
-        // a zero scale divides by 1 instead (its codes are then multiplied by 0)
-        const FastP fq(sc > 0.0f ? sc : 1.0f);
+        const u32x2 cw = cbuf[(RP & 1) * 64 + lane];  // 16 E2M1 codes from X
         const uint16_t* dt = dstile + (RP & 1) * 1024;
         const uint16_t* sQ = ring(RP, 0);
         const uint16_t* sDO = ring(RP, 1);
@@ -361,38 +365,23 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
           return lds_operand_cols_at(tile + 16 * (k / DB) * D, co.a[k % DB], co.b[k % DB]);
         };
         // dK += dS^T Q^ first (dS arrived with the step), interleaved with the
-        // P^F VALU work: quotients, E2M1 codes, P^F = code * scale
+        // P^F VALU work: P^F = code * scale, packed to bf16
         const bf16x8 as[2] = {lds_operand_cols_at(dt, cp.a[0], cp.b[0]),
                               lds_operand_cols_at(dt + 16 * 32, cp.a[0], cp.b[0])};
-        f32x4 p4[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) p4[g] = *reinterpret_cast<const f32x4*>(ps + (g * 64 + lane) * 4);
         bf16x8 b[NH];
 #pragma unroll
         for (int k = 0; k < kAheadY; ++k) b[k] = operand(sQ, k);
-        f32x4 q4[4];
-        uint32_t codes[2];
         u32x4 pf[2];
-        // VALU share of dK MFMA k (NH = 8 for D = 128, 4 for D = 64)
+        // VALU share of dK MFMA k (NH = 8 for D = 128, 4 for D = 64): the 8
+        // dequantized pairs
         auto valu_part = [&](int part, int nparts) __attribute__((always_inline)) {
-          // parts: quotient groups 0..3, then codes, then the 8 dequantized pairs
-          constexpr int NW = 4 + 1 + 8;  // work items
-          const int w0 = part * NW / nparts, w1 = (part + 1) * NW / nparts;
+          const int i0 = part * 8 / nparts, i1 = (part + 1) * 8 / nparts;
 #pragma unroll
-          for (int w = 0; w < NW; ++w) {
-            if (w < w0 || w >= w1) continue;
-            if (w < 4) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) q4[w][e] = fq.quotient(p4[w][e]);
-            } else if (w == 4) {
-              codes[0] = FastP::codes8(q4[0], q4[1]);
-              codes[1] = FastP::codes8(q4[2], q4[3]);
-            } else {
-              const int i = w - 5;
-              float y0, y1;
-              FastP::dequant_codes(codes[i >> 2], i & 3, sc, y0, y1);
-              pf[i >> 2][i & 3] = pack_bf16x2(y0, y1);
-            }
+          for (int i = 0; i < 8; ++i) {
+            if (i < i0 || i >= i1) continue;
+            float y0, y1;
+            FastP::dequant_codes(cw[i >> 2], i & 3, sc, y0, y1);
+            pf[i >> 2][i & 3] = pack_bf16x2(y0, y1);
           }
         };
 #pragma unroll
