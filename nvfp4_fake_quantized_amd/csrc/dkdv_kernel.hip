@@ -88,6 +88,20 @@ struct DkdvLds {
   static constexpr int TOTAL = PAIR + DL + kRing * kSub * 4;
 };
 
+// X-wave VALU items of one step and their approximate instruction counts:
+// 16 elements, the scale, 4 quotient groups, the codes, the dS rows.
+constexpr int kXItems = 23;
+constexpr int x_item_cost(int i) { return i < 16 ? 6 : i == 16 ? 10 : i < 21 ? 12 : 8; }
+// MFMA slot (of nslot) in which item i is issued: items in order, spread by cost
+constexpr int x_item_slot(int i, int nslot) {
+  int before = 0, total = 0;
+  for (int t = 0; t < kXItems; ++t) {
+    if (t < i) before += x_item_cost(t);
+    total += x_item_cost(t);
+  }
+  return before * nslot / total;
+}
+
 template <int D, bool CAUSAL, bool UNIT_P>
 __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
   using L = DkdvLds<D>;
@@ -234,8 +248,42 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
           lim = qj < nq ? lim : 0;
         }
       }
+      // VALU work items, spread over the MFMA slots by their cost: the 16
+      // elements (P, dS, amax), the scale, four groups of refined
+      // quotients, the E2M1 codes (-> Y), the dS rows (-> tile)
       float p[16], ds[16];
-      float amax = 0.0f;
+      float amax = 0.0f, scv = 0.0f;
+      FastP fq(1.0f);
+      f32x4 q4[4];
+      auto item = [&](int i) __attribute__((always_inline)) {
+        if (i < 16) {
+          float x = __builtin_fmaf(sc[i], sl2, -lse2);
+          if (MASK) x = i < lim ? x : -INFINITY;
+          const float pv = fast_exp2(x);
+          ds[i] = pv * (dc[i] - dl);
+          p[i] = UNIT_P ? pv : pv * psc;
+          amax = fmaxf(amax, p[i]);
+        } else if (i == 16) {
+          scv = e4m3_scale_from_amax(amax);
+          // a zero scale divides by 1 instead (its codes are then multiplied by 0)
+          fq = FastP(scv > 0.0f ? scv : 1.0f);
+        } else if (i < 21) {
+          const int g = i - 17;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q4[g][e] = fq.quotient(p[4 * g + e]);
+        } else if (i == 21) {
+          cbuf[(R & 1) * 64 + lane] = u32x2{FastP::codes8(q4[0], q4[1]),
+                                            FastP::codes8(q4[2], q4[3])};
+          sbuf[(R & 1) * 64 + lane] = scv;
+        } else {
+          u32x4 dsb[2];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dsb[e >> 2][e & 3] = pack_bf16x2(ds[2 * e], ds[2 * e + 1]);
+          uint16_t* dt = dstile + (R & 1) * 1024;
+          *reinterpret_cast<u32x4*>(dt + pw0) = dsb[0];
+          *reinterpret_cast<u32x4*>(dt + pw1) = dsb[1];
+        }
+      };
       constexpr int NSLOT = NM > 16 ? NM : 16;
 #pragma unroll
       for (int k = 0; k < NSLOT; ++k) {
@@ -246,36 +294,12 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
           else
             sn = mfma32x32x16(kf[k >> 1], b[k], k == 0 ? zero_f32x16() : sn);
         }
-        if (DO_V && k < 16) {  // element k of this lane's 16
-          float x = __builtin_fmaf(sc[k], sl2, -lse2);
-          if (MASK) x = k < lim ? x : -INFINITY;
-          const float pv = fast_exp2(x);
-          ds[k] = pv * (dc[k] - dl);
-          p[k] = UNIT_P ? pv : pv * psc;
-          amax = fmaxf(amax, p[k]);
+        if (DO_V) {
+#pragma unroll
+          for (int i = 0; i < kXItems; ++i)
+            if (x_item_slot(i, NSLOT) == k) item(i);
         }
         __builtin_amdgcn_sched_barrier(0);
-      }
-      if (DO_V) {
-        // dS rows -> tile (j & 1); P and its group scale -> handover buffer
-        u32x4 dsb[2];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dsb[i >> 2][i & 3] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
-        uint16_t* dt = dstile + (R & 1) * 1024;
-        *reinterpret_cast<u32x4*>(dt + pw0) = dsb[0];
-        *reinterpret_cast<u32x4*>(dt + pw1) = dsb[1];
-        // the group's E2M1 codes (refined quotients, hardware RNE) go to Y
-        const float sc = e4m3_scale_from_amax(amax);
-        // a zero scale divides by 1 instead (its codes are then multiplied by 0)
-        const FastP fq(sc > 0.0f ? sc : 1.0f);
-        f32x4 q4[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q4[g][e] = fq.quotient(p[4 * g + e]);
-        cbuf[(R & 1) * 64 + lane] = u32x2{FastP::codes8(q4[0], q4[1]),
-                                          FastP::codes8(q4[2], q4[3])};
-        sbuf[(R & 1) * 64 + lane] = sc;
       }
     };
 
