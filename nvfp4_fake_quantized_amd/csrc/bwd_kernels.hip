@@ -35,6 +35,7 @@ constexpr int kDqBM = 128;              // queries per workgroup (k_dq)
 #endif
 constexpr int kDqAhead = ATTNQAT_DQ_AHEAD;  // MFMA operand reads issued this many MFMAs ahead
 
+
 // Pieces of one wave's work on one 32-key block (32 queries x 32 keys).
 //
 // A operand of S^T/dP^T MFMA k (S^T = K^ Q^T for even k, dP^T = V^ dO^T for
@@ -258,7 +259,11 @@ void k_dq(AttnArgs a) {
     // every later tile is then skipped too
     if (!MASK || !(CAUSAL && qw0 + 31 < k0)) {
       f32x16 s, dp;
+      // the MFMA-only phase runs at raised wave priority, so that the other
+      // wave on the SIMD fills its gaps rather than competing for issue
+      __builtin_amdgcn_s_setprio(1);
       dq_sdp<D>(qf, df, sK[buf], sV[buf], ro, s, dp);
+      __builtin_amdgcn_s_setprio(0);
       bf16x8 b[2];
       if (have_prev)
         dq_ds_acc<D, CAUSAL, MASK, true>(s, dp, k0, h, qi, qok, nkv, lse2, dl, sl2, b, acc,

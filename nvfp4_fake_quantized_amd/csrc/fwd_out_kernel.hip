@@ -238,7 +238,11 @@ void k_fwd_out(AttnArgs a) {
     // every later tile is then skipped too
     if (!MASK || !(CAUSAL && qw0 + 31 < k0)) {
       f32x16 s;
+      // the MFMA-only phase runs at raised wave priority (the other wave on
+      // the SIMD fills its gaps)
+      __builtin_amdgcn_s_setprio(1);
       out_s<D>(qf, sK[buf], ro, s);
+      __builtin_amdgcn_s_setprio(0);
       bf16x8 b[2];
       if (have_prev)
         out_pf_pv<D, CAUSAL, MASK, true, UNIT_P>(s, b, o, b_prev, sV[pbuf], cb, k0, h, qi, nkv,
