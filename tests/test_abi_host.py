@@ -74,6 +74,11 @@ def _prob(**kw):
     ({"softmax_scale": float("inf")}, B.ERR_INVALID_ARGUMENT),
     ({"p_scale": -1.0}, B.ERR_INVALID_ARGUMENT),
     ({"batch": 300, "heads": 300}, B.ERR_UNSUPPORTED),
+    # at most 2^28 rows per tensor (batch * heads * max(seqlen_q, seqlen_kv))
+    ({"batch": 300, "heads": 300, "seqlen_q": 128, "seqlen_kv": 128}, B.OK),
+    ({"batch": 1, "heads": 65536}, B.OK),
+    ({"batch": 1, "heads": 65537}, B.ERR_UNSUPPORTED),
+    ({"batch": 1, "heads": 65536, "seqlen_q": 16, "seqlen_kv": 4097}, B.ERR_UNSUPPORTED),
 ])
 def test_check_support(kw, code):
     assert B.attnqat_check_support(_prob(**kw)) == code
