@@ -407,6 +407,17 @@ __device__ __forceinline__ void buf_ld16_lds(const u32x4& desc, uint32_t voff, u
       : "s"(lds), "v"(voff), "s"(desc)
       : "memory", "m0");
 }
+// The same for 4 bytes per lane (buffer_load_dword ... lds): lane l's dword
+// lands at lds + 4*l.
+__device__ __forceinline__ void buf_ld4_lds(const u32x4& desc, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(desc)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t voff) {

@@ -83,9 +83,9 @@ struct DkdvLds {
   static constexpr int DS = CB + 4 * 2 * 512;        // dS[pair][2] 32x32 bf16 tiles
   static constexpr int PF = DS + 4 * 2 * 2048;       // P^F[pair] 32x32 bf16 tiles
   static constexpr int SB = PF + 4 * 2048;           // scale[pair][2][64] floats
-  static constexpr int LSE = SB + 4 * 2 * 256;       // lse[kRing][32] (raw)
-  static constexpr int DL = LSE + kRing * kSub * 4;  // delta[kRing][32]
-  static constexpr int TOTAL = PAIR + DL + kRing * kSub * 4;
+  static constexpr int LSE = SB + 4 * 2 * 256;       // lse[kRing][64] (raw; 32 used)
+  static constexpr int DL = LSE + kRing * 64 * 4;    // delta[kRing][64]
+  static constexpr int TOTAL = PAIR + DL + kRing * 64 * 4;
 };
 
 // X-wave VALU items of one step and their approximate instruction counts:
@@ -168,50 +168,43 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
     const bool keys_tail = kw0 + 32 > nkv;
     const RowOffsets<D> ro(lane);  // row reads (S, dP B operands)
 
-    // ---- staging of sub-tile j (Q^ and dO rows, lse, delta) into slot j % kRing
-    u32x4 rst[CH];
-    float rl = 0.0f;
+    // ---- staging of sub-tile j (Q^ and dO rows, lse, delta) into slot j % kRing,
+    // copied global -> LDS directly.  Copy instruction c of X wave w fills the
+    // slot's LDS chunks 64*(CH*w + c) + lane (the Q^ tile, then the dO tile);
+    // chunk (row r, position jj) of the XOR-swizzled layout holds column chunk
+    // swz(r, jj), so each lane fetches that chunk (the swizzle is an
+    // involution).  Waves 0 and 1 copy the sub-tile's lse and delta.
     uint32_t goff[CH];
-    int loff[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int idx = tid + kStagers * c;
-      const int ch = idx % NCH;
-      goff[c] = (uint32_t)((ch / CPR) * D + (ch % CPR) * 8) * 2u;
-      loff[c] = 2 * swz<D>(ch / CPR, (ch % CPR) * 8);
+      const int pc = (64 * (CH * wave + c) + lane) % NCH;
+      goff[c] = (uint32_t)swz<D>(pc / CPR, 8 * (pc % CPR)) * 2u;
     }
-    auto load_sub = [&](int j) __attribute__((always_inline)) {
+    auto issue_sub = [&](int j, auto stag) __attribute__((always_inline)) {
+      constexpr int S = decltype(stag)::value;  // ring slot
       const int q0 = qfirst + kSub * j;
       const int rows = min(nq - q0, kSub);
-      const uint32_t bytes = (uint32_t)(rows * D) * 2u;  // rows past nq read as zeros
-      const auto rsq = make_rsrc(Q + (size_t)q0 * D, bytes);
-      const auto rsd = make_rsrc(dO + (size_t)q0 * D, bytes);
+      const uint32_t bytes = (uint32_t)(rows * D) * 2u;  // rows past nq arrive as zeros
+      const u32x4 dq_ = buf_desc(Q + (size_t)q0 * D, bytes);
+      const u32x4 dd_ = buf_desc(dO + (size_t)q0 * D, bytes);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const bool is_q = 64 * wave + kStagers * c < NCH;  // uniform per wave
-        rst[c] = buf_ld16(is_q ? rsq : rsd, goff[c]);
+        const bool is_q = CH * wave + c < NCH / 64;  // uniform per instruction
+        buf_ld16_lds(is_q ? dq_ : dd_, goff[c],
+                     __builtin_amdgcn_readfirstlane(lds_addr(
+                         smem + L::RING + 2 * S * L::SUBT + 16 * 64 * (CH * wave + c))));
       }
-      // wave 0 stages lse, wave 1 delta (lanes past the sub-tile read zeros)
-      if (wave < 2)
-        rl = buf_ldf(make_rsrc((wave == 0 ? LSE : DL) + q0, (uint32_t)rows * 4u),
-                     (uint32_t)lane * 4u);
-    };
-    auto store_sub = [&](auto rtag) __attribute__((always_inline)) {
-      constexpr int S = decltype(rtag)::value;  // ring slot
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const bool is_q = 64 * wave + kStagers * c < NCH;
-        *reinterpret_cast<u32x4*>(smem + L::RING + (2 * S + (is_q ? 0 : 1)) * L::SUBT +
-                                  loff[c]) = rst[c];
-      }
-      if (wave < 2 && lane < kSub)
-        reinterpret_cast<float*>(pair + (wave == 0 ? L::LSE : L::DL))[S * kSub + lane] = rl;
+      if (wave < 2)  // lanes past the sub-tile read zeros
+        buf_ld4_lds(buf_desc((wave == 0 ? LSE : DL) + q0, (uint32_t)rows * 4u),
+                    (uint32_t)lane * 4u,
+                    __builtin_amdgcn_readfirstlane(
+                        lds_addr(pair + (wave == 0 ? L::LSE : L::DL) + S * 64 * 4)));
     };
 
     const float sl2 = a.softmax_scale * kLog2e;
     const float psc = a.p_scale;
     const float* const slse = reinterpret_cast<const float*>(pair + L::LSE);
-    const float* const sdl = reinterpret_cast<const float*>(pair + L::DL);
+    const float* const sdl = reinterpret_cast<const float*>(pair + L::DL);  // [kRing][64]
     // MFMA k of a sub-tile (slot RN): S^T for even k, dP^T for odd k, over
     // head-dim block k / 2
     auto operand = [&](int k, auto rntag) __attribute__((always_inline)) {
@@ -238,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       float lse2 = 0.0f, dl = 0.0f;
       int lim = 16;
       if (DO_V) {
-        lse2 = slse[R * kSub + l32] * kLog2e;
-        dl = sdl[R * kSub + l32];
+        lse2 = slse[R * 64 + l32] * kLog2e;
+        dl = sdl[R * 64 + l32];
         // this lane: query qj, keys kw0 + 16h + v; under MASK key v is valid
         // when v < lim (below nkv, not above the query, query below nq)
         if (MASK) {
@@ -304,15 +297,9 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
     };
 
     // prologue: sub-tiles 0 and 1 staged, S^T(0) and dP^T(0)
-    if (nsub > 0) {
-      load_sub(0);
-      store_sub(IntTag<0>());
-    }
-    if (nsub > 1) {
-      load_sub(1);
-      store_sub(IntTag<1>());
-    }
-    vmem_wait_all();  // in-loop waits then only track the loop's own prefetches
+    if (nsub > 0) issue_sub(0, IntTag<0>());
+    if (nsub > 1) issue_sub(1, IntTag<1>());
+    vmem_wait_all();  // in-loop waits then only track the loop's own copies
     __syncthreads();
     f32x16 s_even, d_even, s_odd, d_odd;  // S^T / dP^T of even and odd sub-tiles
     if (nsub > 0 && !skipped(0))
@@ -326,7 +313,9 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       f32x16& dc = (R & 1) ? d_odd : d_even;
       f32x16& sn = (R & 1) ? s_even : s_odd;
       f32x16& dn = (R & 1) ? d_even : d_odd;
-      if (j + 2 < nsub) load_sub(j + 2);
+      // slot (j+2) % kRing last held sub-tile j-2, last used by Y at step j-1
+      const bool stage = j + 2 < nsub;
+      if (stage) issue_sub(j + 2, IntTag<(R + 2) % kRing>());
       const bool do_m = j + 1 < nsub && !skipped(j + 1);
       const bool do_v = j < nsub && !skipped(j);
       const int q0 = qfirst + kSub * j;
@@ -348,8 +337,8 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
           x_step_body(j, rtag, BoolTag<false>(), BoolTag<true>(), BoolTag<false>(), sc, dc, sn,
                       dn);
       }
-      // slot (j+2) % kRing last held sub-tile j-2, last used by Y at step j-1
-      if (j + 2 < nsub) store_sub(IntTag<(R + 2) % kRing>());
+      // sub-tile j+2 has landed (this wave's copies; the barrier covers the others')
+      if (stage) vmem_wait<0>();
       __syncthreads();
     };
     for (int j0 = 0; j0 < nsteps; j0 += kRing) {
