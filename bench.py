@@ -327,6 +327,22 @@ def main():
     fq_ms = sum(hip.ms(e[0], e[3]) for e in evq) / KQ
     fq_pass_ms = sum(hip.ms(e[2], e[3]) for e in evq) / KQ
 
+    # The forward reading K^/V^ from packed NVFP4 storage (codes + scale
+    # bytes, packed once beforehand), plain calls with events around each.
+    kc, ks = B.attnqat_nvfp4_pack(kd)
+    vc, vs = B.attnqat_nvfp4_pack(vd)
+    o_p = torch.empty_like(qd)
+    lse_p = torch.empty_like(lse)
+    evk = [hip.array(2) for _ in range(KQ)]
+    for i in range(2):
+        B.attnqat_fwd_packed(p, qd, kc, ks, vc, vs, o_p, lse_p, wsf, stream)
+    for i in range(KQ):
+        hip.record(evk[i][0], stream)
+        B.attnqat_fwd_packed(p, qd, kc, ks, vc, vs, o_p, lse_p, wsf, stream)
+        hip.record(evk[i][1], stream)
+    torch.cuda.synchronize()
+    fp_ms = sum(hip.ms(e[0], e[1]) for e in evk) / KQ
+
     names_f = ["fwd_quant_qkv", "fwd_attention"]
     names_b = ["bwd_quant_q_delta", "bwd_quant_kv", "bwd_dq", "bwd_dkdv"]
     per = {n: 0.0 for n in names_f + names_b}
@@ -388,6 +404,7 @@ def main():
     for n in names_f + names_b:
         log(f"  {n:20s} {per[n]:8.4f} ms")
     log(f"  fwd with quantized output {fq_ms:.4f} ms (output pass {fq_pass_ms:.4f} ms)")
+    log(f"  fwd from packed NVFP4 K/V {fp_ms:.4f} ms")
     log(f"  with events between the kernels: fwd {fwd_ms_inst:.4f} ms, bwd {bwd_ms_inst:.4f} ms")
     log(f"  fwd {fwd_ms:.4f} ms ({fwd_tflops:.1f} TFLOP/s), bwd {bwd_ms:.4f} ms "
         f"({bwd_tflops:.1f} TFLOP/s = {100 * bwd_tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
@@ -415,6 +432,7 @@ def main():
         "fwd_tflops": round(fwd_tflops, 2),
         "kernels_ms": {n: round(per[n], 4) for n in names_f + names_b},
         "roofline": roofline,
+        "fwd_packed_kv_ms": round(fp_ms, 4),
         "fwd_quantized": {"ms": round(fq_ms, 4), "output_pass_ms": round(fq_pass_ms, 4),
                           "output_pass_tflops": round(w.fwd_flops() / (fq_pass_ms * 1e-3) / 1e12,
                                                       2)},

@@ -132,6 +132,18 @@ ATTNQAT_API int attnqat_workspace_layout(const attnqat_problem* p, int which,
 ATTNQAT_API int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_t* scales,
                                    int64_t rows, int64_t row_len, hipStream_t stream);
 
+/* Packed NVFP4 storage of a bf16 tensor (rows, row_len), row_len % 16 == 0:
+ * the same rounding as attnqat_fake_nvfp4, kept as 4-bit E2M1 codes (bit 3
+ * the sign, bits 0-2 the magnitude index into 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+ * element 2i in the low nibble and 2i+1 in the high nibble of byte i of the
+ * row) in `codes` (rows, row_len/2) and the E4M3FN scale bytes in `scales`
+ * (rows, row_len/16); value = code * scale.  4.5 bits per element instead
+ * of 16 (Attn-QAT summary, Key claims: the FP4 forward kernel keeps Q and K
+ * in block-scaled NVFP4).  x and codes 16-byte aligned; rows == 0 is a
+ * no-op; bit-exact to the definition. */
+ATTNQAT_API int attnqat_nvfp4_pack(const void* x, uint8_t* codes, uint8_t* scales,
+                                   int64_t rows, int64_t row_len, hipStream_t stream);
+
 /* QAT forward producing the backward's auxiliaries (page §High-level
  * wrapper: O_hp is softmax(Q^ K^T * scale) V^ saved before probability
  * quantization; lse its natural-log log-sum-exp).
@@ -141,6 +153,20 @@ ATTNQAT_API int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_
 ATTNQAT_API int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k,
                             const void* v, void* o_hp, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/* attnqat_fwd with K^ and V^ given in packed NVFP4 storage (for instance a
+ * cache written by attnqat_nvfp4_pack): k_codes, v_codes (B,H,Nkv,D/2) and
+ * k_scales, v_scales (B,H,Nkv,D/16).  The kernel dequantizes them to bf16
+ * exactly while staging its tiles, so o_hp and lse are bit-identical to
+ * attnqat_fwd's on the K and V the codes were made from.  q is fake-quantized
+ * as in attnqat_fwd (the workspace holds Q^ and its scales afterwards; its
+ * K^/V^ parts are not written).  q, the code arrays, o_hp, lse and the
+ * workspace 16-byte aligned; errors as attnqat_fwd. */
+ATTNQAT_API int attnqat_fwd_packed(const attnqat_problem* p, const void* q,
+                                   const uint8_t* k_codes, const uint8_t* k_scales,
+                                   const uint8_t* v_codes, const uint8_t* v_scales, void* o_hp,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 /* The full QAT forward: attnqat_fwd's work plus the quantized, user-visible
  * output O = P^F V^ (Attn-QAT summary, §Method: the FP32 softmax P is

@@ -70,6 +70,9 @@ _SIGS = {
     "attnqat_bwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                    _vp]),
     "attnqat_fwd_quantized": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "attnqat_nvfp4_pack": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]),
+    "attnqat_fwd_packed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                          _vp]),
     "attnqat_fwd_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "attnqat_fwd_quantized_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                                    _vp, _vp]),
@@ -183,6 +186,30 @@ def attnqat_fake_nvfp4(x, x_hat=None, scales=None, stream=None):
 def attnqat_fwd(p: attnqat_problem, q, k, v, o_hp, lse, workspace, stream=None):
     _check(_lib.attnqat_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp), _ptr(lse),
                             _ptr(workspace), workspace.numel(), _stream(stream)), "attnqat_fwd")
+
+
+def attnqat_nvfp4_pack(x, codes=None, scales=None, stream=None):
+    """Packed NVFP4 storage of a bf16 tensor along its last dim: returns
+    ``(codes, scales)`` (uint8, last dim L/2 and L/16)."""
+    if x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("expected a contiguous bf16 tensor")
+    L = x.shape[-1]
+    rows = x.numel() // L if L else 0
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (L // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (L // 16,), dtype=torch.uint8, device=x.device)
+    _check(_lib.attnqat_nvfp4_pack(_ptr(x), _ptr(codes), _ptr(scales), rows, L,
+                                   _stream(stream)), "attnqat_nvfp4_pack")
+    return codes, scales
+
+
+def attnqat_fwd_packed(p: attnqat_problem, q, k_codes, k_scales, v_codes, v_scales, o_hp, lse,
+                       workspace, stream=None):
+    _check(_lib.attnqat_fwd_packed(ctypes.byref(p), _ptr(q), _ptr(k_codes), _ptr(k_scales),
+                                   _ptr(v_codes), _ptr(v_scales), _ptr(o_hp), _ptr(lse),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)),
+           "attnqat_fwd_packed")
 
 
 def attnqat_fwd_quantized(p: attnqat_problem, q, k, v, o_hp, lse, o, workspace, stream=None):

@@ -160,6 +160,21 @@ int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_t* scales, i
   return e == hipSuccess ? ATTNQAT_OK : ATTNQAT_ERR_HIP;
 }
 
+int attnqat_nvfp4_pack(const void* x, uint8_t* codes, uint8_t* scales, int64_t rows,
+                       int64_t row_len, hipStream_t stream) {
+  if (rows < 0 || row_len <= 0 || (row_len % 16) != 0) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (rows > ((int64_t)1 << 40) / row_len) return ATTNQAT_ERR_UNSUPPORTED;
+  if (rows == 0) return ATTNQAT_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(codes)) return ATTNQAT_ERR_MISALIGNED;
+  const int dst = device_status();
+  if (dst != ATTNQAT_OK) return dst;
+  (void)hipGetLastError();
+  QuantJob job{x, nullptr, scales, rows * (row_len / 16)};
+  return attnqat::launch_pack_bf16(job, codes, stream) == hipSuccess ? ATTNQAT_OK
+                                                                     : ATTNQAT_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace {
@@ -220,6 +235,46 @@ int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* 
     if (attnqat::launch_fwd_out(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
     if (!record(ev, 3, stream)) return ATTNQAT_ERR_HIP;
   }
+  return ATTNQAT_OK;
+}
+
+int run_fwd_packed(const attnqat_problem* p, const void* q, const uint8_t* k_codes,
+                   const uint8_t* k_scales, const uint8_t* v_codes, const uint8_t* v_scales,
+                   void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st != ATTNQAT_OK) return st;
+  const void* ptrs[] = {q, k_codes, k_scales, v_codes, v_scales, o_hp, lse, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  const void* aligned[] = {q, k_codes, v_codes, o_hp, lse, workspace};
+  for (const void* ptr : aligned)
+    if (!aligned16(ptr)) return ATTNQAT_ERR_MISALIGNED;
+  const Layout L = make_layout(p, false);
+  if (workspace_bytes < L.total) return ATTNQAT_ERR_WORKSPACE_TOO_SMALL;
+  st = device_status();
+  if (st != ATTNQAT_OK) return st;
+  (void)hipGetLastError();
+
+  const int64_t bh = (int64_t)p->batch * p->heads;
+  uint16_t* qh = at<uint16_t>(workspace, L.q_hat);
+  QuantJob job = {q, qh, at<uint8_t>(workspace, L.q_scale), bh * p->seqlen_q * p->head_dim / 16};
+  if (attnqat::launch_quant_bf16(&job, 1, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  AttnArgs a = {};
+  a.q_hat = qh;
+  a.k_codes = k_codes;
+  a.k_scales = k_scales;
+  a.v_codes = v_codes;
+  a.v_scales = v_scales;
+  a.o_hp = static_cast<uint16_t*>(o_hp);
+  a.lse_out = lse;
+  a.bh = (int)bh;
+  a.nq = p->seqlen_q;
+  a.nkv = p->seqlen_kv;
+  a.causal = p->causal;
+  a.softmax_scale = p->softmax_scale;
+  a.p_scale = p->p_scale;
+  if (attnqat::launch_fwd_packed(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
   return ATTNQAT_OK;
 }
 
@@ -303,6 +358,13 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
                 hipStream_t stream) {
   return run_fwd(p, q, k, v, o_hp, lse, false, nullptr, workspace, workspace_bytes, stream,
                  nullptr);
+}
+int attnqat_fwd_packed(const attnqat_problem* p, const void* q, const uint8_t* k_codes,
+                       const uint8_t* k_scales, const uint8_t* v_codes,
+                       const uint8_t* v_scales, void* o_hp, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  return run_fwd_packed(p, q, k_codes, k_scales, v_codes, v_scales, o_hp, lse, workspace,
+                        workspace_bytes, stream);
 }
 int attnqat_fwd_quantized(const attnqat_problem* p, const void* q, const void* k, const void* v,
                           void* o_hp, float* lse, void* o, void* workspace,

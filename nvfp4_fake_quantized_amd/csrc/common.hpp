@@ -138,6 +138,24 @@ __device__ __forceinline__ float e2m1_dequant(float x, float s) {
   return __builtin_copysignf(c * s, x);
 }
 
+// The 4-bit E2M1 code of the same rounding (bit 3: the sign of x, bits 0-2:
+// the magnitude index into 0, 0.5, 1, 1.5, 2, 3, 4, 6; the layout of the
+// gfx950 FP4 conversions).  s == 0 yields a signed zero code.
+__device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
+  const float a = fabsf(x);
+  uint32_t k = (a > 0.25f * s) + (a >= 0.75f * s) + (a > 1.25f * s) + (a >= 1.75f * s) +
+               (a > 2.5f * s) + (a >= 3.5f * s) + (a > 5.0f * s);
+  k = s > 0.0f ? k : 0u;
+  return k | ((__float_as_uint(x) >> 31) << 3);
+}
+
+// The value of an E4M3FN scale byte (e << 3 | m, bias 7; no NaN codes are
+// produced by e4m3_byte).
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
 // Faster exact path for non-negative fp32 values (the probabilities P), used
 // where the scale is shared by the 16 values one lane holds:
 //   q  = |x|/s refined from q0 = x * rcp(s) by one FMA residual step

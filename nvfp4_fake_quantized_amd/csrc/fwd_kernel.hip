@@ -163,7 +163,7 @@ __device__ __forceinline__ void fwd_softmax_pv(const f32x16& s, float& m, float&
   m = mnew;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PACKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_FWD_WAVES, 8)))
 void k_fwd(AttnArgs a) {
   constexpr int KB = D / 16;
@@ -229,15 +229,67 @@ void k_fwd(AttnArgs a) {
                    __builtin_amdgcn_readfirstlane(lds_addr(&sV[buf][512 * (CH * wave + c)])));
     }
   };
+  // Packed K^/V^ (NVFP4 storage): thread g of the workgroup owns group g of
+  // a tile (row g / GPR, columns 16 (g % GPR) ..): it loads the 8 code bytes
+  // and the scale byte of K^ and of V^ one tile ahead, and at the end of the
+  // step writes the dequantized bf16 values (exact) into the swizzled tile.
+  constexpr int GPR = D / 16;             // groups per row
+  constexpr int NG = BN * GPR;            // groups per tile
+  const int pg = tid % NG, pr = pg / GPR, pgi = pg % GPR;
+  const bool pown = tid < NG;
+  const uint8_t* KC = a.k_codes + (size_t)bh * nkv * (D / 2);
+  const uint8_t* KS = a.k_scales + (size_t)bh * nkv * GPR;
+  const uint8_t* VC = a.v_codes + (size_t)bh * nkv * (D / 2);
+  const uint8_t* VS = a.v_scales + (size_t)bh * nkv * GPR;
+  u32x2 pkc = {0u, 0u}, pvc = {0u, 0u};
+  uint32_t pks = 0u, pvs = 0u;
+  auto load_packed = [&](int it) __attribute__((always_inline)) {
+    const int k0 = it * BN;
+    const int rows = min(nkv - k0, BN);  // rows past nkv read as zeros
+    const auto rkc = make_rsrc(KC + (size_t)k0 * (D / 2), (uint32_t)rows * (D / 2));
+    const auto rvc = make_rsrc(VC + (size_t)k0 * (D / 2), (uint32_t)rows * (D / 2));
+    const auto rks = make_rsrc(KS + (size_t)k0 * GPR, (uint32_t)rows * GPR);
+    const auto rvs = make_rsrc(VS + (size_t)k0 * GPR, (uint32_t)rows * GPR);
+    const uint32_t off = (uint32_t)pg * 8u;
+    pkc = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rkc, off, 0, 0));
+    pvc = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvc, off, 0, 0));
+    pks = __builtin_amdgcn_raw_buffer_load_b8(rks, (uint32_t)pg, 0, 0);
+    pvs = __builtin_amdgcn_raw_buffer_load_b8(rvs, (uint32_t)pg, 0, 0);
+  };
+  auto store_packed = [&](int buf) __attribute__((always_inline)) {
+    if (!pown) return;
+    auto put = [&](uint16_t* tile, u32x2 cw, uint32_t sb) __attribute__((always_inline)) {
+      const float sc = e4m3_value(sb);
+      u32x4 w[2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float y0, y1;
+        FastP::dequant_codes(cw[i >> 2], i & 3, sc, y0, y1);
+        w[i >> 2][i & 3] = pack_bf16x2(y0, y1);
+      }
+      *reinterpret_cast<u32x4*>(tile + swz<D>(pr, 16 * pgi)) = w[0];
+      *reinterpret_cast<u32x4*>(tile + swz<D>(pr, 16 * pgi + 8)) = w[1];
+    };
+    put(sK[buf], pkc, pks);
+    put(sV[buf], pvc, pvs);
+  };
 
   // Leading tiles are interior (branch-free); masks start at the first tile
   // that reaches past nkv or above the workgroup's first query (causal).
   int it_hi = min(ntiles, nkv / BN);
   if (CAUSAL) it_hi = min(it_hi, (qblk0 + 1) / BN);
 
-  if (ntiles > 0) issue_tile(0);
-  if (ntiles > 1) issue_tile(1);
-  vmem_wait_all();
+  if constexpr (PACKED) {
+    if (ntiles > 0) {
+      load_packed(0);
+      store_packed(0);
+    }
+    if (ntiles > 1) load_packed(1);
+  } else {
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    vmem_wait_all();
+  }
   __syncthreads();
 
   bf16x8 b_prev[2];
@@ -249,7 +301,9 @@ void k_fwd(AttnArgs a) {
     const int buf = it % NB;
     const int pbuf = (it + NB - 1) % NB;
     const int k0 = it * BN;
-    if (it + 2 < ntiles) issue_tile(it + 2);
+    if constexpr (!PACKED) {
+      if (it + 2 < ntiles) issue_tile(it + 2);
+    }
     // (boundary tiles only) every key above every query of this wave: skip;
     // every later tile is then skipped too
     if (!MASK || !(CAUSAL && qw0 + 31 < k0)) {
@@ -274,12 +328,18 @@ void k_fwd(AttnArgs a) {
       fwd_pv<D>(o, b_prev, sV[pbuf], co);
       have_prev = false;
     }
-    // tile it+1 has landed (this wave's copies; the barrier covers the
-    // other waves'), tile it+2 may still be in flight
-    if (it + 2 < ntiles)
-      vmem_wait<2 * CH>();
-    else
-      vmem_wait<0>();
+    if constexpr (PACKED) {
+      // buffer (it+1) % NB last held tile it-3
+      if (it + 1 < ntiles) store_packed((it + 1) % NB);
+      if (it + 2 < ntiles) load_packed(it + 2);
+    } else {
+      // tile it+1 has landed (this wave's copies; the barrier covers the
+      // other waves'), tile it+2 may still be in flight
+      if (it + 2 < ntiles)
+        vmem_wait<2 * CH>();
+      else
+        vmem_wait<0>();
+    }
     __syncthreads();
   };
   int it = 0;
@@ -310,20 +370,29 @@ void k_fwd(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream) {
+template <bool PACKED>
+hipError_t launch_fwd_t(const AttnArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid((unsigned)(((a.nq + kFwdBM - 1) / kFwdBM) * a.bh));
   if (head_dim == 128) {
     if (a.causal)
-      hipLaunchKernelGGL((k_fwd<128, true>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_fwd<128, true, PACKED>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_fwd<128, false>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_fwd<128, false, PACKED>), grid, dim3(256), 0, stream, a);
   } else {
     if (a.causal)
-      hipLaunchKernelGGL((k_fwd<64, true>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_fwd<64, true, PACKED>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_fwd<64, false>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_fwd<64, false, PACKED>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream) {
+  return launch_fwd_t<false>(a, head_dim, stream);
+}
+
+hipError_t launch_fwd_packed(const AttnArgs& a, int head_dim, hipStream_t stream) {
+  return launch_fwd_t<true>(a, head_dim, stream);
 }
 
 }  // namespace attnqat

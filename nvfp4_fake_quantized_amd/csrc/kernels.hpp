@@ -22,6 +22,10 @@ struct AttnArgs {
   uint16_t* dk;           // (BH, nkv, D)
   uint16_t* dv;           // (BH, nkv, D)
   uint16_t* o_q;          // (BH, nq, D)       quantized forward output (second pass)
+  const uint8_t* k_codes;   // (BH, nkv, D/2)  packed NVFP4 K^ (forward from packed K/V)
+  const uint8_t* k_scales;  // (BH, nkv, D/16)
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
   int bh;                 // batch * heads
   int nq, nkv;
   int causal;
@@ -39,6 +43,8 @@ struct QuantJob {
 
 // fake_nvfp4 over up to three bf16 tensors in one launch.
 hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream);
+// Packed NVFP4 codes (2 per byte) and scale bytes of one bf16 tensor.
+hipError_t launch_pack_bf16(const QuantJob& job, uint8_t* codes, hipStream_t stream);
 // fake_nvfp4 over one fp32 tensor.
 hipError_t launch_quant_f32(const QuantJob& job, hipStream_t stream);
 // Q fake-quant fused with delta = rowsum(O_hp * dO) (fp32), D in {64,128}.
@@ -47,6 +53,8 @@ hipError_t launch_quant_q_delta(const uint16_t* q, const uint16_t* o_hp, const u
                                 int64_t rows, int head_dim, hipStream_t stream);
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream);
+// The same forward with K^ and V^ given as packed NVFP4 (a.k_codes ...).
+hipError_t launch_fwd_packed(const AttnArgs& a, int head_dim, hipStream_t stream);
 // O = P^F V^ from Q^, K^, V^ and the forward's lse (a.lse), into a.o_q.
 hipError_t launch_fwd_out(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream);

@@ -67,6 +67,27 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf16(QuantJobs3 jobs) {
   if (J.scales) J.scales[g] = (uint8_t)e4m3_byte(s);
 }
 
+// Packed NVFP4 storage: per group of 16 bf16 values, 8 bytes of E2M1 codes
+// (element 2i in the low nibble of byte i, 2i+1 in the high nibble) and the
+// E4M3FN scale byte.
+__global__ __launch_bounds__(kThreads) void k_pack_bf16(QuantJob J, uint8_t* codes) {
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= J.groups) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(J.src) + 2 * g;
+  const u32x4 lo = src[0], hi = src[1];
+  float x[16];
+  unpack_bf16x16(lo, hi, x);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float s = e4m3_scale_from_amax(amax);
+  u32x2 w = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_code(x[i], s) << (4 * (i & 7));
+  reinterpret_cast<u32x2*>(codes)[g] = w;
+  J.scales[g] = (uint8_t)e4m3_byte(s);
+}
+
 __global__ __launch_bounds__(kThreads) void k_quant_f32(QuantJob J) {
   const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (g >= J.groups) return;
@@ -161,6 +182,13 @@ hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream
   if (maxg == 0) return hipSuccess;
   dim3 grid(grid_for(maxg), njobs);
   hipLaunchKernelGGL(k_quant_bf16, grid, dim3(kThreads), 0, stream, j3);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_bf16(const QuantJob& job, uint8_t* codes, hipStream_t stream) {
+  if (job.groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_bf16, dim3(grid_for(job.groups)), dim3(kThreads), 0, stream, job,
+                     codes);
   return hipGetLastError();
 }
 
