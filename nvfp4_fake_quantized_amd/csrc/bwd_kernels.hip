@@ -9,9 +9,13 @@
 // MFMA.  Layout (gfx950, wave64): each wave owns 32 queries (Q^ and dO rows
 // in registers as B operands).  S^T and dP^T accumulators hold one query per
 // lane, so dS^T feeds the B operand of dQ^T = K^T dS^T from registers; K^
-// and V^ tiles are staged row-major in double-buffered, XOR-swizzled LDS
-// (prefetched one tile ahead through registers) and the K^T operand is read
-// with LDS transpose reads.  Only tiles on a boundary (tails, causal
+// and V^ tiles are staged row-major in a 4-deep ring of XOR-swizzled LDS
+// tiles, copied global -> LDS directly two tiles ahead, and the K^T operand
+// is read with LDS transpose reads.  Software pipeline: step t issues the
+// S^T/dP^T MFMAs of tile t (at raised wave priority), then the dS VALU work
+// of tile t interleaved with the dQ^T MFMAs of tile t-1.  Causal launches
+// hand out each head's query tiles last-first (the heaviest first).  Only
+// tiles on a boundary (tails, causal
 // diagonal) evaluate masks; causal tiles entirely above the diagonal are
 // skipped per wave, the diagonal tile keeps the elementwise key <= query
 // mask, keys >= Nkv get P = 0, loads beyond the ends read zeros and stores

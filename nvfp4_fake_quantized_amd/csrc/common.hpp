@@ -19,16 +19,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Build-time tiling knobs (defaults are the tuned values).
-// Waves per SIMD the register allocation of each attention kernel targets.
+// Build-time knobs (defaults are the tuned values): waves per SIMD that the
+// register allocation of the forward and dQ kernels targets (the dK/dV
+// kernel's 512-thread workgroup fixes its own: two waves per SIMD).
 #ifndef ATTNQAT_FWD_WAVES
 #define ATTNQAT_FWD_WAVES 2
 #endif
 #ifndef ATTNQAT_DQ_WAVES
 #define ATTNQAT_DQ_WAVES 2
-#endif
-#ifndef ATTNQAT_DKDV_WAVES
-#define ATTNQAT_DKDV_WAVES 1
 #endif
 // Steps by which the dK/dV pipeline reads its LDS MFMA operands ahead.
 #ifndef ATTNQAT_DKDV_PREFETCH

@@ -9,14 +9,19 @@
 //  * the key loop stages 32-key tiles of K^ and V^ row-major (XOR-swizzled
 //    16-byte chunks) in a 4-deep LDS ring, copied global -> LDS directly two
 //    tiles ahead; the V^T operand is read with LDS transpose reads;
-//  * software pipeline: step t issues the S^T MFMAs of tile t, then the
-//    softmax VALU work of tile t interleaved with the O^T MFMAs of tile t-1;
+//  * software pipeline: step t issues the S^T MFMAs of tile t (at raised
+//    wave priority), then the softmax VALU work of tile t interleaved with
+//    the O^T MFMAs of tile t-1;
+//  * a PACKED instance reads K^/V^ from packed NVFP4 storage (E2M1 codes
+//    and E4M3 scale bytes) through registers one tile ahead and writes the
+//    exactly dequantized bf16 values into the same LDS tiles;
 //  * S^T's accumulator layout puts one query per lane (and 16 of its keys in
 //    VGPRs), so the online-softmax row statistics are per lane (plus one
 //    exchange with the lane 32 away), and P^T feeds the B operand of
 //    O^T = V^T P^T straight from registers;
 //  * the running max only triggers a rescale of the accumulator when it
-//    moved for some row of the wave (otherwise the factor is exactly 1);
+//    moved for some row of the wave (otherwise the factor is exactly 1),
+//    applied just before the next tile's P^T V^ is added;
 //  * only boundary tiles (the last key tiles: tail, causal diagonal) evaluate
 //    masks; the leading tiles run a branch-free loop;
 //  * causal: tiles with every key above the wave's last query are skipped
