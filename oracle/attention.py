@@ -191,6 +191,22 @@ def qat_backward_full_head(q, k, v, o_hp, do, lse, softmax_scale: float, causal:
     return dq, dk, dv
 
 
+def qat_ds_head(q, k, v, o_hp, do, lse, softmax_scale: float, causal: bool):
+    """The backward's dS = P * (dO V^T - rowsum(O_hp * dO)) of one head,
+    (Nq, Nk) in fp64 (page "NVFP4 Attention QAT Backward", §Overview formula
+    block), with P recomputed from lse from the fake-quantized Q^ and K^ and
+    masked entries 0.  dQ = s dS K^ and dK = s dS^T Q^ of
+    :func:`qat_backward_head` are products with it."""
+    q, k, v, o_hp, do, lse = map(_as64, (q, k, v, o_hp, do, lse))
+    Nq, Nk = q.shape[0], k.shape[0]
+    if causal and Nq != Nk:
+        raise ValueError("causal attention is self-attention only (Nq == Nk)")
+    qh, kh, vh = quantize_qkv(q, k, v)
+    delta = (o_hp * do).sum(axis=1)
+    P = _probabilities(qh, kh, lse, softmax_scale, causal, np.arange(Nq), np.arange(Nk))
+    return P * (do @ vh.T - delta[:, None])
+
+
 def _heads(B, H, heads):
     return [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
 

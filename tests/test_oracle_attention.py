@@ -17,8 +17,8 @@ import pytest
 import torch
 
 from oracle.attention import (qat_backward, qat_backward_full_head, qat_backward_head,
-                              qat_forward, qat_forward_head, qat_forward_quantized_head,
-                              quantize_qkv)
+                              qat_ds_head, qat_forward, qat_forward_head,
+                              qat_forward_quantized_head, quantize_qkv)
 from oracle.nvfp4 import fake_nvfp4_values
 from workloads import make_inputs
 
@@ -147,6 +147,25 @@ def test_ds_rows_and_dk_sum_to_zero():
     # recover dS from dQ = s dS K^ and check its rows sum to zero
     dS = np.linalg.lstsq(kh.T, (dq / s).T, rcond=None)[0].T
     assert np.max(np.abs(dS.sum(1))) <= 1e-9
+
+
+@pytest.mark.parametrize("causal,n,nk", [(False, 40, 72), (True, 56, 56)])
+def test_ds_intermediate(causal, n, nk):
+    """dS reproduces dQ = s dS K^ and dK = s dS^T Q^ (both pinned against
+    autograd above), its rows sum to zero (softmax Jacobian, O_hp exact) and
+    causal entries above the diagonal are exactly zero."""
+    q, k, v, do = _heads_np(n, 64, seed=n + nk, nk=nk)
+    s = 0.11
+    o, lse = qat_forward_head(q, k, v, s, causal)
+    qh, kh, _ = quantize_qkv(q, k, v)
+    dS = qat_ds_head(q, k, v, o, do, lse, s, causal)
+    dq, dk, _ = qat_backward_head(q, k, v, o, do, lse, s, causal)
+    assert dS.shape == (n, nk)
+    assert np.max(np.abs(s * dS @ kh - dq)) <= 1e-12 * np.abs(dq).max()
+    assert np.max(np.abs(s * dS.T @ qh - dk)) <= 1e-12 * np.abs(dk).max()
+    assert np.max(np.abs(dS.sum(1))) <= 1e-12 * np.abs(dS).max() * nk
+    if causal:
+        assert np.all(dS[np.triu_indices(n, 1)] == 0.0)
 
 
 def test_causal_row_zero_closed_form():
