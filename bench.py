@@ -4,7 +4,9 @@
 One step = one pass of the whole hot path over one batch: attnqat_fwd (Q/K/V
 fake-quant + the QAT forward producing O_hp and lse) followed by
 attnqat_bwd on that output (Q fake-quant + delta, K/V fake-quant, dQ,
-dK/dV).  Inputs are resident in HBM before timing starts.
+dK/dV).  Inputs are resident in HBM before timing starts; warmup steps
+bring the clocks to their steady state first (the kernels' durations drift
+over the first few dozen steps as the power management settles).
 
 The reported metric is the backward's throughput: counted backward work
 10*B*H*N^2*D (halved when causal) divided by the backward's own duration,
@@ -238,8 +240,8 @@ def p_scale_study(p_scales=(1.0, 64.0, 512.0, 2688.0), reps=5):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="ref_shape")
     ap.add_argument("--p-scale", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
