@@ -259,6 +259,36 @@ def test_single_token_causal_closed_form():
     assert float(dq.abs().max()) <= 2e-3 * float(do.abs().max())
 
 
+@pytest.mark.parametrize("mag", [3000.0, 0.02])
+def test_extreme_magnitudes(mag):
+    """Inputs far outside N(0,1): at 3000 most groups' amax/6 exceeds E4M3's
+    448, so Q^/K^/V^ saturate (scale 448, codes up to 6); at 0.02 the scales
+    (amax/6 below 2^-6) sit in E4M3's subnormal range.  The softmax scale
+    keeps the logits of order one."""
+    q, k, v, do = _synthetic(160, 64, seed=int(mag * 7) % 1000 + 3, heads=2)
+    q, k, v = (t.float().mul(mag).to(torch.bfloat16) for t in (q, k, v))
+    codes = np.concatenate([fake_nvfp4(t[0, 0].double().numpy())[2].ravel() for t in (q, k, v)])
+    if mag > 1:
+        assert np.mean(codes == 0x7E) > 0.5  # scale 448: saturated groups
+    else:
+        assert np.all(codes < 8) and np.all(codes > 0)  # E4M3 subnormal scales
+    scale = 1.0 / (8.0 * 2688.0 * 2688.0) if mag > 1 else 100.0
+    run_full_case(q, k, v, do, False, scale, label=f"magnitude {mag:g}")
+
+
+@pytest.mark.parametrize("p_scale", [0.25, 1e4])
+def test_p_scale_below_one_and_large(p_scale):
+    q, k, v, do = _synthetic(96, 128, seed=41, heads=2)
+    run_full_case(q, k, v, do, True, 1.0 / math.sqrt(128), p_scale=p_scale,
+                  label=f"p_scale {p_scale:g}")
+
+
+def test_batched_cross_attention_d64():
+    """B2 H3, 640 queries against 1000 keys (tails on both axes), D = 64."""
+    q, k, v, do = _synthetic(640, 64, seed=17, nk=1000, heads=3, batch=2)
+    run_full_case(q, k, v, do, False, 0.125, heads=[(0, 0), (1, 2)], label="cross B2 H3")
+
+
 def test_p_scale_on_causal_workload():
     w = WORKLOADS["small_causal"]
     q, k, v, do = make_inputs(w, heads=2)
