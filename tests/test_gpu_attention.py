@@ -178,6 +178,22 @@ def test_ref_shape_workload():
                                     rows=rows)
         check_close(o_g[0, h, rows].cpu(), o64, f"ref_shape O_hp rows h={h}")
         check_close(lse_g[0, h, rows].cpu(), l64, f"ref_shape lse rows h={h}")
+    # every head: sampled backward rows and key groups, on the GPU forward's
+    # own outputs (the launch configuration the bench times).  The relative
+    # Frobenius bar is a whole-tensor measure; a sample of a few rows is
+    # dominated by the rows whose dQ nearly cancels, so the sample is the
+    # forward's 48 rows and 6 key groups, as in the other sampled checks.
+    dq, dk, dv, _, _ = gpu_bwd(qd, kd, vd, o_g, do.to(DEV), lse_g, w.causal, w.softmax_scale)
+    brows = rows
+    groups = [0, 77, 128, 200, 254, 255]
+    keys = np.concatenate([np.arange(16 * g, 16 * g + 16) for g in groups])
+    for h in range(w.heads):
+        rq, rk, rv = qat_backward_head(q[0, h], k[0, h], v[0, h], o_g[0, h].cpu(), do[0, h],
+                                       lse_g[0, h].cpu(), w.softmax_scale, w.causal,
+                                       rows=brows, key_groups=groups)
+        check_close(dq[0, h, brows].cpu(), rq, f"ref_shape dQ rows h={h}")
+        check_close(dk[0, h, keys].cpu(), rk, f"ref_shape dK groups h={h}")
+        check_close(dv[0, h, keys].cpu(), rv, f"ref_shape dV groups h={h}")
 
 
 def _sampled_big_workload(name, heads, n_rows=96, n_groups=6):
