@@ -327,6 +327,32 @@ def test_bitwise_deterministic_and_stream_ordered():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_results_do_not_depend_on_workspace_or_output_contents(causal):
+    """Workspaces and outputs pre-filled with NaN bit patterns (0xFF bytes)
+    give bit-identical results to zero-filled ones: nothing reads memory the
+    call has not written."""
+    n, d, H = 333, 128, 2
+    q, k, v, do = (t.to(DEV) for t in _synthetic(n, d, seed=23, heads=H))
+    p = B.problem_for(q, k, causal, 0.1)
+    res = []
+    for fill in (0x00, 0xFF):
+        wsf = torch.full((B.attnqat_fwd_workspace_bytes(p),), fill, dtype=torch.uint8, device=DEV)
+        wsb = torch.full((B.attnqat_bwd_workspace_bytes(p),), fill, dtype=torch.uint8, device=DEV)
+        outs = [torch.full_like(q, 0.0).view(torch.int16).fill_(-1 if fill else 0).view(torch.bfloat16)
+                for _ in range(4)]
+        o, dq, dk, dv = outs
+        lse = torch.full((1, H, n), float("nan") if fill else 0.0, device=DEV)
+        B.attnqat_fwd(p, q, k, v, o, lse, wsf)
+        B.attnqat_bwd(p, q, k, v, o, do, lse, dq, dk, dv, wsb)
+        torch.cuda.synchronize()
+        res.append([t.clone() for t in (o, lse, dq, dk, dv)])
+    for a_, b_ in zip(*res):
+        assert torch.equal(a_.view(torch.uint8) if a_.dtype != torch.float32 else a_,
+                           b_.view(torch.uint8) if b_.dtype != torch.float32 else b_)
+        assert torch.all(torch.isfinite(a_.float()))
+
+
 def test_outputs_and_workspace_stay_in_bounds():
     """Canary guard bands after every output and the workspace."""
     n, d, H = 200, 64, 2
