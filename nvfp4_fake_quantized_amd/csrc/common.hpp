@@ -87,35 +87,35 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // E4M3FN block scale of a group with max magnitude `amax` (finite, >= 0):
 // the E4M3FN value nearest to amax/6, ties to the even mantissa, saturating
 // at 448.  y approximates amax/6 by a product with the fp32 reciprocal of 6
-// and one FMA residual correction; rounding y to E4M3 as below gives the
-// exact rounding of amax/6 for every finite non-negative fp32 amax (checked
-// exhaustively over all 2^31 - 2^23 such values against exact comparisons
-// with 6 times the E4M3 midpoints).  The plain product alone does not.
-__device__ __forceinline__ float e4m3_scale_from_amax(float amax) {
+// and one FMA residual correction; rounding y to E4M3 gives the exact
+// rounding of amax/6 for every finite non-negative fp32 amax (checked
+// exhaustively over all such values against exact comparisons with 6 times
+// the E4M3 midpoints).  The plain product alone does not.
+__device__ __forceinline__ float e4m3_quotient(float amax) {
   constexpr float kSixth = 1.0f / 6.0f;
   const float y0 = amax * kSixth;
-  const float y = __builtin_fmaf(__builtin_fmaf(-y0, 6.0f, amax), kSixth, y0);
-  float s;
-  if (y < 0x1p-6f) {
-    // subnormal E4M3 range: multiples of 2^-9 (y * 512 is exact)
-    s = __builtin_rintf(y * 512.0f) * 0x1p-9f;
-  } else {
-    // keep 3 mantissa bits, round to nearest even on the fp32 bit pattern
-    uint32_t u = __float_as_uint(y);
-    u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
-    s = __uint_as_float(u);
-  }
-  return fminf(s, 448.0f);
+  return __builtin_fmaf(__builtin_fmaf(-y0, 6.0f, amax), kSixth, y0);
 }
 
-// The E4M3FN byte (e << 3 | m, bias 7) of a scale produced above.
-__device__ __forceinline__ uint32_t e4m3_byte(float s) {
-  if (s < 0x1p-6f) return (uint32_t)(s * 512.0f);
-  const uint32_t u = __float_as_uint(s);
-  const uint32_t e = ((u >> 23) & 0xFFu) - 120u;  // -127 + 7
-  const uint32_t m = (u >> 20) & 7u;
-  return (e << 3) | m;
+// The E4M3FN byte (e << 3 | m, bias 7) nearest to y >= 0, ties to even,
+// saturating at 448: the gfx950 FP8 conversion rounds to nearest even on
+// the OCP E4M3FN grid (subnormals included) and yields NaN above 464, hence
+// the clamp.
+__device__ __forceinline__ uint32_t e4m3_rne_byte(float y) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(y, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
+
+// The value of an E4M3FN byte (no NaN codes are produced above).
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+}
+
+__device__ __forceinline__ float e4m3_scale_from_amax(float amax) {
+  return e4m3_value(e4m3_rne_byte(e4m3_quotient(amax)));
+}
+
+// The E4M3FN byte of a scale produced above (an exact conversion).
+__device__ __forceinline__ uint32_t e4m3_byte(float s) { return e4m3_rne_byte(s); }
 
 // Dequantized E2M1 value c * s (with the sign of x) for c = RNE(|x| / s).
 // Comparing |x| with the exact products m * s of the E2M1 midpoints m is the
@@ -147,32 +147,32 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
   return k | ((__float_as_uint(x) >> 31) << 3);
 }
 
-// The value of an E4M3FN scale byte (e << 3 | m, bias 7; no NaN codes are
-// produced by e4m3_byte).
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-}
-
 // Faster exact path for non-negative fp32 values (the probabilities P), used
 // where the scale is shared by the 16 values one lane holds:
-//   q  = |x|/s refined from q0 = x * rcp(s) by one FMA residual step
-//        (q0 + (x - q0*s) * rcp(s)),
+//   q  = |x|/s from a two-term reciprocal: r_hi = rcp(s) and
+//        r_lo = (1 - r_hi*s) * r_hi (one FMA residual step), then
+//        q = fma(x, r_hi, x * r_lo), which is x/s within a relative 2^-46
+//        before its final rounding,
 //   c  = RNE_E2M1(q) by the hardware FP4 conversion (scale 1: no scaling;
 //        ties to even, saturating at 6), converted back to fp32,
 //   x^ = c * s.
-// For every E4M3 scale s and every fp32 x in [0.2 s, 8 s) the code c equals
-// the exact comparison result of e2m1_dequant (checked exhaustively on gfx950;
-// below 0.2 s both give 0 and at or above 8 s both saturate at 6).  s == 0
+// An exact tie x = m*s (m an E2M1 midpoint) yields q = m exactly and the
+// conversion rounds it to even; otherwise x/s lies more than 1.06 half-ulps
+// of m away from m (x and m*s are distinct fp32 values and m*s has at most
+// 7 significant bits), so q falls on the same side of m as x/s.  Hence c is
+// the code of the exact quotient for every fp32 x >= 0 (checked
+// exhaustively on the CPU for every fp32 x in [0.125 s, 8 s) and every E4M3
+// mantissa of s, with rcp within 1 ulp; below 0.125 s both give 0).  s == 0
 // uses rcp 0 and yields 0.
 struct FastP {
-  float s, r;
+  float s, r, rl;
   __device__ __forceinline__ explicit FastP(float scale)
-      : s(scale), r(scale > 0.0f ? __builtin_amdgcn_rcpf(scale) : 0.0f) {}
-  // the refined quotient x / s (x >= 0)
+      : s(scale), r(scale > 0.0f ? __builtin_amdgcn_rcpf(scale) : 0.0f) {
+    rl = __builtin_fmaf(-r, scale, 1.0f) * r;
+  }
+  // x / s for x >= 0 (see above)
   __device__ __forceinline__ float quotient(float x) const {
-    const float a = x * r;
-    return __builtin_fmaf(__builtin_fmaf(-a, s, x), r, a);
+    return __builtin_fmaf(x, r, x * rl);
   }
   // E2M1-rounded quotients q0, q1 times the scale s
   __device__ __forceinline__ static void dequant_pair(float q0, float q1, float s, float& y0,
@@ -320,6 +320,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// bf16 pair of two floats that are exactly representable in bf16 (their low
+// 16 bits are zero): a byte permute instead of a rounding conversion.
+__device__ __forceinline__ uint32_t pack_exact_bf16x2(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // Returns x unchanged but makes the compiler materialize it here: the value

@@ -60,7 +60,13 @@ constexpr int kRing = 4;       // Q^/dO sub-tile slots (also the unroll factor)
 #define ATTNQAT_DKDV_AHEAD 2
 #endif
 #ifndef ATTNQAT_DKDV_AHEAD_Y
-#define ATTNQAT_DKDV_AHEAD_Y 2
+#define ATTNQAT_DKDV_AHEAD_Y 4
+#endif
+#ifndef ATTNQAT_DKDV_SGB
+#define ATTNQAT_DKDV_SGB 1
+#endif
+#ifndef ATTNQAT_DKDV_SGB_VALU
+#define ATTNQAT_DKDV_SGB_VALU 8
 #endif
 constexpr int kAhead = ATTNQAT_DKDV_AHEAD;     // X: MFMA operand reads issued this many MFMAs ahead
 constexpr int kAheadY = ATTNQAT_DKDV_AHEAD_Y;  // Y: the same
@@ -79,19 +85,19 @@ struct DkdvLds {
   static constexpr int RING = 0;                        // slot r: Q^ at 2r SUBT, dO at (2r+1) SUBT
   static constexpr int PAIR = RING + kRing * 2 * SUBT;  // per-pair buffers start here
   // offsets within the per-pair area
-  static constexpr int CB = 0;                       // E2M1 codes[pair][2][64 lanes] (8 B)
-  static constexpr int DS = CB + 4 * 2 * 512;        // dS[pair][2] 32x32 bf16 tiles
-  static constexpr int PF = DS + 4 * 2 * 2048;       // P^F[pair] 32x32 bf16 tiles
-  static constexpr int SB = PF + 4 * 2048;           // scale[pair][2][64] floats
-  static constexpr int LSE = SB + 4 * 2 * 256;       // lse[kRing][64] (raw; 32 used)
+  static constexpr int DS = 0;                       // dS[pair][2] 32x32 bf16 tiles
+  static constexpr int PF = DS + 4 * 2 * 2048;       // P^F[pair][2] 32x32 bf16 tiles
+  static constexpr int LSE = PF + 4 * 2 * 2048;      // lse[kRing][64] (raw; 32 used)
   static constexpr int DL = LSE + kRing * 64 * 4;    // delta[kRing][64]
   static constexpr int TOTAL = PAIR + DL + kRing * 64 * 4;
 };
 
 // X-wave VALU items of one step and their approximate instruction counts:
-// 16 elements, the scale, 4 quotient groups, the codes, the dS rows.
-constexpr int kXItems = 23;
-constexpr int x_item_cost(int i) { return i < 16 ? 6 : i == 16 ? 10 : i < 21 ? 12 : 8; }
+// 16 elements, the scale, 4 quotient groups, 2 halves of P^F, the dS rows.
+constexpr int kXItems = 24;
+constexpr int x_item_cost(int i) {
+  return i < 16 ? 6 : i == 16 ? 5 : i < 21 ? 12 : i < 23 ? 22 : 10;
+}
 // MFMA slot (of nslot) in which item i is issued: items in order, spread by cost
 constexpr int x_item_slot(int i, int nslot) {
   int before = 0, total = 0;
@@ -144,9 +150,8 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
     return reinterpret_cast<const uint16_t*>(smem + L::RING + (2 * slot + tensor) * L::SUBT);
   };
   uint8_t* const pair = smem + L::PAIR;
-  u32x2* const cbuf = reinterpret_cast<u32x2*>(pair + L::CB + kk * 2 * 512);
-  float* const sbuf = reinterpret_cast<float*>(pair + L::SB + kk * 2 * 256);
   uint16_t* const dstile = reinterpret_cast<uint16_t*>(pair + L::DS + kk * 2 * 2048);
+  uint16_t* const pftile = reinterpret_cast<uint16_t*>(pair + L::PF + kk * 2 * 2048);
   const int pw0 = swz<32>(l32, 16 * h), pw1 = swz<32>(l32, 16 * h + 8);  // tile row writes
 
   if (is_x) {
@@ -166,6 +171,10 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       }
     }
     const bool keys_tail = kw0 + 32 > nkv;
+    // A operand of the delta MFMA: k = 0, 1, 2 of every key row are -1 (bf16
+    // 0xBF80), the other k are 0
+    const bf16x8 adl = __builtin_bit_cast(
+        bf16x8, h == 0 ? u32x4{0xBF80BF80u, 0x0000BF80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
     const RowOffsets<D> ro(lane);  // row reads (S, dP B operands)
 
     // ---- staging of sub-tile j (Q^ and dO rows, lse, delta) into slot j % kRing,
@@ -224,15 +233,25 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       constexpr bool MASK = decltype(mask_tag)::value;
       constexpr int NM = 2 * KB;  // MFMAs per sub-tile
       bf16x8 b[NM];
+      bf16x8 bdl;  // -delta of sub-tile j+1 as three bf16 terms (see adl)
       if (DO_M) {
 #pragma unroll
         for (int k = 0; k < kAhead; ++k) b[k] = operand(k, IntTag<RN>());
+        // delta = d1 + d2 + d3 exactly: d1, d2 take the top 8 significant
+        // bits of delta and of its remainder (exact truncations), d3 the
+        // last 8 (fits bf16)
+        const float dl1 = sdl[RN * 64 + l32];
+        const float d1 = __uint_as_float(__float_as_uint(dl1) & 0xFFFF0000u);
+        const float r1 = dl1 - d1;
+        const float d2 = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+        const float d3 = r1 - d2;
+        bdl = __builtin_bit_cast(bf16x8, u32x4{pack_exact_bf16x2(d1, d2),
+                                               __float_as_uint(d3) >> 16, 0u, 0u});
       }
-      float lse2 = 0.0f, dl = 0.0f;
+      float lse2 = 0.0f;
       int lim = 16;
       if (DO_V) {
         lse2 = slse[R * 64 + l32] * kLog2e;
-        dl = sdl[R * 64 + l32];
         // this lane: query qj, keys kw0 + 16h + v; under MASK key v is valid
         // when v < lim (below nkv, not above the query, query below nq)
         if (MASK) {
@@ -243,31 +262,45 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       }
       // VALU work items, spread over the MFMA slots by their cost: the 16
       // elements (P, dS, amax), the scale, four groups of refined
-      // quotients, the E2M1 codes (-> Y), the dS rows (-> tile)
+      // quotients, P^F = E2M1(quotient) * scale in two halves (-> tile),
+      // the dS rows (-> tile)
       float p[16], ds[16];
       float amax = 0.0f, scv = 0.0f;
       FastP fq(1.0f);
       f32x4 q4[4];
+      u32x4 pfw[2];
       auto item = [&](int i) __attribute__((always_inline)) {
         if (i < 16) {
           float x = __builtin_fmaf(sc[i], sl2, -lse2);
           if (MASK) x = i < lim ? x : -INFINITY;
           const float pv = fast_exp2(x);
-          ds[i] = pv * (dc[i] - dl);
+          ds[i] = pv * dc[i];  // dc holds dP - delta
           p[i] = UNIT_P ? pv : pv * psc;
           amax = fmaxf(amax, p[i]);
         } else if (i == 16) {
           scv = e4m3_scale_from_amax(amax);
-          // a zero scale divides by 1 instead (its codes are then multiplied by 0)
+          // a zero scale divides by 1 instead (its values are then multiplied by 0)
           fq = FastP(scv > 0.0f ? scv : 1.0f);
         } else if (i < 21) {
           const int g = i - 17;
 #pragma unroll
           for (int e = 0; e < 4; ++e) q4[g][e] = fq.quotient(p[4 * g + e]);
-        } else if (i == 21) {
-          cbuf[(R & 1) * 64 + lane] = u32x2{FastP::codes8(q4[0], q4[1]),
-                                            FastP::codes8(q4[2], q4[3])};
-          sbuf[(R & 1) * 64 + lane] = scv;
+        } else if (i < 23) {
+          // P^F of elements 8h'..8h'+7 (h' = i - 21): E2M1 rounding of the
+          // quotients, times the scale (exact in bf16)
+          const int hh = i - 21;
+          const uint32_t cw = FastP::codes8(q4[2 * hh], q4[2 * hh + 1]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float y0, y1;
+            FastP::dequant_codes(cw, e, scv, y0, y1);
+            pfw[hh][e] = pack_exact_bf16x2(y0, y1);
+          }
+          if (hh == 1) {
+            uint16_t* pt = pftile + (R & 1) * 1024;
+            *reinterpret_cast<u32x4*>(pt + pw0) = pfw[0];
+            *reinterpret_cast<u32x4*>(pt + pw1) = pfw[1];
+          }
         } else {
           u32x4 dsb[2];
 #pragma unroll
@@ -282,15 +315,29 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       for (int k = 0; k < NSLOT; ++k) {
         if (DO_M && k < NM) {
           if (k + kAhead < NM) b[k + kAhead] = operand(k + kAhead, IntTag<RN>());
-          if (k & 1)
-            dn = mfma32x32x16(vf[k >> 1], b[k], k == 1 ? zero_f32x16() : dn);
-          else
+          if (k & 1) {
+            // the dP^T chain starts from -delta: (-1, -1, -1) x (d1, d2, d3)
+            if (k == 1) dn = mfma32x32x16(adl, bdl, zero_f32x16());
+            dn = mfma32x32x16(vf[k >> 1], b[k], dn);
+          } else {
             sn = mfma32x32x16(kf[k >> 1], b[k], k == 0 ? zero_f32x16() : sn);
+          }
         }
         if (DO_V) {
 #pragma unroll
           for (int i = 0; i < kXItems; ++i)
             if (x_item_slot(i, NSLOT) == k) item(i);
+        }
+        if (!(ATTNQAT_DKDV_SGB && DO_M && DO_V)) __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (ATTNQAT_DKDV_SGB && DO_M && DO_V) {
+        // one scheduling region for the whole step: the compiler fills the
+        // VALU groups between consecutive MFMAs with ready instructions
+#pragma unroll
+        for (int k = 0; k < NM + 1; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, ATTNQAT_DKDV_SGB_VALU, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -348,11 +395,10 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       x_step(j0 + 3, IntTag<3>());
     }
   } else {
-    // ---- Y, step j: P^F(j-1); dV += P^F^T dO(j-1), dK += dS^T Q^(j-1)
-    const float psc = a.p_scale;
+    // ---- Y, step j: dK += dS^T Q^(j-1), dV += P^F^T dO(j-1), with dS and
+    // P^F from X's tiles of the previous step: MFMAs and LDS reads only
     const ColOffsets<D> co(8 * h, 8 * h + 4, lane);   // column reads (dV, dK B operands)
     const ColOffsets<32> cp(8 * h, 8 * h + 4, lane);  // key-column reads of P^F / dS tiles
-    uint16_t* const pftile = reinterpret_cast<uint16_t*>(pair + L::PF + kk * 2048);
     f32x16 dv[DB], dk[DB];  // lane -> d, VGPR -> key
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -367,59 +413,37 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       constexpr int RP = (R + kRing - 1) % kRing;  // slot of sub-tile j-1
       if (j >= nsteps) return;
       if (j >= 1 && !skipped(j - 1)) {  // j - 1 < nsub holds for j < nsteps
-        const float sc = sbuf[(RP & 1) * 64 + lane];
-        const u32x2 cw = cbuf[(RP & 1) * 64 + lane];  // 16 E2M1 codes from X
         const uint16_t* dt = dstile + (RP & 1) * 1024;
-        const uint16_t* sQ = ring(RP, 0);
-        const uint16_t* sDO = ring(RP, 1);
+        const uint16_t* pt = pftile + (RP & 1) * 1024;
         constexpr int NH = 2 * DB;  // MFMAs per product (dK, dV)
-        // B operand of MFMA k of a product: 16-query k-block k / DB, d block k % DB
-        auto operand = [&](const uint16_t* tile, int k) __attribute__((always_inline)) {
-          return lds_operand_cols_at(tile + 16 * (k / DB) * D, co.a[k % DB], co.b[k % DB]);
+        // B operand of MFMA k: the dK product (Q^ columns) for k < NH, then
+        // the dV product (dO columns); 16-query k-block (k % NH) / DB, d
+        // block k % DB
+        auto operand = [&](int k) __attribute__((always_inline)) {
+          const uint16_t* tile = ring(RP, k < NH ? 0 : 1);
+          const int kk2 = k % NH;
+          return lds_operand_cols_at(tile + 16 * (kk2 / DB) * D, co.a[kk2 % DB], co.b[kk2 % DB]);
         };
-        // dK += dS^T Q^ first (dS arrived with the step), interleaved with the
-        // P^F VALU work: P^F = code * scale, packed to bf16
         const bf16x8 as[2] = {lds_operand_cols_at(dt, cp.a[0], cp.b[0]),
                               lds_operand_cols_at(dt + 16 * 32, cp.a[0], cp.b[0])};
-        bf16x8 b[NH];
+        bf16x8 b[2 * NH];
 #pragma unroll
-        for (int k = 0; k < kAheadY; ++k) b[k] = operand(sQ, k);
-        u32x4 pf[2];
-        // VALU share of dK MFMA k (NH = 8 for D = 128, 4 for D = 64): the 8
-        // dequantized pairs
-        auto valu_part = [&](int part, int nparts) __attribute__((always_inline)) {
-          const int i0 = part * 8 / nparts, i1 = (part + 1) * 8 / nparts;
+        for (int k = 0; k < kAheadY; ++k) b[k] = operand(k);
+        bf16x8 ap[2];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            if (i < i0 || i >= i1) continue;
-            float y0, y1;
-            FastP::dequant_codes(cw[i >> 2], i & 3, sc, y0, y1);
-            pf[i >> 2][i & 3] = pack_bf16x2(y0, y1);
+        for (int k = 0; k < 2 * NH; ++k) {
+          if (k + kAheadY < 2 * NH) b[k + kAheadY] = operand(k + kAheadY);
+          if (k == NH - kAheadY || (NH <= kAheadY && k == 0)) {
+            ap[0] = lds_operand_cols_at(pt, cp.a[0], cp.b[0]);
+            ap[1] = lds_operand_cols_at(pt + 16 * 32, cp.a[0], cp.b[0]);
           }
-        };
-#pragma unroll
-        for (int k = 0; k < NH; ++k) {
-          if (k + kAheadY < NH) b[k + kAheadY] = operand(sQ, k + kAheadY);
-          dk[k % DB] = mfma32x32x16(as[k / DB], b[k], dk[k % DB]);
-          valu_part(k, NH);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        *reinterpret_cast<u32x4*>(pftile + pw0) = pf[0];
-        *reinterpret_cast<u32x4*>(pftile + pw1) = pf[1];
-        wave_lds_fence();
-        // dV += P^F^T dO
-        const bf16x8 ap[2] = {lds_operand_cols_at(pftile, cp.a[0], cp.b[0]),
-                              lds_operand_cols_at(pftile + 16 * 32, cp.a[0], cp.b[0])};
-#pragma unroll
-        for (int k = 0; k < kAheadY; ++k) b[k] = operand(sDO, k);
-#pragma unroll
-        for (int k = 0; k < NH; ++k) {
-          if (k + kAheadY < NH) b[k + kAheadY] = operand(sDO, k + kAheadY);
-          dv[k % DB] = mfma32x32x16(ap[k / DB], b[k], dv[k % DB]);
+          if (k < NH)
+            dk[k % DB] = mfma32x32x16(as[k / DB], b[k], dk[k % DB]);
+          else
+            dv[k % DB] = mfma32x32x16(ap[(k - NH) / DB], b[k], dv[k % DB]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      (void)psc;
       __syncthreads();
     };
     for (int j0 = 0; j0 < nsteps; j0 += kRing) {
@@ -430,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
     }
 
     // accumulators: lane -> d = 32*db + l32, VGPR v -> key kw0 + 8*(v/4) + 4h + v%4
-    const float vsc = UNIT_P ? 1.0f : 1.0f / psc;
+    const float vsc = UNIT_P ? 1.0f : 1.0f / a.p_scale;
     const float ksc = a.softmax_scale;
     uint16_t* DV = a.dv + (size_t)bh * nkv * D;
     uint16_t* DK = a.dk + (size_t)bh * nkv * D;

@@ -9,6 +9,11 @@ REL_FRO_TOL = 5e-3
 ELEM_TOL = 2e-2
 
 
+# Every check_close call appends (name, relative Frobenius error, max abs
+# error, max|ref|) here; tests/conftest.py can write them out as a table.
+MARGINS: list = []
+
+
 def as_np64(x) -> np.ndarray:
     if hasattr(x, "detach"):
         x = x.detach().to("cpu").double().numpy()
@@ -31,6 +36,7 @@ def check_close(got, ref, name: str = "", rel_tol: float = REL_FRO_TOL,
     rf = rel_fro(got, ref)
     amax = float(np.max(np.abs(ref))) if ref.size else 0.0
     emax = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    MARGINS.append((name, rf, emax, amax, rel_tol, elem_tol))
     assert rf <= rel_tol, f"{name}: rel Frobenius error {rf:.3e} > {rel_tol}"
     assert emax <= elem_tol * amax + 1e-30, (
         f"{name}: max abs error {emax:.3e} > {elem_tol} * max|ref| ({amax:.3e})")

@@ -4,8 +4,11 @@
  *
  * The kernels form the quotient without a divide: y0 = amax * (1/6)f, then
  * one FMA correction y = fma(fma(-y0, 6, amax), (1/6)f, y0), and round y to
- * E4M3 (nearest even on the fp32 bit pattern in the normal range, rint(y*512)
- * / 512 below 2^-6, saturating at 448).  For every finite non-negative fp32
+ * E4M3 with the hardware FP8 conversion after clamping at 448 (round to
+ * nearest even, subnormals included; the GPU codec tests pin that conversion
+ * at every E4M3 rounding boundary).  Here that rounding is written out: nearest
+ * even on the fp32 bit pattern in the normal range, rint(y*512) / 512 below
+ * 2^-6, saturating at 448.  For every finite non-negative fp32
  * amax this program compares that result with the exact rounding of the
  * rational amax/6 onto the E4M3 grid (comparisons against 6*g in double,
  * which are exact), and prints the number of mismatches.  It also counts

@@ -3,10 +3,11 @@ from it (attnqat_fwd_packed).
 
 The packed codes and scale bytes are bit-exact to the oracle's E2M1 codes
 and E4M3FN bytes ("NVFP4 Attention QAT Backward", §Overview rounding; the
-nibble order is the one documented in the header).  Dequantization is exact,
-so the packed forward must reproduce attnqat_fwd's O_hp and lse bit for bit
-on the same K and V; attnqat_fwd itself is checked against the oracle
-elsewhere.
+nibble order is the one documented in the header).  The packed forward's
+O_hp and lse are checked against the oracle forward at the stated bar
+(relative Frobenius error 5e-3, elementwise 2e-2 * max|ref|); since its
+dequantization is exact it also agrees with attnqat_fwd to within fp32
+rounding order (a much tighter check of the same kernel pipeline).
 """
 from __future__ import annotations
 
@@ -17,7 +18,9 @@ import pytest
 import torch
 
 from nvfp4_fake_quantized_amd import binding as B
+from oracle.attention import qat_forward_head
 from oracle.nvfp4 import fake_nvfp4
+from tests._util import check_close, rel_fro
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -93,24 +96,37 @@ def _synthetic(n, d, seed, nk=None, heads=2):
     return mk(n), mk(nk), mk(nk)
 
 
+def _check_packed_forward(q, k, v, causal, scale, heads, label):
+    """Packed forward against the oracle forward on the given heads, and
+    against attnqat_fwd to within fp32 rounding order."""
+    o1, l1 = _fwd(q, k, v, causal, scale, packed=False)
+    o2, l2 = _fwd(q, k, v, causal, scale, packed=True)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    for b_, h in heads:
+        o64, l64 = qat_forward_head(qc[b_, h], kc[b_, h], vc[b_, h], scale, causal)
+        check_close(o2[b_, h].cpu(), o64, f"{label} packed O_hp[{b_},{h}]")
+        check_close(l2[b_, h].cpu(), l64, f"{label} packed lse[{b_},{h}]")
+    # one bf16 rounding of O_hp, fp32 rounding order of the softmax sums
+    assert rel_fro(o2, o1) <= 1e-3, (label, rel_fro(o2, o1))
+    assert rel_fro(l2, l1) <= 1e-6, (label, rel_fro(l2, l1))
+
+
 @pytest.mark.parametrize("n,d,causal,nk", [
     (128, 64, False, None), (200, 64, True, None), (333, 128, False, None), (77, 64, True, None),
     (100, 128, False, 260), (300, 64, False, 40), (1, 128, True, None), (17, 64, False, None),
 ])
-def test_packed_forward_equals_forward(n, d, causal, nk):
+def test_packed_forward_matches_oracle(n, d, causal, nk):
     q, k, v = _synthetic(n, d, seed=n + 3 * d, nk=nk)
-    o1, l1 = _fwd(q, k, v, causal, 1.0 / math.sqrt(d), packed=False)
-    o2, l2 = _fwd(q, k, v, causal, 1.0 / math.sqrt(d), packed=True)
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    _check_packed_forward(q, k, v, causal, 1.0 / math.sqrt(d), [(0, 0), (0, 1)],
+                          f"n={n} d={d} causal={causal} nk={nk}")
 
 
-@pytest.mark.parametrize("name", ["ref_shape", "small_causal"])
-def test_packed_forward_on_workloads(name):
+@pytest.mark.parametrize("name,heads", [("ref_shape", [(0, 0), (0, 8), (0, 15)]),
+                                        ("small_causal", [(0, 0), (0, 1), (0, 2), (0, 3)])])
+def test_packed_forward_on_workloads(name, heads):
     w = WORKLOADS[name]
     q, k, v, _ = (t.to(DEV) for t in make_inputs(w))
-    o1, l1 = _fwd(q, k, v, w.causal, w.softmax_scale, packed=False)
-    o2, l2 = _fwd(q, k, v, w.causal, w.softmax_scale, packed=True)
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    _check_packed_forward(q, k, v, w.causal, w.softmax_scale, heads, name)
 
 
 def test_pack_and_packed_forward_reject_bad_arguments():

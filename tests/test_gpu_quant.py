@@ -171,3 +171,33 @@ def test_empty_and_misaligned():
         B.attnqat_fake_nvfp4(bad, x_hat=torch.empty_like(bad),
                              scales=torch.empty(16, 4, dtype=torch.uint8, device=DEV))
     assert e.value.status == B.ERR_MISALIGNED
+
+
+def test_scale_at_every_e4m3_rounding_boundary():
+    """The block scale is the E4M3 rounding (ties to even, saturating at 448)
+    of amax/6.  Groups whose amax is 6 times every E4M3 midpoint, nudged by
+    0..4 fp32 ulps either way, plus every positive bf16 amax up to 6 * 480:
+    the scale bytes and the dequantized values are bit-exact to the oracle
+    (fp32 path, which shares the device scale arithmetic of every kernel)."""
+    g = _e4m3_values()
+    mids = np.concatenate([[2.0 ** -10], (g[:-1] + g[1:]) / 2, [464.0, 470.0, 480.0, 1e4]])
+    amax = []
+    for m in (6.0 * mids).astype(np.float32):
+        up = dn = m
+        amax.append(m)
+        for _ in range(4):
+            up = np.nextafter(up, np.float32(np.inf))
+            dn = np.nextafter(dn, np.float32(0))
+            amax += [up, dn]
+    bf = _all_positive_bf16()
+    amax = np.concatenate([np.array(amax, dtype=np.float64), bf[bf <= 6 * 480.0]])
+    x64 = np.zeros((amax.size, 16))
+    x64[:, 0] = amax
+    x64[:, 1] = amax / 3.0  # a second value rounded with the same scale
+    x64 = x64.astype(np.float32).astype(np.float64)
+    x = torch.from_numpy(x64.astype(np.float32))
+    xh, sc = B.attnqat_fake_nvfp4(x.to(DEV))
+    torch.cuda.synchronize()
+    ref, _, scode, _ = fake_nvfp4(x64)
+    assert np.array_equal(sc.cpu().numpy(), scode)
+    assert np.array_equal(xh.cpu().double().numpy(), ref)
