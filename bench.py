@@ -4,16 +4,20 @@
 One step = one pass of the whole hot path over one batch: attnqat_fwd (Q/K/V
 fake-quant + the QAT forward producing O_hp and lse) followed by
 attnqat_bwd on that output (Q fake-quant + delta, K/V fake-quant, dQ,
-dK/dV).  Inputs are resident in HBM before timing starts; warmup steps
-bring the clocks to their steady state first (the kernels' durations drift
-over the first few dozen steps as the power management settles).
+dK/dV).  Inputs are resident in HBM before timing starts.
+
+Order of the run: a clock-settling phase (plain steps until --settle-s
+seconds have passed: the kernels' durations drift over the first few dozen
+steps while the power management settles), W warmup steps, the K timed
+steps (the headline: HIP events on the benchmark's stream around each
+attnqat_fwd and attnqat_bwd call, wall clock around all K), then, in the same
+steady state, K steps of the instrumented entry points for the per-kernel
+split and the roofline entry, the full forward with the quantized output,
+the forward from packed K/V, the backward after a flush of the 256 MB
+Infinity Cache, and the sustained MFMA rate probe.
 
 The reported metric is the backward's throughput: counted backward work
-10*B*H*N^2*D (halved when causal) divided by the backward's own duration,
-measured with HIP events recorded on the benchmark's stream around each
-attnqat_bwd call.  A separate run of the instrumented entry points
-(attnqat_fwd_timed / attnqat_bwd_timed, which also record events between
-the kernels) gives each kernel's average duration for the roofline entry.
+10*B*H*N^2*D (halved when causal) divided by the median backward duration.
 Prints exactly one JSON line on stdout; human-readable details go to
 stderr.
 """
@@ -34,7 +38,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "QAT-attn bwd TFLOP/s & % bf16 MFMA peak, B1 H16 N4096 D128 non-causal"
-PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak (roofline entry)
+# the metric's denominator: 256 CUs x 4096 bf16 flop/clk x 2.4 GHz
+NOMINAL_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
@@ -237,14 +243,47 @@ def p_scale_study(p_scales=(1.0, 64.0, 512.0, 2688.0), reps=5):
     return out
 
 
+def _stats(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"median": round(med, 4), "min": round(xs[0], 4), "max": round(xs[-1], 4),
+            "mean": round(sum(xs) / n, 4)}
+
+
+def mfma_probe(B, dev, hip, stream, blocks=2048, iters=400, reps=5):
+    """Sustained bf16 MFMA rate on random operands (TFLOP/s, best of reps)."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(123)
+    n = 32 * 256 * blocks
+    a = torch.randn(n, generator=g).to(torch.bfloat16).to(dev)
+    b = torch.randn(n, generator=g).to(torch.bfloat16).to(dev)
+    out = torch.empty(256 * blocks, dtype=torch.float32, device=dev)
+    flops = B.attnqat_probe_mfma_peak(a, b, out, blocks, iters, stream)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e = hip.array(2)
+        hip.record(e[0], stream)
+        B.attnqat_probe_mfma_peak(a, b, out, blocks, iters, stream)
+        hip.record(e[1], stream)
+        torch.cuda.synchronize()
+        best = max(best, flops / (hip.ms(e[0], e[1]) * 1e-3) / 1e12)
+    return best
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup (clock settling)")
     ap.add_argument("--workload", default="ref_shape")
     ap.add_argument("--p-scale", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the quantized/packed forwards, the cache-flush run and the probe")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
     ap.add_argument("--p-scale-study", action="store_true",
@@ -277,87 +316,108 @@ def main():
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     stream = torch.cuda.current_stream()
     hip = HipEvents()
-    K, W = args.steps, args.warmup
-    evf = [hip.array(3) for _ in range(max(K, 1))]
-    evb = [hip.array(5) for _ in range(max(K, 1))]
+    K, W = max(args.steps, 1), max(args.warmup, 0)
 
-    def step(i):
-        B.attnqat_fwd_timed(p, qd, kd, vd, o, lse, wsf, evf[i % len(evf)], stream)
-        B.attnqat_bwd_timed(p, qd, kd, vd, o, dod, lse, dq, dk, dv, wsb, evb[i % len(evb)],
-                            stream)
-
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
-    for i in range(K):
-        step(i)
-    torch.cuda.synchronize()
-
-    # The headline times come from the plain entry points, with events only
-    # around each call (the events between the kernels above serve the
-    # per-kernel split).
-    evp = [hip.array(3) for _ in range(max(K, 1))]
-
-    def plain_step(i):
-        e = evp[i % len(evp)]
-        hip.record(e[0], stream)
+    def plain_step(e=None):
+        if e is not None:
+            hip.record(e[0], stream)
         B.attnqat_fwd(p, qd, kd, vd, o, lse, wsf, stream)
-        hip.record(e[1], stream)
+        if e is not None:
+            hip.record(e[1], stream)
         B.attnqat_bwd(p, qd, kd, vd, o, dod, lse, dq, dk, dv, wsb, stream)
-        hip.record(e[2], stream)
+        if e is not None:
+            hip.record(e[2], stream)
 
-    for i in range(W):
-        plain_step(i)
+    # clock settling, then the warmup steps
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(10):
+            plain_step()
+        settle_steps += 10
+        torch.cuda.synchronize()
+    for _ in range(W):
+        plain_step()
     torch.cuda.synchronize()
+
+    # the K timed steps: events only around each call
+    evp = [hip.array(3) for _ in range(K)]
     t0 = time.perf_counter()
     for i in range(K):
-        plain_step(i)
+        plain_step(evp[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    fwd_list = [hip.ms(e[0], e[1]) for e in evp]
+    bwd_list = [hip.ms(e[1], e[2]) for e in evp]
 
-    # The full QAT forward with the quantized output O = fq(P) V^ (a second
-    # pass over the keys), timed on its own after the step loop.
-    o_q = torch.empty_like(qd)
-    KQ = max(min(K, 10), 1)
-    evq = [hip.array(4) for _ in range(KQ)]
-    for i in range(2):
-        B.attnqat_fwd_quantized_timed(p, qd, kd, vd, o, lse, o_q, wsf, evq[0], stream)
+    # per-kernel split in the same steady state (instrumented entry points)
+    evf = [hip.array(3) for _ in range(K)]
+    evb = [hip.array(5) for _ in range(K)]
+    for i in range(K):
+        B.attnqat_fwd_timed(p, qd, kd, vd, o, lse, wsf, evf[i], stream)
+        B.attnqat_bwd_timed(p, qd, kd, vd, o, dod, lse, dq, dk, dv, wsb, evb[i], stream)
     torch.cuda.synchronize()
-    for i in range(KQ):
-        B.attnqat_fwd_quantized_timed(p, qd, kd, vd, o, lse, o_q, wsf, evq[i], stream)
-    torch.cuda.synchronize()
-    fq_ms = sum(hip.ms(e[0], e[3]) for e in evq) / KQ
-    fq_pass_ms = sum(hip.ms(e[2], e[3]) for e in evq) / KQ
-
-    # The forward reading K^/V^ from packed NVFP4 storage (codes + scale
-    # bytes, packed once beforehand), plain calls with events around each.
-    kc, ks = B.attnqat_nvfp4_pack(kd)
-    vc, vs = B.attnqat_nvfp4_pack(vd)
-    o_p = torch.empty_like(qd)
-    lse_p = torch.empty_like(lse)
-    evk = [hip.array(2) for _ in range(KQ)]
-    for i in range(2):
-        B.attnqat_fwd_packed(p, qd, kc, ks, vc, vs, o_p, lse_p, wsf, stream)
-    for i in range(KQ):
-        hip.record(evk[i][0], stream)
-        B.attnqat_fwd_packed(p, qd, kc, ks, vc, vs, o_p, lse_p, wsf, stream)
-        hip.record(evk[i][1], stream)
-    torch.cuda.synchronize()
-    fp_ms = sum(hip.ms(e[0], e[1]) for e in evk) / KQ
-
     names_f = ["fwd_quant_qkv", "fwd_attention"]
     names_b = ["bwd_quant_q_delta", "bwd_quant_kv", "bwd_dq", "bwd_dkdv"]
-    per = {n: 0.0 for n in names_f + names_b}
-    fwd_ms = bwd_ms = fwd_ms_inst = bwd_ms_inst = 0.0
-    for i in range(K):
-        for j, n in enumerate(names_f):
-            per[n] += hip.ms(evf[i][j], evf[i][j + 1]) / K
-        for j, n in enumerate(names_b):
-            per[n] += hip.ms(evb[i][j], evb[i][j + 1]) / K
-        fwd_ms_inst += hip.ms(evf[i][0], evf[i][2]) / K
-        bwd_ms_inst += hip.ms(evb[i][0], evb[i][4]) / K
-        fwd_ms += hip.ms(evp[i][0], evp[i][1]) / K
-        bwd_ms += hip.ms(evp[i][1], evp[i][2]) / K
+    per_lists = {n: [hip.ms(e[j], e[j + 1]) for e in evf] for j, n in enumerate(names_f)}
+    per_lists.update({n: [hip.ms(e[j], e[j + 1]) for e in evb] for j, n in enumerate(names_b)})
+    per = {n: sum(x) / len(x) for n, x in per_lists.items()}
+    bwd_inst = [hip.ms(e[0], e[4]) for e in evb]
+
+    extras = {}
+    if not args.no_extras:
+        # the full QAT forward with the quantized output O = fq(P) V^ (a
+        # second pass over the keys)
+        o_q = torch.empty_like(qd)
+        KQ = max(min(K, 20), 1)
+        evq = [hip.array(4) for _ in range(KQ)]
+        for i in range(KQ):
+            B.attnqat_fwd_quantized_timed(p, qd, kd, vd, o, lse, o_q, wsf, evq[i], stream)
+        torch.cuda.synchronize()
+        fq_ms = [hip.ms(e[0], e[3]) for e in evq]
+        fq_pass = [hip.ms(e[2], e[3]) for e in evq]
+        extras["fwd_quantized"] = {
+            "ms": _stats(fq_ms), "output_pass_ms": _stats(fq_pass),
+            "output_pass_tflops": round(w.fwd_flops() / (_stats(fq_pass)["median"] * 1e-3) / 1e12,
+                                        2)}
+        # the forward reading K^/V^ from packed NVFP4 storage
+        kc, ks = B.attnqat_nvfp4_pack(kd)
+        vc, vs = B.attnqat_nvfp4_pack(vd)
+        o_p, lse_p = torch.empty_like(qd), torch.empty_like(lse)
+        evk = [hip.array(2) for _ in range(KQ)]
+        for i in range(KQ):
+            hip.record(evk[i][0], stream)
+            B.attnqat_fwd_packed(p, qd, kc, ks, vc, vs, o_p, lse_p, wsf, stream)
+            hip.record(evk[i][1], stream)
+        torch.cuda.synchronize()
+        extras["fwd_packed_kv_ms"] = _stats([hip.ms(e[0], e[1]) for e in evk])
+        # the backward after writing 512 MiB (evicting the 256 MB Infinity
+        # Cache and the L2s) before each call
+        flush = torch.empty(256 << 20, dtype=torch.int16, device=dev)
+        evc = [hip.array(2) for _ in range(KQ)]
+        for i in range(KQ):
+            flush.fill_(i)
+            hip.record(evc[i][0], stream)
+            B.attnqat_bwd(p, qd, kd, vd, o, dod, lse, dq, dk, dv, wsb, stream)
+            hip.record(evc[i][1], stream)
+        torch.cuda.synchronize()
+        extras["bwd_ms_after_cache_flush"] = _stats([hip.ms(e[0], e[1]) for e in evc])
+        del flush
+        extras["mfma_probe_tflops"] = round(mfma_probe(B, dev, hip, stream), 1)
+        # a plain device copy moving as many bytes as the backward's K/V
+        # fake-quant kernel reads and writes (context for the codec rates)
+        nb = 2 * kd.numel()  # bf16 elements of K and V
+        csrc = torch.empty(nb, dtype=torch.bfloat16, device=dev)
+        cdst = torch.empty_like(csrc)
+        evy = [hip.array(2) for _ in range(KQ)]
+        for i in range(KQ):
+            hip.record(evy[i][0], stream)
+            cdst.copy_(csrc)
+            hip.record(evy[i][1], stream)
+        torch.cuda.synchronize()
+        cms = _stats([hip.ms(e[0], e[1]) for e in evy])["median"]
+        extras["device_copy_gbs"] = round(2 * 2 * nb / (cms * 1e-3) / 1e9, 1)
+        del csrc, cdst
     hip.close()
 
     if args.copy_calibration:
@@ -370,6 +430,8 @@ def main():
     BH = w.batch * w.heads
     N, D = w.seqlen, w.head_dim
     half = 0.5 if w.causal else 1.0
+    bwd_s, fwd_s = _stats(bwd_list), _stats(fwd_list)
+    bwd_ms, fwd_ms = bwd_s["median"], fwd_s["median"]
     bwd_tflops = w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
     fwd_tflops = w.fwd_flops() / (fwd_ms * 1e-3) / 1e12
     # algorithmic work of each kernel per launch (GEMM flops or HBM bytes)
@@ -398,18 +460,23 @@ def main():
                 "traffic": read_traffic(kernel_name, w.name, digest),
                 "kernel": kernel_name, "avg_launch_ms": round(per[dominant], 4),
                 "algorithmic_per_launch": amount}
+    # rates of the codec kernels against HBM (algorithmic bytes)
+    codec_gbs = {n: round(work[n][1] / (per[n] * 1e-3) / 1e9, 1)
+                 for n in ("fwd_quant_qkv", "bwd_quant_q_delta", "bwd_quant_kv")}
 
     props = torch.cuda.get_device_properties(dev)
     log(f"[receipt] device={props.name} arch={getattr(props, 'gcnArchName', '?')} "
         f"CUs={props.multi_processor_count} workload={w.name} p_scale={args.p_scale} "
-        f"source={digest}")
+        f"source={digest} settle_steps={settle_steps}")
     for n in names_f + names_b:
         log(f"  {n:20s} {per[n]:8.4f} ms")
-    log(f"  fwd with quantized output {fq_ms:.4f} ms (output pass {fq_pass_ms:.4f} ms)")
-    log(f"  fwd from packed NVFP4 K/V {fp_ms:.4f} ms")
-    log(f"  with events between the kernels: fwd {fwd_ms_inst:.4f} ms, bwd {bwd_ms_inst:.4f} ms")
-    log(f"  fwd {fwd_ms:.4f} ms ({fwd_tflops:.1f} TFLOP/s), bwd {bwd_ms:.4f} ms "
-        f"({bwd_tflops:.1f} TFLOP/s = {100 * bwd_tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+    log(f"  sum of the backward's kernels {sum(per[n] for n in names_b):.4f} ms "
+        f"(instrumented backward {_stats(bwd_inst)['median']:.4f} ms)")
+    for key, val in extras.items():
+        log(f"  {key}: {val}")
+    log(f"  fwd {fwd_ms:.4f} ms ({fwd_tflops:.1f} TFLOP/s), bwd {bwd_ms:.4f} ms median "
+        f"[{bwd_s['min']:.4f}, {bwd_s['max']:.4f}] ({bwd_tflops:.1f} TFLOP/s = "
+        f"{100 * bwd_tflops / NOMINAL_BF16_TFLOPS:.1f}% of {NOMINAL_BF16_TFLOPS:.1f})")
 
     result = {
         "metric": METRIC,
@@ -418,7 +485,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round((t1 - t0) * 1e3 / max(K, 1), 4),
+        "ms_per_step": round((t1 - t0) * 1e3 / K, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -427,18 +494,20 @@ def main():
         "config": {"workload": w.description, "batch": w.batch, "heads": w.heads,
                    "seqlen": N, "head_dim": D, "causal": w.causal,
                    "softmax_scale": w.softmax_scale, "p_scale": args.p_scale},
-        "pct_of_bf16_peak": round(100 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
-        "bwd_ms": round(bwd_ms, 4),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms_with_kernel_events": round(bwd_ms_inst, 4),
+        "pct_of_bf16_peak": round(100 * bwd_tflops / NOMINAL_BF16_TFLOPS, 2),
+        "bf16_peak_tflops": round(NOMINAL_BF16_TFLOPS, 1),
+        "settle_steps": settle_steps,
+        "bwd_ms": bwd_s,
+        "fwd_ms": fwd_s,
         "fwd_tflops": round(fwd_tflops, 2),
         "kernels_ms": {n: round(per[n], 4) for n in names_f + names_b},
+        "bwd_kernels_sum_ms": round(sum(per[n] for n in names_b), 4),
+        "codec_gbs": codec_gbs,
         "roofline": roofline,
-        "fwd_packed_kv_ms": round(fp_ms, 4),
-        "fwd_quantized": {"ms": round(fq_ms, 4), "output_pass_ms": round(fq_pass_ms, 4),
-                          "output_pass_tflops": round(w.fwd_flops() / (fq_pass_ms * 1e-3) / 1e12,
-                                                      2)},
     }
+    result.update(extras)
+    if "mfma_probe_tflops" in extras:
+        result["pct_of_mfma_probe"] = round(100 * bwd_tflops / extras["mfma_probe_tflops"], 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, do)
     print(json.dumps(result), flush=True)

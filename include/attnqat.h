@@ -127,7 +127,9 @@ ATTNQAT_API int attnqat_workspace_layout(const attnqat_problem* p, int which,
  * row_len % 16 == 0, groups of 16 contiguous values along each row.
  * Writes x_hat (same dtype and shape; may alias x) and, when `scales` is
  * not NULL, the E4M3FN byte of every group (rows, row_len/16).  rows == 0
- * is a no-op.  Results are bit-exact to the definition above.
+ * is a no-op.  Results are bit-exact to the definition above.  At most
+ * 2^35 elements (rows * row_len) per call: beyond that,
+ * ATTNQAT_ERR_UNSUPPORTED.  x and x_hat 16-byte aligned.
  * (Page: "NVFP4 Attention QAT Backward", §Overview.) */
 ATTNQAT_API int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_t* scales,
                                    int64_t rows, int64_t row_len, hipStream_t stream);
@@ -140,7 +142,8 @@ ATTNQAT_API int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_
  * (rows, row_len/16); value = code * scale.  4.5 bits per element instead
  * of 16 (Attn-QAT summary, Key claims: the FP4 forward kernel keeps Q and K
  * in block-scaled NVFP4).  x and codes 16-byte aligned; rows == 0 is a
- * no-op; bit-exact to the definition. */
+ * no-op; at most 2^35 elements per call (ATTNQAT_ERR_UNSUPPORTED beyond);
+ * bit-exact to the definition. */
 ATTNQAT_API int attnqat_nvfp4_pack(const void* x, uint8_t* codes, uint8_t* scales,
                                    int64_t rows, int64_t row_len, hipStream_t stream);
 
@@ -157,8 +160,9 @@ ATTNQAT_API int attnqat_fwd(const attnqat_problem* p, const void* q, const void*
 /* attnqat_fwd with K^ and V^ given in packed NVFP4 storage (for instance a
  * cache written by attnqat_nvfp4_pack): k_codes, v_codes (B,H,Nkv,D/2) and
  * k_scales, v_scales (B,H,Nkv,D/16).  The kernel dequantizes them to bf16
- * exactly while staging its tiles, so o_hp and lse are bit-identical to
- * attnqat_fwd's on the K and V the codes were made from.  q is fake-quantized
+ * exactly while staging its tiles, so it computes attnqat_fwd's o_hp and lse
+ * from the same K^/V^ values (equal up to the fp32 rounding order of the
+ * softmax sums) on the K and V the codes were made from.  q is fake-quantized
  * as in attnqat_fwd (the workspace holds Q^ and its scales afterwards; its
  * K^/V^ parts are not written).  q, the code arrays, o_hp, lse and the
  * workspace 16-byte aligned; errors as attnqat_fwd. */
@@ -193,33 +197,6 @@ ATTNQAT_API int attnqat_bwd(const attnqat_problem* p, const void* q, const void*
                             const void* v, const void* o_hp, const void* d_o,
                             const float* lse, void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
-
-/* Instrumented variants for measurement: identical work and results, plus
- * hipEventRecord of caller-created events on `stream` around the kernel
- * launches, so per-kernel durations can be read with hipEventElapsedTime
- * without any synchronization inside the call.
- * attnqat_fwd_timed: events[0] before the Q/K/V fake-quant kernel,
- *   events[1] before the attention kernel, events[2] after it.
- * attnqat_fwd_quantized_timed: as attnqat_fwd_timed, plus events[3] after
- *   the second (quantized-output) pass.
- * attnqat_bwd_timed: events[0] before the Q fake-quant + delta kernel,
- *   events[1] before the K/V fake-quant kernel, events[2] before the dQ
- *   kernel, events[3] before the dK/dV kernel, events[4] after it.
- * A NULL array or NULL event is ATTNQAT_ERR_INVALID_ARGUMENT. */
-ATTNQAT_API int attnqat_fwd_timed(const attnqat_problem* p, const void* q, const void* k,
-                                  const void* v, void* o_hp, float* lse, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream,
-                                  hipEvent_t* events);
-ATTNQAT_API int attnqat_fwd_quantized_timed(const attnqat_problem* p, const void* q,
-                                            const void* k, const void* v, void* o_hp,
-                                            float* lse, void* o, void* workspace,
-                                            size_t workspace_bytes, hipStream_t stream,
-                                            hipEvent_t* events);
-ATTNQAT_API int attnqat_bwd_timed(const attnqat_problem* p, const void* q, const void* k,
-                                  const void* v, const void* o_hp, const void* d_o,
-                                  const float* lse, void* dq, void* dk, void* dv,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                  hipEvent_t* events);
 
 #ifdef __cplusplus
 }

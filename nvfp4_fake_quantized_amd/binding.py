@@ -1,4 +1,5 @@
-"""Thin ctypes binding of libattnqat.so (include/attnqat.h).
+"""Thin ctypes binding of libattnqat.so (include/attnqat.h and the
+measurement entry points of include/attnqat_instrument.h).
 
 Argument marshalling only: every step of the path runs in the HIP library.
 PyTorch supplies device memory (``data_ptr()``) and streams.  The functions
@@ -6,6 +7,10 @@ keep the C names; ``nvfp4_attention_qat_backward`` additionally mirrors the
 high-level wrapper of "NVFP4 Attention QAT Backward" (§High-level wrapper:
 it returns ``dq_tensor``/``dk_tensor``/``dv_tensor``, accepts preallocated
 outputs and an explicit stream).
+
+The C ABI takes plain pointers and cannot check buffer sizes, so every
+function here checks each tensor's dtype, shape, contiguity and device
+against the problem before the call and raises ValueError on a mismatch.
 
 If the library is missing this module raises on import: there is no
 fallback implementation.
@@ -78,6 +83,7 @@ _SIGS = {
                                                    _vp, _vp]),
     "attnqat_bwd_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _sz, _vp, _vp]),
+    "attnqat_probe_mfma_peak": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -114,17 +120,69 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def make_problem(batch, heads, seqlen_q, seqlen_kv, head_dim, causal=False,
-                 softmax_scale=None, p_scale=1.0) -> attnqat_problem:
+# The page's default softmax scale (§Tensor contract: it must match the
+# forward's), used only by the high-level wrappers when none is given.
+PAGE_DEFAULT_SOFTMAX_SCALE = 1.0 / math.sqrt(128.0)
+
+
+def make_problem(batch, heads, seqlen_q, seqlen_kv, head_dim, causal, softmax_scale,
+                 p_scale=1.0) -> attnqat_problem:
+    """The C problem struct; ``softmax_scale`` is required (the library has
+    no default)."""
     if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(head_dim)
+        raise ValueError("softmax_scale is required (it must match the forward's)")
     return attnqat_problem(batch, heads, seqlen_q, seqlen_kv, head_dim, int(bool(causal)),
                            float(softmax_scale), float(p_scale))
 
 
-def problem_for(q, k, causal=False, softmax_scale=None, p_scale=1.0) -> attnqat_problem:
+def problem_for(q, k, causal, softmax_scale, p_scale=1.0) -> attnqat_problem:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be (B, H, S, D) tensors")
     B, H, Nq, D = q.shape
     return make_problem(B, H, Nq, k.shape[2], D, causal, softmax_scale, p_scale)
+
+
+# ---- argument checks (the C ABI takes raw pointers) --------------------------
+
+def _expect(t, name, dtype, shape=None, numel=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _device_of(t):
+    if not t.is_cuda:
+        raise ValueError("tensors must be on a GPU (HIP) device")
+    return t.device
+
+
+def _check_attention(p: attnqat_problem, q, k=None, v=None, o_hp=None, d_o=None, lse=None,
+                     dq=None, dk=None, dv=None, o=None, workspace=None):
+    """Every tensor of an attention call against the problem."""
+    qs = (p.batch, p.heads, p.seqlen_q, p.head_dim)
+    ks = (p.batch, p.heads, p.seqlen_kv, p.head_dim)
+    bf = torch.bfloat16
+    _expect(q, "q", bf, qs)
+    dev = _device_of(q)
+    for t, n, shp in ((k, "k", ks), (v, "v", ks), (o_hp, "o_hp", qs), (d_o, "d_o", qs),
+                      (dq, "dq", qs), (dk, "dk", ks), (dv, "dv", ks), (o, "o", qs)):
+        if t is not None:
+            _expect(t, n, bf, shp, device=dev)
+    if lse is not None:
+        _expect(lse, "lse", torch.float32, qs[:3], device=dev)
+    if workspace is not None:
+        _expect(workspace, "workspace", torch.uint8, device=dev)
 
 
 # ---- C-ABI functions (same names) --------------------------------------------
@@ -175,15 +233,17 @@ def attnqat_fake_nvfp4(x, x_hat=None, scales=None, stream=None):
     if scales is None:
         scales = torch.empty(x.shape[:-1] + (max(L // 16, 0),), dtype=torch.uint8,
                              device=x.device)
-    for t in (x, x_hat, scales):
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _expect(x, "x", x.dtype)
+    _expect(x_hat, "x_hat", x.dtype, numel=x.numel(), device=x.device)
+    _expect(scales, "scales", torch.uint8, numel=rows * (L // 16), device=x.device)
+    _device_of(x)
     _check(_lib.attnqat_fake_nvfp4(_ptr(x), dtype, _ptr(x_hat), _ptr(scales), rows, L,
                                    _stream(stream)), "attnqat_fake_nvfp4")
     return x_hat, scales
 
 
 def attnqat_fwd(p: attnqat_problem, q, k, v, o_hp, lse, workspace, stream=None):
+    _check_attention(p, q, k, v, o_hp=o_hp, lse=lse, workspace=workspace)
     _check(_lib.attnqat_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp), _ptr(lse),
                             _ptr(workspace), workspace.numel(), _stream(stream)), "attnqat_fwd")
 
@@ -199,6 +259,9 @@ def attnqat_nvfp4_pack(x, codes=None, scales=None, stream=None):
         codes = torch.empty(x.shape[:-1] + (L // 2,), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(x.shape[:-1] + (L // 16,), dtype=torch.uint8, device=x.device)
+    _expect(codes, "codes", torch.uint8, numel=rows * (L // 2), device=x.device)
+    _expect(scales, "scales", torch.uint8, numel=rows * (L // 16), device=x.device)
+    _device_of(x)
     _check(_lib.attnqat_nvfp4_pack(_ptr(x), _ptr(codes), _ptr(scales), rows, L,
                                    _stream(stream)), "attnqat_nvfp4_pack")
     return codes, scales
@@ -206,6 +269,12 @@ def attnqat_nvfp4_pack(x, codes=None, scales=None, stream=None):
 
 def attnqat_fwd_packed(p: attnqat_problem, q, k_codes, k_scales, v_codes, v_scales, o_hp, lse,
                        workspace, stream=None):
+    _check_attention(p, q, o_hp=o_hp, lse=lse, workspace=workspace)
+    rows = p.batch * p.heads * p.seqlen_kv
+    for t, n, per in ((k_codes, "k_codes", p.head_dim // 2), (v_codes, "v_codes", p.head_dim // 2),
+                      (k_scales, "k_scales", p.head_dim // 16),
+                      (v_scales, "v_scales", p.head_dim // 16)):
+        _expect(t, n, torch.uint8, numel=rows * per, device=q.device)
     _check(_lib.attnqat_fwd_packed(ctypes.byref(p), _ptr(q), _ptr(k_codes), _ptr(k_scales),
                                    _ptr(v_codes), _ptr(v_scales), _ptr(o_hp), _ptr(lse),
                                    _ptr(workspace), workspace.numel(), _stream(stream)),
@@ -213,19 +282,23 @@ def attnqat_fwd_packed(p: attnqat_problem, q, k_codes, k_scales, v_codes, v_scal
 
 
 def attnqat_fwd_quantized(p: attnqat_problem, q, k, v, o_hp, lse, o, workspace, stream=None):
+    _check_attention(p, q, k, v, o_hp=o_hp, lse=lse, o=o, workspace=workspace)
     _check(_lib.attnqat_fwd_quantized(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),
                                       _ptr(lse), _ptr(o), _ptr(workspace), workspace.numel(),
                                       _stream(stream)), "attnqat_fwd_quantized")
 
 
 def attnqat_bwd(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace, stream=None):
+    _check_attention(p, q, k, v, o_hp=o_hp, d_o=d_o, lse=lse, dq=dq, dk=dk, dv=dv,
+                     workspace=workspace)
     _check(_lib.attnqat_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp), _ptr(d_o),
                             _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                             workspace.numel(), _stream(stream)), "attnqat_bwd")
 
 
 def attnqat_fwd_timed(p: attnqat_problem, q, k, v, o_hp, lse, workspace, events, stream=None):
-    """``events``: a ctypes array of 3 hipEvent_t handles (see the header)."""
+    """``events``: a ctypes array of 3 hipEvent_t handles (attnqat_instrument.h)."""
+    _check_attention(p, q, k, v, o_hp=o_hp, lse=lse, workspace=workspace)
     _check(_lib.attnqat_fwd_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),
                                   _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream),
                                   events), "attnqat_fwd_timed")
@@ -233,7 +306,8 @@ def attnqat_fwd_timed(p: attnqat_problem, q, k, v, o_hp, lse, workspace, events,
 
 def attnqat_fwd_quantized_timed(p: attnqat_problem, q, k, v, o_hp, lse, o, workspace, events,
                                 stream=None):
-    """``events``: a ctypes array of 4 hipEvent_t handles (see the header)."""
+    """``events``: a ctypes array of 4 hipEvent_t handles (attnqat_instrument.h)."""
+    _check_attention(p, q, k, v, o_hp=o_hp, lse=lse, o=o, workspace=workspace)
     _check(_lib.attnqat_fwd_quantized_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(o_hp), _ptr(lse), _ptr(o), _ptr(workspace),
                                             workspace.numel(), _stream(stream), events),
@@ -242,11 +316,28 @@ def attnqat_fwd_quantized_timed(p: attnqat_problem, q, k, v, o_hp, lse, o, works
 
 def attnqat_bwd_timed(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace,
                       events, stream=None):
-    """``events``: a ctypes array of 5 hipEvent_t handles (see the header)."""
+    """``events``: a ctypes array of 5 hipEvent_t handles (attnqat_instrument.h)."""
+    _check_attention(p, q, k, v, o_hp=o_hp, d_o=d_o, lse=lse, dq=dq, dk=dk, dv=dv,
+                     workspace=workspace)
     _check(_lib.attnqat_bwd_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),
                                   _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                   _ptr(workspace), workspace.numel(), _stream(stream), events),
            "attnqat_bwd_timed")
+
+
+def attnqat_probe_mfma_peak(a, b, out, blocks, iters, stream=None):
+    """Sustained bf16 MFMA rate probe (attnqat_instrument.h); the caller times
+    it.  Returns the flops it executes."""
+    need = 32 * 256 * blocks
+    _expect(a, "a", torch.bfloat16)
+    _expect(b, "b", torch.bfloat16, device=a.device)
+    _expect(out, "out", torch.float32, device=a.device)
+    if a.numel() < need or b.numel() < need or out.numel() < 256 * blocks:
+        raise ValueError("probe buffers too small")
+    _device_of(a)
+    _check(_lib.attnqat_probe_mfma_peak(_ptr(a), _ptr(b), _ptr(out), blocks, iters,
+                                        _stream(stream)), "attnqat_probe_mfma_peak")
+    return blocks * 4 * iters * 16 * 32768
 
 
 # ---- conveniences (allocation via torch, then one C call) --------------------
@@ -261,8 +352,12 @@ def nvfp4_attention_qat_forward(q, k, v, is_causal=False, softmax_scale=None, p_
                                 workspace=None, current_stream=None, quantized_output=False):
     """Returns ``(high_precision_o, lse)`` of the QAT forward, or
     ``(o, high_precision_o, lse)`` with ``quantized_output=True``, where ``o``
-    is the quantized user-visible output fake_nvfp4(P) V^."""
+    is the quantized user-visible output fake_nvfp4(P) V^.  Without
+    ``softmax_scale`` the page's default 1/sqrt(128) is used (whatever the
+    head dim), as in its wrapper; the backward must get the same value."""
     _check_bhsd(q, k, v)
+    if softmax_scale is None:
+        softmax_scale = PAGE_DEFAULT_SOFTMAX_SCALE
     p = problem_for(q, k, is_causal, softmax_scale, p_scale)
     o_hp = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
@@ -281,8 +376,12 @@ def nvfp4_attention_qat_backward(do, q, k, v, high_precision_o, lse, is_causal=F
                                  softmax_scale=None, p_scale=1.0, dq_tensor=None,
                                  dk_tensor=None, dv_tensor=None, workspace=None,
                                  current_stream=None):
-    """Returns ``{"dq_tensor", "dk_tensor", "dv_tensor"}``."""
+    """Returns ``{"dq_tensor", "dk_tensor", "dv_tensor"}``.  Without
+    ``softmax_scale`` the page's default 1/sqrt(128) is used, as in its
+    wrapper; it must be the forward's."""
     _check_bhsd(do, q, k, v, high_precision_o)
+    if softmax_scale is None:
+        softmax_scale = PAGE_DEFAULT_SOFTMAX_SCALE
     p = problem_for(q, k, is_causal, softmax_scale, p_scale)
     dq = torch.empty_like(q) if dq_tensor is None else dq_tensor
     dk = torch.empty_like(k) if dk_tensor is None else dk_tensor

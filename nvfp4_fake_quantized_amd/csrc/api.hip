@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "attnqat.h"
+#include "attnqat_instrument.h"
 #include "kernels.hpp"
 
 namespace {
@@ -15,6 +16,9 @@ using attnqat::AttnArgs;
 using attnqat::QuantJob;
 
 constexpr size_t kAlign = 256;
+// Codec calls: at most 2^35 elements, so that every codec launch stays below
+// 2^32 threads (one thread per 16 values for the fp32 and packing kernels).
+constexpr int64_t kMaxCodecElements = (int64_t)1 << 35;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -147,7 +151,7 @@ int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_t* scales, i
                        int64_t row_len, hipStream_t stream) {
   if (dtype != ATTNQAT_DTYPE_BF16 && dtype != ATTNQAT_DTYPE_F32) return ATTNQAT_ERR_INVALID_ARGUMENT;
   if (rows < 0 || row_len <= 0 || (row_len % 16) != 0) return ATTNQAT_ERR_INVALID_ARGUMENT;
-  if (rows > ((int64_t)1 << 40) / row_len) return ATTNQAT_ERR_UNSUPPORTED;
+  if (rows > kMaxCodecElements / row_len) return ATTNQAT_ERR_UNSUPPORTED;
   if (rows == 0) return ATTNQAT_OK;
   if (x == nullptr || x_hat == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(x_hat)) return ATTNQAT_ERR_MISALIGNED;
@@ -163,7 +167,7 @@ int attnqat_fake_nvfp4(const void* x, int dtype, void* x_hat, uint8_t* scales, i
 int attnqat_nvfp4_pack(const void* x, uint8_t* codes, uint8_t* scales, int64_t rows,
                        int64_t row_len, hipStream_t stream) {
   if (rows < 0 || row_len <= 0 || (row_len % 16) != 0) return ATTNQAT_ERR_INVALID_ARGUMENT;
-  if (rows > ((int64_t)1 << 40) / row_len) return ATTNQAT_ERR_UNSUPPORTED;
+  if (rows > kMaxCodecElements / row_len) return ATTNQAT_ERR_UNSUPPORTED;
   if (rows == 0) return ATTNQAT_OK;
   if (x == nullptr || codes == nullptr || scales == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(codes)) return ATTNQAT_ERR_MISALIGNED;
@@ -404,3 +408,19 @@ int attnqat_bwd_timed(const attnqat_problem* p, const void* q, const void* k, co
 }
 
 }  // extern "C"
+
+extern "C" int attnqat_probe_mfma_peak(const void* a, const void* b, float* out, int blocks,
+                                       int iters, hipStream_t stream) {
+  if (a == nullptr || b == nullptr || out == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out)) return ATTNQAT_ERR_MISALIGNED;
+  const int st = device_status();
+  if (st != ATTNQAT_OK) return st;
+  (void)hipGetLastError();
+  return attnqat::launch_mfma_peak(static_cast<const uint16_t*>(a),
+                                   static_cast<const uint16_t*>(b), out, blocks, iters,
+                                   stream) == hipSuccess
+             ? ATTNQAT_OK
+             : ATTNQAT_ERR_HIP;
+}

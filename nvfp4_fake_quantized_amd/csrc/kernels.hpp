@@ -59,5 +59,9 @@ hipError_t launch_fwd_packed(const AttnArgs& a, int head_dim, hipStream_t stream
 hipError_t launch_fwd_out(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream);
+// Sustained bf16 MFMA rate probe: blocks of 256 threads, each thread reading
+// 32 bf16 of a and of b at offset 32 * thread.
+hipError_t launch_mfma_peak(const uint16_t* a, const uint16_t* b, float* out, int blocks,
+                            int iters, hipStream_t stream);
 
 }  // namespace attnqat

@@ -1,6 +1,6 @@
 """Host-side tests of the C ABI (no GPU needed, no kernel launched).
 
-The library must load, export every function include/attnqat.h declares,
+The library must load, export every function include/*.h declares,
 and reject invalid arguments on the host, before any HIP call, with the
 documented status codes.  Pointers handed to the library here are never
 dereferenced: every call below returns during validation.
@@ -8,6 +8,7 @@ dereferenced: every call below returns during validation.
 from __future__ import annotations
 
 import ctypes
+import glob
 import math
 import os
 import re
@@ -17,12 +18,15 @@ import pytest
 from nvfp4_fake_quantized_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attnqat.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    return re.findall(r"ATTNQAT_API\s+[\w\s\*]+?\b(attnqat_\w+)\s*\(", text)
+    names = []
+    for path in HEADERS:
+        text = open(path).read()
+        names += re.findall(r"ATTNQAT_API\s+[\w\s\*]+?\b(attnqat_\w+)\s*\(", text)
+    return names
 
 
 def test_header_declares_expected_functions():
@@ -158,3 +162,86 @@ def test_fake_nvfp4_rejects_bad_arguments_before_launch():
         B.ERR_MISALIGNED
     # empty input: nothing to do, nothing launched
     assert lib.attnqat_fake_nvfp4(None, B.DTYPE_F32, None, None, 0, 16, None) == B.OK
+
+
+def test_codec_size_limit():
+    """At most 2^35 elements per codec call; beyond: unsupported, decided on
+    the host before any pointer is used."""
+    lib = B._lib
+    big_rows = (1 << 35) // 128 + 1
+    assert lib.attnqat_fake_nvfp4(None, B.DTYPE_BF16, None, None, big_rows, 128, None) == \
+        B.ERR_UNSUPPORTED
+    assert lib.attnqat_fake_nvfp4(None, B.DTYPE_F32, None, None, big_rows, 128, None) == \
+        B.ERR_UNSUPPORTED
+    assert lib.attnqat_nvfp4_pack(None, None, None, big_rows, 128, None) == B.ERR_UNSUPPORTED
+    # at the limit: validation proceeds to the (NULL) pointers
+    assert lib.attnqat_fake_nvfp4(None, B.DTYPE_BF16, None, None, (1 << 35) // 128, 128,
+                                  None) == B.ERR_INVALID_ARGUMENT
+
+
+def test_problem_requires_softmax_scale():
+    with pytest.raises(ValueError):
+        B.make_problem(1, 1, 16, 16, 64, False, None)
+    assert abs(B.PAGE_DEFAULT_SOFTMAX_SCALE - 1 / math.sqrt(128)) < 1e-12
+
+
+def _cpu_case(nq=32, nk=48, d=64, heads=2):
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(1, heads, nq, d, dtype=bf)
+    k = torch.zeros(1, heads, nk, d, dtype=bf)
+    p = B.problem_for(q, k, False, 0.125)
+    return p, q, k
+
+
+@pytest.mark.parametrize("bad", ["k_heads", "v_shape", "lse_dtype", "lse_shape", "dq_dtype",
+                                 "dk_shape", "o_hp_shape", "do_noncontig", "ws_dtype"])
+def test_binding_rejects_mismatched_tensors(bad):
+    """Tensors that do not match the problem raise ValueError in the binding
+    (the C ABI cannot see buffer sizes); nothing reaches the library."""
+    import torch
+    p, q, k = _cpu_case()
+    bf = torch.bfloat16
+    v = torch.zeros_like(k)
+    o = torch.zeros_like(q)
+    do = torch.zeros_like(q)
+    lse = torch.zeros(q.shape[:3])
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    ws = torch.zeros(64, dtype=torch.uint8)
+    if bad == "k_heads":
+        k = torch.zeros(1, 1, 48, 64, dtype=bf)
+    elif bad == "v_shape":
+        v = torch.zeros(1, 2, 47, 64, dtype=bf)
+    elif bad == "lse_dtype":
+        lse = lse.to(bf)
+    elif bad == "lse_shape":
+        lse = torch.zeros(1, 2, 31)
+    elif bad == "dq_dtype":
+        dq = dq.float()
+    elif bad == "dk_shape":
+        dk = torch.zeros(1, 2, 32, 64, dtype=bf)
+    elif bad == "o_hp_shape":
+        o = torch.zeros(1, 2, 48, 64, dtype=bf)
+    elif bad == "do_noncontig":
+        do = torch.zeros(1, 2, 64, 32, dtype=bf).transpose(2, 3)
+    elif bad == "ws_dtype":
+        ws = torch.zeros(16, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        B.attnqat_bwd(p, q, k, v, o, do, lse, dq, dk, dv, ws)
+
+
+def test_binding_rejects_host_tensors_and_bad_codec_outputs():
+    import torch
+    p, q, k = _cpu_case()
+    v = torch.zeros_like(k)
+    # right shapes on the host: the binding asks for device tensors
+    with pytest.raises(ValueError):
+        B.attnqat_fwd(p, q, k, v, torch.zeros_like(q), torch.zeros(q.shape[:3]),
+                      torch.zeros(64, dtype=torch.uint8))
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # x_hat of the wrong dtype
+        B.attnqat_fake_nvfp4(x, x_hat=torch.zeros(4, 32))
+    with pytest.raises(ValueError):  # too few scale bytes
+        B.attnqat_fake_nvfp4(x, scales=torch.zeros(4, 1, dtype=torch.uint8))
+    with pytest.raises(ValueError):  # too few code bytes
+        B.attnqat_nvfp4_pack(x, codes=torch.zeros(4, 8, dtype=torch.uint8))

@@ -43,3 +43,10 @@ def test_committed_profiles_name_their_digest():
             text = open(os.path.join(ROOT, "profiles", name)).read()
             assert "- source_digest: `" in text, name
             assert "- hbm_bytes_per_launch:" in text, name
+
+
+def test_stats_reports_median_min_max():
+    s = bench._stats([3.0, 1.0, 2.0, 10.0])
+    assert s == {"median": 2.5, "min": 1.0, "max": 10.0, "mean": 4.0}
+    assert bench._stats([5.0])["median"] == 5.0
+    assert abs(bench.NOMINAL_BF16_TFLOPS - 2516.58) < 0.01
