@@ -198,6 +198,23 @@ ATTNQAT_API int attnqat_bwd(const attnqat_problem* p, const void* q, const void*
                             const float* lse, void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* attnqat_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results as attnqat_bwd, with the workspace taken from
+ * a static device array of ATTNQAT_NOALLOC_MAX_WORKSPACE_BYTES that the
+ * library holds on every GPU it runs on until the process ends (its address
+ * is looked up once per device, on the first call there).  The call itself
+ * allocates nothing.  Problems whose attnqat_bwd_workspace_bytes exceed that
+ * size return ATTNQAT_ERR_UNSUPPORTED.  All calls on one GPU share its array:
+ * calls that overlap on one GPU (different streams or threads) race and must
+ * be serialized by the caller; the array keeps the last call's contents,
+ * which no call depends on.  Other arguments and errors as attnqat_bwd. */
+#define ATTNQAT_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)64 << 20)
+ATTNQAT_API int attnqat_bwd_noalloc(const attnqat_problem* p, const void* q, const void* k,
+                                    const void* v, const void* o_hp, const void* d_o,
+                                    const float* lse, void* dq, void* dk, void* dv,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

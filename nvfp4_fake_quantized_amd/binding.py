@@ -84,6 +84,7 @@ _SIGS = {
     "attnqat_bwd_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _sz, _vp, _vp]),
     "attnqat_probe_mfma_peak": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp]),
+    "attnqat_bwd_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -294,6 +295,17 @@ def attnqat_bwd(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspa
     _check(_lib.attnqat_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp), _ptr(d_o),
                             _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                             workspace.numel(), _stream(stream)), "attnqat_bwd")
+
+
+NOALLOC_MAX_WORKSPACE_BYTES = 64 << 20
+
+
+def attnqat_bwd_noalloc(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, stream=None):
+    """attnqat_bwd with the library's static device workspace (no allocation)."""
+    _check_attention(p, q, k, v, o_hp=o_hp, d_o=d_o, lse=lse, dq=dq, dk=dk, dv=dv)
+    _check(_lib.attnqat_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),
+                                    _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _stream(stream)), "attnqat_bwd_noalloc")
 
 
 def attnqat_fwd_timed(p: attnqat_problem, q, k, v, o_hp, lse, workspace, events, stream=None):

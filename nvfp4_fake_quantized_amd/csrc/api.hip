@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "attnqat.h"
 #include "attnqat_instrument.h"
 #include "kernels.hpp"
@@ -423,4 +425,49 @@ extern "C" int attnqat_probe_mfma_peak(const void* a, const void* b, float* out,
                                    stream) == hipSuccess
              ? ATTNQAT_OK
              : ATTNQAT_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Backward without a workspace argument, for callers that cannot allocate.
+//
+// The workspace lives in a file-scope device array of kScratchBytes (each
+// GPU the library runs on holds its own copy until the process ends).  In
+// host code `scratch` only names the symbol: its device address on the
+// current GPU comes from hipGetSymbolAddress, taken once per device on the
+// first call there and kept in g_scratch.  Every call on a GPU shares that
+// GPU's array, so calls that overlap on one GPU race; nothing in the array
+// needs to start at zero (the backward writes every workspace byte it reads).
+namespace {
+
+constexpr size_t kScratchBytes = ATTNQAT_NOALLOC_MAX_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch[256];
+
+// The scratch array's address on the current device, or nullptr on error.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return nullptr;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+    return nullptr;
+  g_scratch[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" int attnqat_bwd_noalloc(const attnqat_problem* p, const void* q, const void* k,
+                                   const void* v, const void* o_hp, const void* d_o,
+                                   const float* lse, void* dq, void* dk, void* dv,
+                                   hipStream_t stream) {
+  const int st = validate_problem(p);
+  if (st != ATTNQAT_OK) return st;
+  if (make_layout(p, true).total > kScratchBytes) return ATTNQAT_ERR_UNSUPPORTED;
+  const int dst = device_status();
+  if (dst != ATTNQAT_OK) return dst;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return ATTNQAT_ERR_HIP;
+  return run_bwd(p, q, k, v, o_hp, d_o, lse, dq, dk, dv, ws, kScratchBytes, stream, nullptr);
 }

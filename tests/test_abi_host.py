@@ -245,3 +245,15 @@ def test_binding_rejects_host_tensors_and_bad_codec_outputs():
         B.attnqat_fake_nvfp4(x, scales=torch.zeros(4, 1, dtype=torch.uint8))
     with pytest.raises(ValueError):  # too few code bytes
         B.attnqat_nvfp4_pack(x, codes=torch.zeros(4, 8, dtype=torch.uint8))
+
+
+def test_noalloc_rejects_large_workspaces_on_the_host():
+    """attnqat_bwd_noalloc refuses a problem whose workspace exceeds its
+    static array before any pointer is used."""
+    p = _prob(batch=2, heads=40, seqlen_q=8192, seqlen_kv=8192, causal=True)
+    assert B.attnqat_bwd_workspace_bytes(p) > B.NOALLOC_MAX_WORKSPACE_BYTES
+    rc = B._lib.attnqat_bwd_noalloc(ctypes.byref(p), None, None, None, None, None, None, None,
+                                    None, None, None)
+    assert rc == B.ERR_UNSUPPORTED
+    assert B._lib.attnqat_bwd_noalloc(ctypes.byref(_prob(head_dim=96)), None, None, None, None,
+                                      None, None, None, None, None, None) == B.ERR_UNSUPPORTED
