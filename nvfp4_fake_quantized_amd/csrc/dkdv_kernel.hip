@@ -71,6 +71,19 @@ constexpr int kRing = 4;       // Q^/dO sub-tile slots (also the unroll factor)
 constexpr int kAhead = ATTNQAT_DKDV_AHEAD;     // X: MFMA operand reads issued this many MFMAs ahead
 constexpr int kAheadY = ATTNQAT_DKDV_AHEAD_Y;  // Y: the same
 
+// Element offset of (row r, column c) in a [query][key] handover tile (32 x 32
+// bf16, 64-byte rows): 16-byte chunk c / 8 of row r sits at chunk position
+// (c / 8) ^ ((r >> 1) & 3).  gfx950's LDS takes writes at 128 bytes per clock
+// (32 banks of 4 bytes: 8 lanes of a 16-byte write) and reads at 256 (64
+// banks); a probe of SQ_LDS_BANK_CONFLICT over write patterns fits that model
+// exactly.  X writes row l32 in 16-byte pieces, 8 lanes (rows) per clock:
+// rows of one parity share a 64-byte half of the 128-byte bank window and
+// the swizzle gives each of the 4 a different chunk.  Y's transpose reads
+// (lanes 0-31: 4 whole consecutive rows) cover 256 bytes once for any
+// permutation within a row.  Both patterns are conflict-free.
+__device__ __forceinline__ int hoff(int r, int c) {
+  return r * 32 + 8 * ((c >> 3) ^ ((r >> 1) & 3)) + (c & 7);
+}
 
 template <int N>
 struct IntTag {
@@ -152,7 +165,13 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
   uint8_t* const pair = smem + L::PAIR;
   uint16_t* const dstile = reinterpret_cast<uint16_t*>(pair + L::DS + kk * 2 * 2048);
   uint16_t* const pftile = reinterpret_cast<uint16_t*>(pair + L::PF + kk * 2 * 2048);
-  const int pw0 = swz<32>(l32, 16 * h), pw1 = swz<32>(l32, 16 * h + 8);  // tile row writes
+  // tile row writes: row l32, columns 16h .. 16h + 15
+  const int hw0 = hoff(l32, 16 * h), hw1 = hoff(l32, 16 * h + 8);
+  auto write_tile_row = [&](uint16_t* tile, const u32x4& lo, const u32x4& hi)
+      __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4*>(tile + hw0) = lo;
+    *reinterpret_cast<u32x4*>(tile + hw1) = hi;
+  };
 
   if (is_x) {
     // K^ and V^ rows of the pair's keys, in the order pi (A operands)
@@ -297,17 +316,13 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
             pfw[hh][e] = pack_exact_bf16x2(y0, y1);
           }
           if (hh == 1) {
-            uint16_t* pt = pftile + (R & 1) * 1024;
-            *reinterpret_cast<u32x4*>(pt + pw0) = pfw[0];
-            *reinterpret_cast<u32x4*>(pt + pw1) = pfw[1];
+            write_tile_row(pftile + (R & 1) * 1024, pfw[0], pfw[1]);
           }
         } else {
           u32x4 dsb[2];
 #pragma unroll
           for (int e = 0; e < 8; ++e) dsb[e >> 2][e & 3] = pack_bf16x2(ds[2 * e], ds[2 * e + 1]);
-          uint16_t* dt = dstile + (R & 1) * 1024;
-          *reinterpret_cast<u32x4*>(dt + pw0) = dsb[0];
-          *reinterpret_cast<u32x4*>(dt + pw1) = dsb[1];
+          write_tile_row(dstile + (R & 1) * 1024, dsb[0], dsb[1]);
         }
       };
       constexpr int NSLOT = NM > 16 ? NM : 16;
@@ -398,7 +413,19 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
     // ---- Y, step j: dK += dS^T Q^(j-1), dV += P^F^T dO(j-1), with dS and
     // P^F from X's tiles of the previous step: MFMAs and LDS reads only
     const ColOffsets<D> co(8 * h, 8 * h + 4, lane);   // column reads (dV, dK B operands)
-    const ColOffsets<32> cp(8 * h, 8 * h + 4, lane);  // key-column reads of P^F / dS tiles
+    // key-column (transpose) reads of the P^F / dS tiles: lane l gets key
+    // column 16*(l/16 % 2) + 4*(l%4) .. of query rows 16kb + 8h + (l%16)/4
+    // (elements 0..3) and 16kb + 8h + 4 + (l%16)/4 (elements 4..7)
+    int tro[2][2];
+    {
+      const int j = lane & 15;
+      const int col = ((lane >> 4) & 1) * 16 + 4 * (j & 3);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        tro[kb][0] = hoff(16 * kb + 8 * h + (j >> 2), col);
+        tro[kb][1] = hoff(16 * kb + 8 * h + 4 + (j >> 2), col);
+      }
+    }
     f32x16 dv[DB], dk[DB];  // lane -> d, VGPR -> key
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -424,8 +451,8 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
           const int kk2 = k % NH;
           return lds_operand_cols_at(tile + 16 * (kk2 / DB) * D, co.a[kk2 % DB], co.b[kk2 % DB]);
         };
-        const bf16x8 as[2] = {lds_operand_cols_at(dt, cp.a[0], cp.b[0]),
-                              lds_operand_cols_at(dt + 16 * 32, cp.a[0], cp.b[0])};
+        const bf16x8 as[2] = {lds_operand_cols_at(dt, tro[0][0], tro[0][1]),
+                              lds_operand_cols_at(dt, tro[1][0], tro[1][1])};
         bf16x8 b[2 * NH];
 #pragma unroll
         for (int k = 0; k < kAheadY; ++k) b[k] = operand(k);
@@ -434,8 +461,8 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
         for (int k = 0; k < 2 * NH; ++k) {
           if (k + kAheadY < 2 * NH) b[k + kAheadY] = operand(k + kAheadY);
           if (k == NH - kAheadY || (NH <= kAheadY && k == 0)) {
-            ap[0] = lds_operand_cols_at(pt, cp.a[0], cp.b[0]);
-            ap[1] = lds_operand_cols_at(pt + 16 * 32, cp.a[0], cp.b[0]);
+            ap[0] = lds_operand_cols_at(pt, tro[0][0], tro[0][1]);
+            ap[1] = lds_operand_cols_at(pt, tro[1][0], tro[1][1]);
           }
           if (k < NH)
             dk[k % DB] = mfma32x32x16(as[k / DB], b[k], dk[k % DB]);
