@@ -215,11 +215,11 @@ def p_scale_study(p_scales=(1.0, 64.0, 512.0, 2688.0), reps=5):
             p = B.problem_for(q, k, w.causal, w.softmax_scale, ps)
             wsb = torch.empty(B.attnqat_bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
             dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-            evs = [hip.array(5) for _ in range(reps)]
+            evs = [hip.array(6) for _ in range(reps)]
             for i in range(2 + reps):
                 B.attnqat_bwd_timed(p, q, k, v, o, do, lse, dq, dk, dv, wsb, evs[max(i - 2, 0)])
             torch.cuda.synchronize()
-            bwd_ms = sum(hip.ms(e[0], e[4]) for e in evs) / reps
+            bwd_ms = sum(hip.ms(e[0], e[5]) for e in evs) / reps
             num = den_a = den_b = 0.0
             zero = total = 0
             for b, h in heads:
@@ -350,19 +350,22 @@ def main():
     fwd_list = [hip.ms(e[0], e[1]) for e in evp]
     bwd_list = [hip.ms(e[1], e[2]) for e in evp]
 
-    # per-kernel split in the same steady state (instrumented entry points)
-    evf = [hip.array(3) for _ in range(K)]
-    evb = [hip.array(5) for _ in range(K)]
+    # per-kernel split in the same steady state: the instrumented entry points
+    # have each launch's dispatch record its own start/stop events (kernel i:
+    # events 2i, 2i+1), so the split adds nothing between the kernels
+    evf = [hip.array(4) for _ in range(K)]
+    evb = [hip.array(6) for _ in range(K)]
     for i in range(K):
         B.attnqat_fwd_timed(p, qd, kd, vd, o, lse, wsf, evf[i], stream)
         B.attnqat_bwd_timed(p, qd, kd, vd, o, dod, lse, dq, dk, dv, wsb, evb[i], stream)
     torch.cuda.synchronize()
     names_f = ["fwd_quant_qkv", "fwd_attention"]
-    names_b = ["bwd_quant_q_delta", "bwd_quant_kv", "bwd_dq", "bwd_dkdv"]
-    per_lists = {n: [hip.ms(e[j], e[j + 1]) for e in evf] for j, n in enumerate(names_f)}
-    per_lists.update({n: [hip.ms(e[j], e[j + 1]) for e in evb] for j, n in enumerate(names_b)})
-    per = {n: sum(x) / len(x) for n, x in per_lists.items()}
-    bwd_inst = [hip.ms(e[0], e[4]) for e in evb]
+    names_b = ["bwd_codec", "bwd_dq", "bwd_dkdv"]
+    per_lists = {n: [hip.ms(e[2 * j], e[2 * j + 1]) for e in evf] for j, n in enumerate(names_f)}
+    per_lists.update({n: [hip.ms(e[2 * j], e[2 * j + 1]) for e in evb]
+                      for j, n in enumerate(names_b)})
+    per = {n: _stats(x)["median"] for n, x in per_lists.items()}
+    bwd_inst = [hip.ms(e[0], e[5]) for e in evb]
 
     extras = {}
     if not args.no_extras:
@@ -370,12 +373,12 @@ def main():
         # second pass over the keys)
         o_q = torch.empty_like(qd)
         KQ = max(min(K, 20), 1)
-        evq = [hip.array(4) for _ in range(KQ)]
+        evq = [hip.array(6) for _ in range(KQ)]
         for i in range(KQ):
             B.attnqat_fwd_quantized_timed(p, qd, kd, vd, o, lse, o_q, wsf, evq[i], stream)
         torch.cuda.synchronize()
-        fq_ms = [hip.ms(e[0], e[3]) for e in evq]
-        fq_pass = [hip.ms(e[2], e[3]) for e in evq]
+        fq_ms = [hip.ms(e[0], e[5]) for e in evq]
+        fq_pass = [hip.ms(e[4], e[5]) for e in evq]
         extras["fwd_quantized"] = {
             "ms": _stats(fq_ms), "output_pass_ms": _stats(fq_pass),
             "output_pass_tflops": round(w.fwd_flops() / (_stats(fq_pass)["median"] * 1e-3) / 1e12,
@@ -441,14 +444,13 @@ def main():
         "bwd_dq": ("mfma", 6.0 * BH * N * N * D * half),
         "bwd_dkdv": ("mfma", 8.0 * BH * N * N * D * half),
         "fwd_quant_qkv": ("hbm", 3 * elems * (4 + 1 / 16)),
-        "bwd_quant_q_delta": ("hbm", elems * (8 + 1 / 16) + BH * N * 4),
-        "bwd_quant_kv": ("hbm", 2 * elems * (4 + 1 / 16)),
+        # Q + delta (reads Q, O_hp, dO; writes Q^, scales, delta) and K, V
+        "bwd_codec": ("hbm", elems * (8 + 1 / 16) + BH * N * 4 + 2 * elems * (4 + 1 / 16)),
     }
     dominant = max(per, key=per.get)
     bound, amount = work[dominant]
     kernel_name = {"fwd_attention": "k_fwd", "bwd_dq": "k_dq", "bwd_dkdv": "k_dkdv",
-                   "fwd_quant_qkv": "k_quant_bf16", "bwd_quant_q_delta": "k_quant_q_delta",
-                   "bwd_quant_kv": "k_quant_bf16"}[dominant]
+                   "fwd_quant_qkv": "k_quant_bf16", "bwd_codec": "k_bwd_codec"}[dominant]
     secs = per[dominant] * 1e-3
     if bound == "mfma":
         achieved, peak, unit = amount / secs / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
@@ -462,7 +464,7 @@ def main():
                 "algorithmic_per_launch": amount}
     # rates of the codec kernels against HBM (algorithmic bytes)
     codec_gbs = {n: round(work[n][1] / (per[n] * 1e-3) / 1e9, 1)
-                 for n in ("fwd_quant_qkv", "bwd_quant_q_delta", "bwd_quant_kv")}
+                 for n in ("fwd_quant_qkv", "bwd_codec")}
 
     props = torch.cuda.get_device_properties(dev)
     log(f"[receipt] device={props.name} arch={getattr(props, 'gcnArchName', '?')} "

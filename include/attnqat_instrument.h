@@ -3,9 +3,9 @@
  *
  * These are not part of the operation's interface (attnqat.h): they run the
  * same kernels as attnqat_fwd, attnqat_fwd_quantized and attnqat_bwd and
- * additionally record caller-created HIP events between the launches, for
- * benchmarks that time each kernel of the four-kernel backward ("NVFP4
- * Attention QAT Backward", §Overview) without synchronizing inside the call.
+ * additionally have each launch record caller-created HIP events, for
+ * benchmarks that time each kernel of the backward ("NVFP4 Attention QAT
+ * Backward", §Overview) without synchronizing inside the call.
  * Conventions, arguments and errors as in attnqat.h.
  */
 #ifndef ATTNQAT_INSTRUMENT_H_
@@ -17,17 +17,18 @@
 extern "C" {
 #endif
 
-/* Instrumented variants for measurement: identical work and results, plus
- * hipEventRecord of caller-created events on `stream` around the kernel
- * launches, so per-kernel durations can be read with hipEventElapsedTime
- * without any synchronization inside the call.
- * attnqat_fwd_timed: events[0] before the Q/K/V fake-quant kernel,
- *   events[1] before the attention kernel, events[2] after it.
- * attnqat_fwd_quantized_timed: as attnqat_fwd_timed, plus events[3] after
+/* Instrumented variants for measurement: identical work and results, and
+ * each kernel launch has its dispatch record a caller-created start and stop
+ * event (hipExtLaunchKernel), so per-kernel durations can be read with
+ * hipEventElapsedTime(events[2i], events[2i+1]) without synchronizing inside
+ * the call and without extra packets or gaps between the kernels.
+ * attnqat_fwd_timed: 4 events; kernel 0 the Q/K/V fake-quant, kernel 1 the
+ *   attention forward.
+ * attnqat_fwd_quantized_timed: 6 events; kernels 0 and 1 as above, kernel 2
  *   the second (quantized-output) pass.
- * attnqat_bwd_timed: events[0] before the Q fake-quant + delta kernel,
- *   events[1] before the K/V fake-quant kernel, events[2] before the dQ
- *   kernel, events[3] before the dK/dV kernel, events[4] after it.
+ * attnqat_bwd_timed: 6 events; kernel 0 the preprocessing (Q fake-quant fused
+ *   with delta, and K/V fake-quant, in one launch), kernel 1 dQ, kernel 2
+ *   dK/dV.
  * A NULL array or NULL event is ATTNQAT_ERR_INVALID_ARGUMENT. */
 ATTNQAT_API int attnqat_fwd_timed(const attnqat_problem* p, const void* q, const void* k,
                                   const void* v, void* o_hp, float* lse, void* workspace,

@@ -185,15 +185,16 @@ int attnqat_nvfp4_pack(const void* x, uint8_t* codes, uint8_t* scales, int64_t r
 
 namespace {
 
-// Records ev[i] on the stream when an event array is given.
-bool record(hipEvent_t* ev, int i, hipStream_t stream) {
-  return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess;
+// Start/stop events of the i-th launch of a call when an event array (two
+// events per launch) is given, else none.
+const attnqat::LaunchEvents* timing(const attnqat::LaunchEvents* ev, int i) {
+  return ev == nullptr ? nullptr : ev + i;
 }
 
 // with_o: also the quantized output o (second pass)
 int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v, void* o_hp,
             float* lse, bool with_o, void* o, void* workspace, size_t workspace_bytes,
-            hipStream_t stream, hipEvent_t* ev) {
+            hipStream_t stream, const attnqat::LaunchEvents* ev) {
   int st = validate_problem(p);
   if (st != ATTNQAT_OK) return st;
   const void* ptrs[] = {q, k, v, o_hp, lse, workspace, with_o ? o : o_hp};
@@ -217,9 +218,8 @@ int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* 
       {k, kh, at<uint8_t>(workspace, L.k_scale), bh * p->seqlen_kv * D / 16},
       {v, vh, at<uint8_t>(workspace, L.v_scale), bh * p->seqlen_kv * D / 16},
   };
-  if (!record(ev, 0, stream)) return ATTNQAT_ERR_HIP;
-  if (attnqat::launch_quant_bf16(jobs, 3, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
-  if (!record(ev, 1, stream)) return ATTNQAT_ERR_HIP;
+  if (attnqat::launch_quant_bf16(jobs, 3, stream, timing(ev, 0)) != hipSuccess)
+    return ATTNQAT_ERR_HIP;
 
   AttnArgs a = {};
   a.q_hat = qh;
@@ -233,13 +233,13 @@ int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   a.causal = p->causal;
   a.softmax_scale = p->softmax_scale;
   a.p_scale = p->p_scale;
-  if (attnqat::launch_fwd(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
-  if (!record(ev, 2, stream)) return ATTNQAT_ERR_HIP;
+  if (attnqat::launch_fwd(a, p->head_dim, stream, timing(ev, 1)) != hipSuccess)
+    return ATTNQAT_ERR_HIP;
   if (with_o) {
     a.lse = lse;  // the first pass's output
     a.o_q = static_cast<uint16_t*>(o);
-    if (attnqat::launch_fwd_out(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
-    if (!record(ev, 3, stream)) return ATTNQAT_ERR_HIP;
+    if (attnqat::launch_fwd_out(a, p->head_dim, stream, timing(ev, 2)) != hipSuccess)
+      return ATTNQAT_ERR_HIP;
   }
   return ATTNQAT_OK;
 }
@@ -286,7 +286,8 @@ int run_fwd_packed(const attnqat_problem* p, const void* q, const uint8_t* k_cod
 
 int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
             const void* o_hp, const void* d_o, const float* lse, void* dq, void* dk, void* dv,
-            void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev) {
+            void* workspace, size_t workspace_bytes, hipStream_t stream,
+            const attnqat::LaunchEvents* ev) {
   int st = validate_problem(p);
   if (st != ATTNQAT_OK) return st;
   const void* ptrs[] = {q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace};
@@ -307,22 +308,19 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   uint16_t* vh = at<uint16_t>(workspace, L.v_hat);
   float* delta = at<float>(workspace, L.delta);
 
-  // 1) Q fake-quantization fused with delta = rowsum(O_hp * dO)
-  if (!record(ev, 0, stream)) return ATTNQAT_ERR_HIP;
-  if (attnqat::launch_quant_q_delta(static_cast<const uint16_t*>(q),
-                                    static_cast<const uint16_t*>(o_hp),
-                                    static_cast<const uint16_t*>(d_o), qh,
-                                    at<uint8_t>(workspace, L.q_scale), delta,
-                                    bh * p->seqlen_q, p->head_dim, stream) != hipSuccess)
+  // 1) Q fake-quantization fused with delta = rowsum(O_hp * dO), and 2) the
+  // K/V fake-quantization, in one launch
+  const attnqat::QDeltaJob qd = {static_cast<const uint16_t*>(q),
+                                 static_cast<const uint16_t*>(o_hp),
+                                 static_cast<const uint16_t*>(d_o),
+                                 qh,
+                                 at<uint8_t>(workspace, L.q_scale),
+                                 delta,
+                                 bh * p->seqlen_q};
+  const QuantJob kj = {k, kh, at<uint8_t>(workspace, L.k_scale), bh * p->seqlen_kv * D / 16};
+  const QuantJob vj = {v, vh, at<uint8_t>(workspace, L.v_scale), bh * p->seqlen_kv * D / 16};
+  if (attnqat::launch_bwd_codec(qd, kj, vj, p->head_dim, stream, timing(ev, 0)) != hipSuccess)
     return ATTNQAT_ERR_HIP;
-  // 2) K/V fake-quantization
-  QuantJob jobs[2] = {
-      {k, kh, at<uint8_t>(workspace, L.k_scale), bh * p->seqlen_kv * D / 16},
-      {v, vh, at<uint8_t>(workspace, L.v_scale), bh * p->seqlen_kv * D / 16},
-  };
-  if (!record(ev, 1, stream)) return ATTNQAT_ERR_HIP;
-  if (attnqat::launch_quant_bf16(jobs, 2, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
-  if (!record(ev, 2, stream)) return ATTNQAT_ERR_HIP;
 
   AttnArgs a = {};
   a.q_hat = qh;
@@ -341,17 +339,20 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   a.softmax_scale = p->softmax_scale;
   a.p_scale = p->p_scale;
   // 3) dQ and 4) dK/dV
-  if (attnqat::launch_bwd_dq(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
-  if (!record(ev, 3, stream)) return ATTNQAT_ERR_HIP;
-  if (attnqat::launch_bwd_dkdv(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
-  if (!record(ev, 4, stream)) return ATTNQAT_ERR_HIP;
+  if (attnqat::launch_bwd_dq(a, p->head_dim, stream, timing(ev, 1)) != hipSuccess)
+    return ATTNQAT_ERR_HIP;
+  if (attnqat::launch_bwd_dkdv(a, p->head_dim, stream, timing(ev, 2)) != hipSuccess)
+    return ATTNQAT_ERR_HIP;
   return ATTNQAT_OK;
 }
 
-bool events_ok(const hipEvent_t* ev, int n) {
+// n launches' start/stop event pairs from a caller's array of 2n events, or
+// false when the array or one of its events is null.
+bool event_pairs(hipEvent_t* ev, int n, attnqat::LaunchEvents* out) {
   if (ev == nullptr) return false;
-  for (int i = 0; i < n; ++i)
+  for (int i = 0; i < 2 * n; ++i)
     if (ev[i] == nullptr) return false;
+  for (int i = 0; i < n; ++i) out[i] = attnqat::LaunchEvents{ev[2 * i], ev[2 * i + 1]};
   return true;
 }
 
@@ -388,25 +389,26 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
 int attnqat_fwd_timed(const attnqat_problem* p, const void* q, const void* k, const void* v,
                       void* o_hp, float* lse, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, hipEvent_t* events) {
-  if (!events_ok(events, 3)) return ATTNQAT_ERR_INVALID_ARGUMENT;
-  return run_fwd(p, q, k, v, o_hp, lse, false, nullptr, workspace, workspace_bytes, stream,
-                 events);
+  attnqat::LaunchEvents ev[2];
+  if (!event_pairs(events, 2, ev)) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  return run_fwd(p, q, k, v, o_hp, lse, false, nullptr, workspace, workspace_bytes, stream, ev);
 }
 int attnqat_fwd_quantized_timed(const attnqat_problem* p, const void* q, const void* k,
                                 const void* v, void* o_hp, float* lse, void* o,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t* events) {
-  if (!events_ok(events, 4)) return ATTNQAT_ERR_INVALID_ARGUMENT;
-  return run_fwd(p, q, k, v, o_hp, lse, true, o, workspace, workspace_bytes, stream, events);
+  attnqat::LaunchEvents ev[3];
+  if (!event_pairs(events, 3, ev)) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  return run_fwd(p, q, k, v, o_hp, lse, true, o, workspace, workspace_bytes, stream, ev);
 }
 
 int attnqat_bwd_timed(const attnqat_problem* p, const void* q, const void* k, const void* v,
                       const void* o_hp, const void* d_o, const float* lse, void* dq, void* dk,
                       void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream,
                       hipEvent_t* events) {
-  if (!events_ok(events, 5)) return ATTNQAT_ERR_INVALID_ARGUMENT;
-  return run_bwd(p, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace, workspace_bytes, stream,
-                 events);
+  attnqat::LaunchEvents ev[3];
+  if (!event_pairs(events, 3, ev)) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  return run_bwd(p, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace, workspace_bytes, stream, ev);
 }
 
 }  // extern "C"

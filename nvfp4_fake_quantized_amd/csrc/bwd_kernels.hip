@@ -313,20 +313,14 @@ void k_dq(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)(((a.nq + kDqBM - 1) / kDqBM) * a.bh));
-  if (head_dim == 128) {
-    if (a.causal)
-      hipLaunchKernelGGL((k_dq<128, true>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_dq<128, false>), grid, dim3(256), 0, stream, a);
-  } else {
-    if (a.causal)
-      hipLaunchKernelGGL((k_dq<64, true>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_dq<64, false>), grid, dim3(256), 0, stream, a);
-  }
-  return hipGetLastError();
+hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream,
+                         const LaunchEvents* ev) {
+  const dim3 grid((unsigned)(((a.nq + kDqBM - 1) / kDqBM) * a.bh)), block(256);
+  if (head_dim == 128)
+    return a.causal ? launch(k_dq<128, true>, grid, block, stream, ev, a)
+                    : launch(k_dq<128, false>, grid, block, stream, ev, a);
+  return a.causal ? launch(k_dq<64, true>, grid, block, stream, ev, a)
+                  : launch(k_dq<64, false>, grid, block, stream, ev, a);
 }
 
 }  // namespace attnqat

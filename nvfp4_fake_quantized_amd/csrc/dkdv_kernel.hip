@@ -500,29 +500,20 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
 }
 
 template <int D, bool CAUSAL>
-void launch_dkdv_d(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)(((a.nkv + kKeys - 1) / kKeys) * a.bh));
-  if (a.p_scale == 1.0f)
-    hipLaunchKernelGGL((k_dkdv<D, CAUSAL, true>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_dkdv<D, CAUSAL, false>), grid, dim3(kThreads), 0, stream, a);
+hipError_t launch_dkdv_d(const AttnArgs& a, hipStream_t stream, const LaunchEvents* ev) {
+  const dim3 grid((unsigned)(((a.nkv + kKeys - 1) / kKeys) * a.bh)), block(kThreads);
+  if (a.p_scale == 1.0f) return launch(k_dkdv<D, CAUSAL, true>, grid, block, stream, ev, a);
+  return launch(k_dkdv<D, CAUSAL, false>, grid, block, stream, ev, a);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) {
-    if (a.causal)
-      launch_dkdv_d<128, true>(a, stream);
-    else
-      launch_dkdv_d<128, false>(a, stream);
-  } else {
-    if (a.causal)
-      launch_dkdv_d<64, true>(a, stream);
-    else
-      launch_dkdv_d<64, false>(a, stream);
-  }
-  return hipGetLastError();
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream,
+                           const LaunchEvents* ev) {
+  if (head_dim == 128)
+    return a.causal ? launch_dkdv_d<128, true>(a, stream, ev)
+                    : launch_dkdv_d<128, false>(a, stream, ev);
+  return a.causal ? launch_dkdv_d<64, true>(a, stream, ev) : launch_dkdv_d<64, false>(a, stream, ev);
 }
 
 }  // namespace attnqat

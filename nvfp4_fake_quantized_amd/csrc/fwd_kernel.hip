@@ -376,28 +376,23 @@ void k_fwd(AttnArgs a) {
 }  // namespace
 
 template <bool PACKED>
-hipError_t launch_fwd_t(const AttnArgs& a, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)(((a.nq + kFwdBM - 1) / kFwdBM) * a.bh));
-  if (head_dim == 128) {
-    if (a.causal)
-      hipLaunchKernelGGL((k_fwd<128, true, PACKED>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_fwd<128, false, PACKED>), grid, dim3(256), 0, stream, a);
-  } else {
-    if (a.causal)
-      hipLaunchKernelGGL((k_fwd<64, true, PACKED>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_fwd<64, false, PACKED>), grid, dim3(256), 0, stream, a);
-  }
-  return hipGetLastError();
+hipError_t launch_fwd_t(const AttnArgs& a, int head_dim, hipStream_t stream,
+                        const LaunchEvents* ev) {
+  const dim3 grid((unsigned)(((a.nq + kFwdBM - 1) / kFwdBM) * a.bh)), block(256);
+  if (head_dim == 128)
+    return a.causal ? launch(k_fwd<128, true, PACKED>, grid, block, stream, ev, a)
+                    : launch(k_fwd<128, false, PACKED>, grid, block, stream, ev, a);
+  return a.causal ? launch(k_fwd<64, true, PACKED>, grid, block, stream, ev, a)
+                  : launch(k_fwd<64, false, PACKED>, grid, block, stream, ev, a);
 }
 
-hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream) {
-  return launch_fwd_t<false>(a, head_dim, stream);
+hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream,
+                      const LaunchEvents* ev) {
+  return launch_fwd_t<false>(a, head_dim, stream, ev);
 }
 
 hipError_t launch_fwd_packed(const AttnArgs& a, int head_dim, hipStream_t stream) {
-  return launch_fwd_t<true>(a, head_dim, stream);
+  return launch_fwd_t<true>(a, head_dim, stream, nullptr);
 }
 
 }  // namespace attnqat

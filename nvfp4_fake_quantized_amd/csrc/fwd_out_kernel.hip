@@ -286,29 +286,19 @@ void k_fwd_out(AttnArgs a) {
 }
 
 template <int D, bool CAUSAL>
-void launch_out_d(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)(((a.nq + kOutBM - 1) / kOutBM) * a.bh));
-  if (a.p_scale == 1.0f)
-    hipLaunchKernelGGL((k_fwd_out<D, CAUSAL, true>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_fwd_out<D, CAUSAL, false>), grid, dim3(256), 0, stream, a);
+hipError_t launch_out_d(const AttnArgs& a, hipStream_t stream, const LaunchEvents* ev) {
+  const dim3 grid((unsigned)(((a.nq + kOutBM - 1) / kOutBM) * a.bh)), block(256);
+  if (a.p_scale == 1.0f) return launch(k_fwd_out<D, CAUSAL, true>, grid, block, stream, ev, a);
+  return launch(k_fwd_out<D, CAUSAL, false>, grid, block, stream, ev, a);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_out(const AttnArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) {
-    if (a.causal)
-      launch_out_d<128, true>(a, stream);
-    else
-      launch_out_d<128, false>(a, stream);
-  } else {
-    if (a.causal)
-      launch_out_d<64, true>(a, stream);
-    else
-      launch_out_d<64, false>(a, stream);
-  }
-  return hipGetLastError();
+hipError_t launch_fwd_out(const AttnArgs& a, int head_dim, hipStream_t stream,
+                          const LaunchEvents* ev) {
+  if (head_dim == 128)
+    return a.causal ? launch_out_d<128, true>(a, stream, ev) : launch_out_d<128, false>(a, stream, ev);
+  return a.causal ? launch_out_d<64, true>(a, stream, ev) : launch_out_d<64, false>(a, stream, ev);
 }
 
 }  // namespace attnqat

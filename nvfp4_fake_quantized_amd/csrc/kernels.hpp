@@ -2,10 +2,44 @@
 // launch error; arguments are validated by the C-ABI layer beforehand.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace attnqat {
+
+// Optional start/stop events of one launch.  hipExtLaunchKernel has the
+// dispatch itself record them (kernel start and end timestamps), so timing a
+// kernel adds no packets to the stream and no gap between kernels.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename... Params, size_t... I>
+inline hipError_t launch_packed(void (*kernel)(Params...), dim3 grid, dim3 block,
+                                hipStream_t stream, const LaunchEvents* ev,
+                                std::tuple<Params...>& values, std::index_sequence<I...>) {
+  void* args[] = {static_cast<void*>(&std::get<I>(values))...};
+  if (ev == nullptr)
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream,
+                            ev->start, ev->stop, 0);
+}
+
+// Launches kernel<<<grid, block, 0, stream>>>(args...), with ev's events when
+// ev is given; returns the launch status.
+template <typename... Params, typename... Args>
+inline hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream,
+                         const LaunchEvents* ev, Args&&... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  std::tuple<Params...> values(std::forward<Args>(args)...);
+  return launch_packed(kernel, grid, block, stream, ev, values,
+                       std::index_sequence_for<Params...>{});
+}
 
 // Per-problem pointers and sizes passed to the attention kernels.  All
 // tensors are contiguous BHSD; bf16 tensors are raw 16-bit words.
@@ -42,23 +76,37 @@ struct QuantJob {
 };
 
 // fake_nvfp4 over up to three bf16 tensors in one launch.
-hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream);
+hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream,
+                             const LaunchEvents* ev = nullptr);
 // Packed NVFP4 codes (2 per byte) and scale bytes of one bf16 tensor.
 hipError_t launch_pack_bf16(const QuantJob& job, uint8_t* codes, hipStream_t stream);
 // fake_nvfp4 over one fp32 tensor.
 hipError_t launch_quant_f32(const QuantJob& job, hipStream_t stream);
-// Q fake-quant fused with delta = rowsum(O_hp * dO) (fp32), D in {64,128}.
-hipError_t launch_quant_q_delta(const uint16_t* q, const uint16_t* o_hp, const uint16_t* d_o,
-                                uint16_t* q_hat, uint8_t* q_scale, float* delta,
-                                int64_t rows, int head_dim, hipStream_t stream);
+// The backward's preprocessing in one launch: Q fake-quant fused with
+// delta = rowsum(O_hp * dO) (fp32), and K and V fake-quant; D in {64, 128}.
+struct QDeltaJob {
+  const uint16_t* q;
+  const uint16_t* o_hp;
+  const uint16_t* d_o;
+  uint16_t* q_hat;
+  uint8_t* q_scale;
+  float* delta;
+  int64_t rows;  // batch * heads * seqlen_q
+};
+hipError_t launch_bwd_codec(const QDeltaJob& qd, const QuantJob& k, const QuantJob& v,
+                            int head_dim, hipStream_t stream, const LaunchEvents* ev = nullptr);
 
-hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream,
+                      const LaunchEvents* ev = nullptr);
 // The same forward with K^ and V^ given as packed NVFP4 (a.k_codes ...).
 hipError_t launch_fwd_packed(const AttnArgs& a, int head_dim, hipStream_t stream);
 // O = P^F V^ from Q^, K^, V^ and the forward's lse (a.lse), into a.o_q.
-hipError_t launch_fwd_out(const AttnArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_fwd_out(const AttnArgs& a, int head_dim, hipStream_t stream,
+                          const LaunchEvents* ev = nullptr);
+hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream,
+                         const LaunchEvents* ev = nullptr);
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream,
+                           const LaunchEvents* ev = nullptr);
 // Sustained bf16 MFMA rate probe: blocks of 256 threads, each thread reading
 // 32 bf16 of a and of b at offset 32 * thread.
 hipError_t launch_mfma_peak(const uint16_t* a, const uint16_t* b, float* out, int blocks,

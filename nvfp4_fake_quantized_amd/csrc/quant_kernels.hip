@@ -2,9 +2,10 @@
 //
 // One thread owns one group of 16 contiguous values ("NVFP4 Attention QAT
 // Backward", §Overview: one E4M3 scale per 16 values); a wave covers 64
-// consecutive groups, i.e. 2 KiB of contiguous bf16 input.  The fused
-// Q + delta kernel is the first of the backward's four kernels (same page,
-// §Overview: "fused Q fake-quantization/delta preprocessing").
+// consecutive groups, i.e. 2 KiB of contiguous bf16 input.  The backward's
+// preprocessing (same page, §Overview: the fused Q fake-quantization / delta
+// kernel and the K/V fake-quantization) runs as one launch, k_bwd_codec, whose
+// blockIdx.y selects Q + delta, K or V: one ramp-up and tail instead of two.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -51,10 +52,8 @@ __device__ __forceinline__ float fq16(float* x) {
   return s;
 }
 
-__global__ __launch_bounds__(kThreads) void k_quant_bf16(QuantJobs3 jobs) {
-  const QuantJob& J = jobs.job[blockIdx.y];
-  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (g >= J.groups) return;
+// fake_nvfp4 of group g of job J (g < J.groups)
+__device__ __forceinline__ void quant_group(const QuantJob& J, int64_t g) {
   const u32x4* src = reinterpret_cast<const u32x4*>(J.src) + 2 * g;
   u32x4 lo = src[0], hi = src[1];
   float x[16];
@@ -65,6 +64,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf16(QuantJobs3 jobs) {
   dst[0] = lo;
   dst[1] = hi;
   if (J.scales) J.scales[g] = (uint8_t)e4m3_byte(s);
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_bf16(QuantJobs3 jobs) {
+  const QuantJob& J = jobs.job[blockIdx.y];
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g < J.groups) quant_group(J, g);
 }
 
 // Packed NVFP4 storage: per group of 16 bf16 values, 8 bytes of E2M1 codes
@@ -124,24 +129,20 @@ __global__ __launch_bounds__(kThreads) void k_quant_f32(QuantJob J) {
   if (J.scales) J.scales[g] = (uint8_t)e4m3_byte(s);
 }
 
+// Q fake-quant of group g fused with its share of delta = rowsum(O_hp * dO).
 // GPR = groups per row (D / 16): 8 for D = 128, 4 for D = 64.  The GPR lanes
-// of a row are consecutive and aligned within the wave.
+// of a row are consecutive and aligned within the wave; the whole wave calls
+// this (the row reduction is a cross-lane shuffle), lanes past the end with
+// g >= groups.
 template <int GPR>
-__global__ __launch_bounds__(kThreads) void k_quant_q_delta(const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ o_hp,
-                                                            const uint16_t* __restrict__ d_o,
-                                                            uint16_t* __restrict__ q_hat,
-                                                            uint8_t* __restrict__ q_scale,
-                                                            float* __restrict__ delta,
-                                                            int64_t rows) {
-  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t groups = rows * GPR;
+__device__ __forceinline__ void q_delta_group(const QDeltaJob& J, int64_t g) {
+  const int64_t groups = J.rows * GPR;
   const bool active = g < groups;
   const int64_t gg = active ? g : 0;
   float part = 0.0f;
   {
-    const u32x4* po = reinterpret_cast<const u32x4*>(o_hp) + 2 * gg;
-    const u32x4* pd = reinterpret_cast<const u32x4*>(d_o) + 2 * gg;
+    const u32x4* po = reinterpret_cast<const u32x4*>(J.o_hp) + 2 * gg;
+    const u32x4* pd = reinterpret_cast<const u32x4*>(J.d_o) + 2 * gg;
     float o[16], d[16];
     unpack_bf16x16(po[0], po[1], o);
     unpack_bf16x16(pd[0], pd[1], d);
@@ -149,21 +150,35 @@ __global__ __launch_bounds__(kThreads) void k_quant_q_delta(const uint16_t* __re
     for (int i = 0; i < 16; ++i) part = fmaf(o[i], d[i], part);
   }
   if (active) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(q) + 2 * g;
+    const u32x4* src = reinterpret_cast<const u32x4*>(J.q) + 2 * g;
     u32x4 lo = src[0], hi = src[1];
     float x[16];
     unpack_bf16x16(lo, hi, x);
     const float s = fq16(x);
     pack_bf16x16(x, lo, hi);
-    u32x4* dst = reinterpret_cast<u32x4*>(q_hat) + 2 * g;
+    u32x4* dst = reinterpret_cast<u32x4*>(J.q_hat) + 2 * g;
     dst[0] = lo;
     dst[1] = hi;
-    q_scale[g] = (uint8_t)e4m3_byte(s);
+    J.q_scale[g] = (uint8_t)e4m3_byte(s);
   }
   // reduce the row's partial dot products over its GPR lanes (fixed order)
 #pragma unroll
   for (int off = 1; off < GPR; off <<= 1) part += __shfl_xor(part, off, 64);
-  if (active && (g % GPR) == 0) delta[g / GPR] = part;
+  if (active && (g % GPR) == 0) J.delta[g / GPR] = part;
+}
+
+// blockIdx.y = 0: Q + delta; 1: K; 2: V.  Blocks past a part's end exit.
+template <int GPR>
+__global__ __launch_bounds__(kThreads) void k_bwd_codec(QDeltaJob qd, QuantJob kj,
+                                                        QuantJob vj) {
+  const int64_t g0 = (int64_t)blockIdx.x * kThreads;
+  const int64_t g = g0 + threadIdx.x;
+  if (blockIdx.y == 0) {
+    if (g0 < qd.rows * GPR) q_delta_group<GPR>(qd, g);  // uniform per workgroup
+  } else {
+    const QuantJob& J = blockIdx.y == 1 ? kj : vj;
+    if (g < J.groups) quant_group(J, g);
+  }
 }
 
 inline unsigned grid_for(int64_t groups) {
@@ -172,7 +187,8 @@ inline unsigned grid_for(int64_t groups) {
 
 }  // namespace
 
-hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream) {
+hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream,
+                             const LaunchEvents* ev) {
   QuantJobs3 j3 = {};
   int64_t maxg = 0;
   for (int i = 0; i < njobs; ++i) {
@@ -180,9 +196,7 @@ hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream
     if (jobs[i].groups > maxg) maxg = jobs[i].groups;
   }
   if (maxg == 0) return hipSuccess;
-  dim3 grid(grid_for(maxg), njobs);
-  hipLaunchKernelGGL(k_quant_bf16, grid, dim3(kThreads), 0, stream, j3);
-  return hipGetLastError();
+  return launch(k_quant_bf16, dim3(grid_for(maxg), njobs), dim3(kThreads), stream, ev, j3);
 }
 
 hipError_t launch_pack_bf16(const QuantJob& job, uint8_t* codes, hipStream_t stream) {
@@ -198,20 +212,16 @@ hipError_t launch_quant_f32(const QuantJob& job, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_quant_q_delta(const uint16_t* q, const uint16_t* o_hp, const uint16_t* d_o,
-                                uint16_t* q_hat, uint8_t* q_scale, float* delta, int64_t rows,
-                                int head_dim, hipStream_t stream) {
-  if (rows == 0) return hipSuccess;
+hipError_t launch_bwd_codec(const QDeltaJob& qd, const QuantJob& k, const QuantJob& v,
+                            int head_dim, hipStream_t stream, const LaunchEvents* ev) {
   const int gpr = head_dim / 16;
-  const unsigned grid = grid_for(rows * gpr);
-  if (gpr == 8) {
-    hipLaunchKernelGGL(k_quant_q_delta<8>, dim3(grid), dim3(kThreads), 0, stream, q, o_hp, d_o,
-                       q_hat, q_scale, delta, rows);
-  } else {
-    hipLaunchKernelGGL(k_quant_q_delta<4>, dim3(grid), dim3(kThreads), 0, stream, q, o_hp, d_o,
-                       q_hat, q_scale, delta, rows);
-  }
-  return hipGetLastError();
+  int64_t maxg = qd.rows * gpr;
+  if (k.groups > maxg) maxg = k.groups;
+  if (v.groups > maxg) maxg = v.groups;
+  if (maxg == 0) return hipSuccess;
+  const dim3 grid(grid_for(maxg), 3);
+  if (gpr == 8) return launch(k_bwd_codec<8>, grid, dim3(kThreads), stream, ev, qd, k, v);
+  return launch(k_bwd_codec<4>, grid, dim3(kThreads), stream, ev, qd, k, v);
 }
 
 }  // namespace attnqat
