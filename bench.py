@@ -3,8 +3,9 @@
 
 One step = one pass of the whole hot path over one batch: attnqat_fwd (Q/K/V
 fake-quant + the QAT forward producing O_hp and lse) followed by
-attnqat_bwd on that output (Q fake-quant + delta, K/V fake-quant, dQ,
-dK/dV).  Inputs are resident in HBM before timing starts.
+attnqat_bwd on that output (one launch for Q fake-quant + delta and K/V
+fake-quant, then dQ, then dK/dV).  Inputs are resident in HBM before timing
+starts.
 
 Order of the run: a clock-settling phase (plain steps until --settle-s
 seconds have passed: the kernels' durations drift over the first few dozen
@@ -12,9 +13,11 @@ steps while the power management settles), W warmup steps, the K timed
 steps (the headline: HIP events on the benchmark's stream around each
 attnqat_fwd and attnqat_bwd call, wall clock around all K), then, in the same
 steady state, K steps of the instrumented entry points for the per-kernel
-split and the roofline entry, the full forward with the quantized output,
-the forward from packed K/V, the backward after a flush of the 256 MB
-Infinity Cache, and the sustained MFMA rate probe.
+split and the roofline entry (each launch's dispatch records its own
+start/stop events, so the split adds no gaps), the full forward with the
+quantized output, the forward from packed K/V, the backward after a flush of
+the 256 MB Infinity Cache, the sustained MFMA rate probe on random and on
+uniform operands, and a plain device copy of the K/V codec's byte count.
 
 The reported metric is the backward's throughput: counted backward work
 10*B*H*N^2*D (halved when causal) divided by the median backward duration.
@@ -251,13 +254,21 @@ def _stats(xs):
             "mean": round(sum(xs) / n, 4)}
 
 
-def mfma_probe(B, dev, hip, stream, blocks=2048, iters=400, reps=5):
-    """Sustained bf16 MFMA rate on random operands (TFLOP/s, best of reps)."""
+def mfma_probe(B, dev, hip, stream, uniform=False, blocks=1024, iters=800, reps=5):
+    """Sustained bf16 MFMA rate (TFLOP/s, best of reps), 4 waves per SIMD, on
+    random N(0,1) operands, or with uniform=True on operands that are all 1.0.
+    The rate depends on the data: operand bits that toggle draw more power
+    and the clock drops, so random operands (like the attention kernels')
+    run well below uniform ones."""
     import torch
     g = torch.Generator(device="cpu").manual_seed(123)
     n = 32 * 256 * blocks
-    a = torch.randn(n, generator=g).to(torch.bfloat16).to(dev)
-    b = torch.randn(n, generator=g).to(torch.bfloat16).to(dev)
+    if uniform:
+        a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        b = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    else:
+        a = torch.randn(n, generator=g).to(torch.bfloat16).to(dev)
+        b = torch.randn(n, generator=g).to(torch.bfloat16).to(dev)
     out = torch.empty(256 * blocks, dtype=torch.float32, device=dev)
     flops = B.attnqat_probe_mfma_peak(a, b, out, blocks, iters, stream)
     torch.cuda.synchronize()
@@ -272,6 +283,74 @@ def mfma_probe(B, dev, hip, stream, blocks=2048, iters=400, reps=5):
     return best
 
 
+ISSUE_MIX_CASES = (
+    # (label, mode, fp32 FMAs per MFMA slot, AGPR accumulators, threads)
+    ("MFMA only, one wave per SIMD", 0, 8, False, 256),
+    ("VALU only, one wave per SIMD", 1, 8, False, 256),
+    ("MFMA + VALU interleaved in one wave", 2, 8, False, 256),
+    ("MFMA wave + VALU wave on one SIMD", 3, 8, False, 512),
+    ("MFMA only, one wave per SIMD, AGPR acc", 0, 8, True, 256),
+    ("MFMA + VALU interleaved in one wave, AGPR acc", 2, 8, True, 256),
+    ("MFMA wave + VALU wave on one SIMD, AGPR acc", 3, 8, True, 512),
+    ("VALU only (16 per slot), one wave per SIMD", 1, 16, False, 256),
+    ("MFMA + VALU (16) interleaved in one wave", 2, 16, False, 256),
+    ("MFMA wave + VALU (16) wave on one SIMD", 3, 16, False, 512),
+    ("MFMA + VALU (16) interleaved in one wave, AGPR acc", 2, 16, True, 256),
+    ("MFMA wave + VALU (16) wave on one SIMD, AGPR acc", 3, 16, True, 512),
+)
+LDS_WRITE_PATTERNS = (
+    "8 B stores, linear",
+    "8 B stores, 64 B rows, unswizzled",
+    "8 B stores, 64 B rows, column ^ 4*((row>>2)&7)",
+    "16 B stores, linear",
+    "16 B stores, 64 B rows, chunk ^ ((row>>2)&3)",
+    "16 B stores, 64 B rows, chunk ^ ((row>>1)&3) (dK/dV tiles)",
+)
+
+
+def run_probes(reps=5):
+    """The MFMA/VALU issue-mix and LDS write-pattern probes (one JSON line).
+    Each case is timed with events on the stream, median of `reps` after one
+    untimed call; 256 workgroups (one per CU)."""
+    import torch
+
+    from nvfp4_fake_quantized_amd import binding as B
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    hip = HipEvents()
+    g = torch.Generator(device="cpu").manual_seed(7)
+    inp = (0.5 * torch.randn(8192, generator=g)).to(torch.bfloat16).to(dev)
+    out = torch.empty(256 * 512, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        evs = [hip.array(2) for _ in range(reps)]
+        for e in evs:
+            hip.record(e[0], stream)
+            fn()
+            hip.record(e[1], stream)
+        torch.cuda.synchronize()
+        return _stats([hip.ms(e[0], e[1]) for e in evs])["median"]
+
+    iters = 4000  # 32000 MFMA slots per wave
+    mix = []
+    for label, mode, nv, agpr, threads in ISSUE_MIX_CASES:
+        ms = timed(lambda: B.attnqat_probe_issue_mix(mode, nv, agpr, inp, out, 256, threads,
+                                                     iters, stream))
+        mix.append({"case": label, "ms": ms})
+        log(f"  issue mix: {label:52s} {ms:.3f} ms")
+    lds = []
+    lds_iters, lds_blocks = 4096, 512
+    for pattern, label in enumerate(LDS_WRITE_PATTERNS):
+        ms = timed(lambda: B.attnqat_probe_lds_write(pattern, out, lds_blocks, lds_iters, stream))
+        nbytes = lds_blocks * 256 * lds_iters * 4 * (16 if pattern >= 3 else 8)
+        lds.append({"pattern": pattern, "case": label, "ms": ms,
+                    "bytes_per_ns": round(nbytes / (ms * 1e6), 1)})
+        log(f"  LDS write {pattern}: {label:58s} {ms:.3f} ms")
+    hip.close()
+    return {"issue_mix": mix, "lds_write": lds}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +359,10 @@ def main():
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup (clock settling)")
     ap.add_argument("--workload", default="ref_shape")
+    ap.add_argument("--seqlen", type=int, default=None,
+                    help="override the workload's sequence length (same seed and recipe)")
+    ap.add_argument("--causal", choices=("yes", "no"), default=None,
+                    help="override the workload's causal flag")
     ap.add_argument("--p-scale", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -289,6 +372,9 @@ def main():
     ap.add_argument("--p-scale-study", action="store_true",
                     help="instead of the benchmark, print the p_scale gradient-quality study "
                          "(one JSON line)")
+    ap.add_argument("--probes", action="store_true",
+                    help="instead of the benchmark, run the MFMA/VALU issue-mix and LDS "
+                         "write-pattern probes (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on a single GPU; multi-GPU runs are not part of this "
@@ -298,6 +384,9 @@ def main():
     if args.p_scale_study:
         print(json.dumps({"p_scale_study": p_scale_study()}), flush=True)
         return
+    if args.probes:
+        print(json.dumps({"probes": run_probes()}), flush=True)
+        return
 
     import torch
 
@@ -305,6 +394,13 @@ def main():
     from workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.seqlen is not None or args.causal is not None:
+        import dataclasses
+        n = args.seqlen if args.seqlen is not None else w.seqlen
+        c = (args.causal == "yes") if args.causal is not None else w.causal
+        w = dataclasses.replace(
+            w, name=f"{w.name}_n{n}{'_causal' if c else ''}", seqlen=n, causal=c,
+            description=f"{w.description}, overridden to N{n} {'causal' if c else 'non-causal'}")
     dev = torch.device("cuda:0")
     q, k, v, do = make_inputs(w)
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
@@ -407,6 +503,7 @@ def main():
         extras["bwd_ms_after_cache_flush"] = _stats([hip.ms(e[0], e[1]) for e in evc])
         del flush
         extras["mfma_probe_tflops"] = round(mfma_probe(B, dev, hip, stream), 1)
+        extras["mfma_probe_uniform_tflops"] = round(mfma_probe(B, dev, hip, stream, uniform=True), 1)
         # a plain device copy moving as many bytes as the backward's K/V
         # fake-quant kernel reads and writes (context for the codec rates)
         nb = 2 * kd.numel()  # bf16 elements of K and V

@@ -57,6 +57,34 @@ ATTNQAT_API int attnqat_bwd_timed(const attnqat_problem* p, const void* q, const
 ATTNQAT_API int attnqat_probe_mfma_peak(const void* a, const void* b, float* out, int blocks,
                                         int iters, hipStream_t stream);
 
+/* How MFMA and VALU instructions share a SIMD: `blocks` workgroups of
+ * `threads` (256: one wave per SIMD, 512: two) threads; every wave runs
+ * iters * 8 slots.  mode 0: one v_mfma_f32_32x32x16_bf16 per slot (two
+ * accumulator chains); 1: valu_per_mfma (8 or 16) independent fp32 FMAs per
+ * slot; 2: both in every wave, interleaved; 3 (threads = 512 only): waves
+ * 0-3 the MFMAs, waves 4-7 the FMAs, so that each SIMD runs one wave of each
+ * (waves w and w + 4 share a SIMD).  agpr != 0 keeps the MFMA accumulators in AGPRs instead of
+ * VGPRs.  Operands are read from `in` (>= 8192 bf16); one float per thread is
+ * written to out (>= blocks * threads floats).  The caller times the call.
+ * Out-of-range arguments: ATTNQAT_ERR_INVALID_ARGUMENT. */
+ATTNQAT_API int attnqat_probe_issue_mix(int mode, int valu_per_mfma, int agpr, const void* in,
+                                        float* out, int blocks, int threads, int iters,
+                                        hipStream_t stream);
+
+/* LDS write patterns, for bank-conflict counters (SQ_LDS_BANK_CONFLICT):
+ * `blocks` workgroups of 256 threads; every wave writes 4 stores per
+ * iteration into its own 4 KiB region, lane l at row r = l % 32, half
+ * h = l / 32, store i:
+ *   0: 8-byte stores at byte 8l (+512 for odd i)           linear
+ *   1: 8-byte stores, row r of 64 bytes, column 16h + 4i    unswizzled rows
+ *   2: as 1 with the column XOR 4 * ((r >> 2) & 7)
+ *   3: 16-byte stores at byte 16l                           linear
+ *   4: 16-byte stores, row r of 64 bytes, 16-byte chunk (2h + i % 2) XOR ((r >> 2) & 3)
+ *   5: as 4 with the chunk XOR ((r >> 1) & 3)  (the dK/dV kernel's tiles)
+ * out >= blocks * 256 floats.  The caller times the call. */
+ATTNQAT_API int attnqat_probe_lds_write(int pattern, float* out, int blocks, int iters,
+                                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,6 +84,10 @@ _SIGS = {
     "attnqat_bwd_timed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _sz, _vp, _vp]),
     "attnqat_probe_mfma_peak": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp]),
+    "attnqat_probe_issue_mix": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
+    "attnqat_probe_lds_write": (ctypes.c_int, [ctypes.c_int, _vp, ctypes.c_int, ctypes.c_int,
+                                               _vp]),
     "attnqat_bwd_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -350,6 +354,29 @@ def attnqat_probe_mfma_peak(a, b, out, blocks, iters, stream=None):
     _check(_lib.attnqat_probe_mfma_peak(_ptr(a), _ptr(b), _ptr(out), blocks, iters,
                                         _stream(stream)), "attnqat_probe_mfma_peak")
     return blocks * 4 * iters * 16 * 32768
+
+
+def attnqat_probe_issue_mix(mode, valu_per_mfma, agpr, inp, out, blocks, threads, iters,
+                            stream=None):
+    """MFMA / VALU issue-mix probe (attnqat_instrument.h); the caller times it."""
+    _expect(inp, "in", torch.bfloat16)
+    _expect(out, "out", torch.float32, device=inp.device)
+    if inp.numel() < 8192 or out.numel() < blocks * threads:
+        raise ValueError("probe buffers too small")
+    _device_of(inp)
+    _check(_lib.attnqat_probe_issue_mix(mode, valu_per_mfma, int(bool(agpr)), _ptr(inp),
+                                        _ptr(out), blocks, threads, iters, _stream(stream)),
+           "attnqat_probe_issue_mix")
+
+
+def attnqat_probe_lds_write(pattern, out, blocks, iters, stream=None):
+    """LDS write-pattern probe (attnqat_instrument.h); the caller times it."""
+    _expect(out, "out", torch.float32)
+    if out.numel() < blocks * 256:
+        raise ValueError("probe buffer too small")
+    _device_of(out)
+    _check(_lib.attnqat_probe_lds_write(pattern, _ptr(out), blocks, iters, _stream(stream)),
+           "attnqat_probe_lds_write")
 
 
 # ---- conveniences (allocation via torch, then one C call) --------------------

@@ -473,3 +473,37 @@ extern "C" int attnqat_bwd_noalloc(const attnqat_problem* p, const void* q, cons
   if (ws == nullptr) return ATTNQAT_ERR_HIP;
   return run_bwd(p, q, k, v, o_hp, d_o, lse, dq, dk, dv, ws, kScratchBytes, stream, nullptr);
 }
+
+extern "C" int attnqat_probe_issue_mix(int mode, int valu_per_mfma, int agpr, const void* in,
+                                       float* out, int blocks, int threads, int iters,
+                                       hipStream_t stream) {
+  if (in == nullptr || out == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (mode < 0 || mode > 3 || (valu_per_mfma != 8 && valu_per_mfma != 16) ||
+      (threads != 256 && threads != 512) || (mode == 3 && threads != 512) || blocks < 1 ||
+      blocks > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (!aligned16(in) || !aligned16(out)) return ATTNQAT_ERR_MISALIGNED;
+  const int st = device_status();
+  if (st != ATTNQAT_OK) return st;
+  (void)hipGetLastError();
+  return attnqat::launch_issue_mix(mode, valu_per_mfma, agpr != 0,
+                                   static_cast<const uint16_t*>(in), out, blocks, threads, iters,
+                                   stream) == hipSuccess
+             ? ATTNQAT_OK
+             : ATTNQAT_ERR_HIP;
+}
+
+extern "C" int attnqat_probe_lds_write(int pattern, float* out, int blocks, int iters,
+                                       hipStream_t stream) {
+  if (out == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (pattern < 0 || pattern > 5 || blocks < 1 || blocks > (1 << 20) || iters < 1 ||
+      iters > (1 << 20))
+    return ATTNQAT_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out)) return ATTNQAT_ERR_MISALIGNED;
+  const int st = device_status();
+  if (st != ATTNQAT_OK) return st;
+  (void)hipGetLastError();
+  return attnqat::launch_lds_write(pattern, out, blocks, iters, stream) == hipSuccess
+             ? ATTNQAT_OK
+             : ATTNQAT_ERR_HIP;
+}

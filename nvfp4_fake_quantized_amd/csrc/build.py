@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libattnqat.so"
 SOURCES = ["api.hip", "quant_kernels.hip", "fwd_kernel.hip", "fwd_out_kernel.hip", "bwd_kernels.hip", "dkdv_kernel.hip",
-           "probe_kernels.hip"]
+           "probe_kernels.hip", "probe_mix_kernels.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -111,5 +111,12 @@ hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream,
 // 32 bf16 of a and of b at offset 32 * thread.
 hipError_t launch_mfma_peak(const uint16_t* a, const uint16_t* b, float* out, int blocks,
                             int iters, hipStream_t stream);
+// MFMA / VALU issue-mix probe (mode 0..3, valu_per_mfma 8 or 16), blocks of
+// `threads` (256 or 512) threads; in holds >= 8192 bf16, out >= blocks*threads.
+hipError_t launch_issue_mix(int mode, int valu_per_mfma, bool agpr, const uint16_t* in,
+                            float* out, int blocks, int threads, int iters, hipStream_t stream);
+// LDS write-pattern probe (pattern 0..5), blocks of 256 threads; out >=
+// blocks*256 floats.
+hipError_t launch_lds_write(int pattern, float* out, int blocks, int iters, hipStream_t stream);
 
 }  // namespace attnqat

@@ -1,6 +1,7 @@
-// Measurement kernels (declared in attnqat_instrument.h): the sustained bf16
-// MFMA rate of the device on changing operand data, the reference against
-// which the attention kernels' MFMA rates are read.
+// Measurement kernel (declared in attnqat_instrument.h): the sustained bf16
+// MFMA rate of the device, the reference against which the attention
+// kernels' MFMA rates are read.  (The compiler keeps its four accumulator
+// chains in AGPRs.)
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
