@@ -10,22 +10,20 @@
 // gfx950 design (wave64, bf16 MFMA 32x32x16, fp32 accumulation).
 //
 // A workgroup of 8 waves owns 128 keys, as four pairs of waves that share a
-// SIMD (waves w and w+4).  A lone wave issues VALU at only half of a SIMD's
-// rate, so the two waves of a pair split the work on their 32 keys by role;
-// each issues 16 MFMAs per 32-query step, and their instruction streams
-// interleave on the SIMD:
-//  * wave X (w < 4) keeps the pair's K^ and V^ rows.  At step j it issues the
-//    MFMAs of S^T(j+1) = K^ Q^T and dP^T(j+1) = V^ dO^T (one step ahead, with
-//    operands read from LDS two MFMAs ahead) interleaved, element by element,
-//    with the VALU work on S^T(j) and dP^T(j) of the previous step:
-//    P = exp2(S s log2e - lse log2e), the group amax and E4M3 scale,
-//    dS = P (dP - delta), then the refined quotients q = P / scale and their
-//    E2M1 codes (the code rounds like the exact quotient, i.e. precise
-//    division).  It hands the 4-bit codes, the scale and the dS tile (bf16)
-//    to Y through LDS: 8 bytes of codes per lane instead of 64 bytes of P.
+// SIMD (waves w and w+4).  The two waves of a pair split the work on their
+// 32 keys by role; per 32-query step:
+//  * wave X (w < 4) keeps the pair's K^ and V^ rows (A operands).  At step j
+//    it issues the MFMAs of S^T(j+1) = K^ Q^T and dP^T(j+1) = V^ dO^T (one
+//    step ahead, with operands read from LDS two MFMAs ahead; the dP^T chain
+//    starts from -delta through one extra MFMA) interleaved with the VALU
+//    work on S^T(j) and dP^T(j): P = exp2(S s log2e - lse log2e), the group
+//    amax and E4M3 scale, dS = P (dP - delta), the quotients P / scale, their
+//    E2M1 codes (rounded like the exact quotient, i.e. precise division) and
+//    P^F = code * scale (exact in bf16).  It writes the dS and P^F tiles
+//    (bf16) to LDS, and stages the Q^/dO sub-tiles two steps ahead.
 //  * wave Y (w >= 4) keeps the dV and dK accumulators.  At step j it adds
-//    dS^T Q^ of sub-tile j-1 to dK while it forms P^F = code * scale (exact
-//    in bf16), then adds P^F^T dO to dV (operands prefetched from LDS).
+//    dS^T Q^ and P^F^T dO of sub-tile j-1 (16 MFMAs, operands from LDS
+//    transpose reads) and issues no VALU work.
 // One barrier per step orders the handover.
 //
 // In the S^T accumulator each lane holds one query and, because the K^/V^
@@ -33,7 +31,7 @@
 // one P quantization group, so the amax and the scale are per-lane work.
 // The Q^/dO sub-tiles (32 queries) sit in a ring of four LDS slots
 // (XOR-swizzled rows; row reads for S/dP, transpose reads for dK/dV); X
-// waves stage them two steps ahead through registers.  The step loops are
+// waves copy them global -> LDS directly, two steps ahead.  The step loops are
 // unrolled by the ring period, so every LDS address is a lane register plus
 // an immediate.  P^F and dS reach the A operands of dV and dK through
 // [query][key] LDS tiles read back with transpose reads.

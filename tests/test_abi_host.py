@@ -257,3 +257,31 @@ def test_noalloc_rejects_large_workspaces_on_the_host():
     assert rc == B.ERR_UNSUPPORTED
     assert B._lib.attnqat_bwd_noalloc(ctypes.byref(_prob(head_dim=96)), None, None, None, None,
                                       None, None, None, None, None, None) == B.ERR_UNSUPPORTED
+
+
+def test_instrumentation_entry_points_reject_bad_arguments_before_launch():
+    """Timed entry points need 2 events per launch; the probes check their
+    ranges and pointers before any HIP call."""
+    lib = B._lib
+    p = _prob(batch=1, heads=1, seqlen_q=128, seqlen_kv=128)
+    need = B.attnqat_bwd_workspace_bytes(p)
+    a = [_vp(0x10000 * (i + 1)) for i in range(10)]
+    ev5 = (ctypes.c_void_p * 6)(*([0x1000] * 5 + [0]))  # the 6th event is null
+    assert lib.attnqat_bwd_timed(ctypes.byref(p), *a[:9], a[9], need, None,
+                                 ctypes.cast(ev5, ctypes.c_void_p)) == B.ERR_INVALID_ARGUMENT
+    assert lib.attnqat_bwd_timed(ctypes.byref(p), *a[:9], a[9], need, None, None) == \
+        B.ERR_INVALID_ARGUMENT
+    buf, out = _vp(0x20000), _vp(0x40000)
+    # issue mix: mode, FMAs per slot, threads, split mode only with 512 threads, null input
+    for args in [(4, 8, 0, buf, out, 1, 256, 1), (0, 12, 0, buf, out, 1, 256, 1),
+                 (0, 8, 0, buf, out, 1, 128, 1), (3, 8, 0, buf, out, 1, 256, 1),
+                 (0, 8, 0, None, out, 1, 256, 1), (0, 8, 0, buf, out, 0, 256, 1),
+                 (0, 8, 0, buf, out, 1, 256, 0)]:
+        assert lib.attnqat_probe_issue_mix(*args, None) == B.ERR_INVALID_ARGUMENT, args
+    assert lib.attnqat_probe_issue_mix(0, 8, 0, _vp(0x20004), out, 1, 256, 1, None) == \
+        B.ERR_MISALIGNED
+    # LDS write patterns 0..5
+    for args in [(6, out, 1, 1), (-1, out, 1, 1), (0, None, 1, 1), (0, out, 0, 1),
+                 (0, out, 1, 1 << 21)]:
+        assert lib.attnqat_probe_lds_write(*args, None) == B.ERR_INVALID_ARGUMENT, args
+    assert lib.attnqat_probe_lds_write(0, _vp(0x40008), 1, 1, None) == B.ERR_MISALIGNED
