@@ -58,7 +58,7 @@ constexpr int kRing = 4;       // Q^/dO sub-tile slots (also the unroll factor)
 #define ATTNQAT_DKDV_AHEAD 2
 #endif
 #ifndef ATTNQAT_DKDV_AHEAD_Y
-#define ATTNQAT_DKDV_AHEAD_Y 4
+#define ATTNQAT_DKDV_AHEAD_Y 6
 #endif
 #ifndef ATTNQAT_DKDV_SGB
 #define ATTNQAT_DKDV_SGB 1
