@@ -351,6 +351,67 @@ def run_probes(reps=5):
     return {"issue_mix": mix, "lds_write": lds}
 
 
+def fwd_split_study(nq_list=(1, 16, 64, 128), nkv=65536, heads=16, d=128, reps=10):
+    """Few queries against long K/V (the forward's split over keys), from
+    bf16 K/V and from packed NVFP4 K/V (one JSON line).  Per query count:
+    the forward from bf16 K/V (its attention launches alone, and the whole
+    call with the Q/K/V fake-quant), the forward from packed K/V (whole call:
+    Q fake-quant and attention), and the K/V bytes each attention pass reads."""
+    import torch
+
+    from nvfp4_fake_quantized_amd import binding as B
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    hip = HipEvents()
+    g = torch.Generator(device="cpu").manual_seed(11)
+    k = torch.randn(1, heads, nkv, d, generator=g).to(torch.bfloat16).to(dev)
+    v = torch.randn(1, heads, nkv, d, generator=g).to(torch.bfloat16).to(dev)
+    kc, ks = B.attnqat_nvfp4_pack(k)
+    vc, vs = B.attnqat_nvfp4_pack(v)
+    kv_bf16 = 2 * heads * nkv * d * 2
+    kv_packed = 2 * heads * nkv * (d // 2 + d // 16)
+    rows = []
+    for nq in nq_list:
+        q = torch.randn(1, heads, nq, d, generator=g).to(torch.bfloat16).to(dev)
+        p = B.problem_for(q, k, False, d ** -0.5)
+        ws = torch.empty(B.attnqat_fwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+        def med(fn, nev):
+            fn(hip.array(nev))
+            evs = [hip.array(nev) for _ in range(reps)]
+            for e in evs:
+                fn(e)
+            torch.cuda.synchronize()
+            return evs
+
+        evt = med(lambda e: B.attnqat_fwd_timed(p, q, k, v, o, lse, ws, e, stream), 4)
+        attn_bf16 = _stats([hip.ms(e[2], e[3]) for e in evt])["median"]
+        call_bf16 = _stats([hip.ms(e[0], e[3]) for e in evt])["median"]
+
+        def packed(e):
+            hip.record(e[0], stream)
+            B.attnqat_fwd_packed(p, q, kc, ks, vc, vs, o, lse, ws, stream)
+            hip.record(e[1], stream)
+        evp = med(packed, 2)
+        call_packed = _stats([hip.ms(e[0], e[1]) for e in evp])["median"]
+        flops = 4.0 * heads * nq * nkv * d
+        rows.append({"nq": nq, "nkv": nkv, "heads": heads, "head_dim": d,
+                     "attention_bf16_kv_ms": attn_bf16, "call_bf16_kv_ms": call_bf16,
+                     "call_packed_kv_ms": call_packed,
+                     "speedup_packed_vs_bf16_attention": round(attn_bf16 / call_packed, 2),
+                     "kv_bytes_bf16": kv_bf16, "kv_bytes_packed": kv_packed,
+                     "kv_read_rate_bf16_gbs": round(kv_bf16 / (attn_bf16 * 1e-3) / 1e9, 1),
+                     "kv_read_rate_packed_gbs": round(kv_packed / (call_packed * 1e-3) / 1e9, 1),
+                     "tflops_packed": round(flops / (call_packed * 1e-3) / 1e12, 1)})
+        log(f"  Nq {nq:4d} x Nkv {nkv}: attention from bf16 K^/V^ {attn_bf16:.4f} ms "
+            f"(whole call with K/V fake-quant {call_bf16:.4f} ms), from packed K/V "
+            f"{call_packed:.4f} ms: x{attn_bf16 / call_packed:.2f}")
+    hip.close()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,6 +433,9 @@ def main():
     ap.add_argument("--p-scale-study", action="store_true",
                     help="instead of the benchmark, print the p_scale gradient-quality study "
                          "(one JSON line)")
+    ap.add_argument("--fwd-split-study", action="store_true",
+                    help="instead of the benchmark, time the forward for few queries against "
+                         "long K/V from bf16 and from packed NVFP4 K/V (one JSON line)")
     ap.add_argument("--probes", action="store_true",
                     help="instead of the benchmark, run the MFMA/VALU issue-mix and LDS "
                          "write-pattern probes (one JSON line)")
@@ -386,6 +450,9 @@ def main():
         return
     if args.probes:
         print(json.dumps({"probes": run_probes()}), flush=True)
+        return
+    if args.fwd_split_study:
+        print(json.dumps({"fwd_split_study": fwd_split_study()}), flush=True)
         return
 
     import torch

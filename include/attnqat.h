@@ -152,7 +152,14 @@ ATTNQAT_API int attnqat_nvfp4_pack(const void* x, uint8_t* codes, uint8_t* scale
  * quantization; lse its natural-log log-sum-exp).
  * In: q (B,H,Nq,D), k, v (B,H,Nkv,D) bf16.  Out: o_hp (B,H,Nq,D) bf16,
  * lse (B,H,Nq) fp32.  The workspace (>= attnqat_fwd_workspace_bytes) holds
- * Q^/K^/V^ and their scales afterwards (attnqat_workspace_layout). */
+ * Q^/K^/V^ and their scales afterwards (attnqat_workspace_layout).
+ * Few queries against long K/V: when the problem is non-causal and its
+ * 128-query tiles over all heads number fewer than 256, the keys are split
+ * over workgroups (splits = min(ceil(512 / tiles), key tiles of 32 / 4),
+ * used when >= 2) and a second launch merges the splits; the workspace
+ * size then includes the partial results (B*H*Nq*splits*(4*D + 8) bytes,
+ * after the parts named by attnqat_workspace_layout).  The results are the
+ * same forward up to the fp32 rounding order. */
 ATTNQAT_API int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k,
                             const void* v, void* o_hp, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
@@ -164,8 +171,11 @@ ATTNQAT_API int attnqat_fwd(const attnqat_problem* p, const void* q, const void*
  * from the same K^/V^ values (equal up to the fp32 rounding order of the
  * softmax sums) on the K and V the codes were made from.  q is fake-quantized
  * as in attnqat_fwd (the workspace holds Q^ and its scales afterwards; its
- * K^/V^ parts are not written).  q, the code arrays, o_hp, lse and the
- * workspace 16-byte aligned; errors as attnqat_fwd. */
+ * K^/V^ parts are not written).  Splits the keys as attnqat_fwd does.  With
+ * few queries against long K/V, where the forward reads mostly K and V, the
+ * packed storage moves 72 instead of 256 bytes per key and head at D = 128.
+ * q, the code arrays, o_hp, lse and the workspace 16-byte aligned; errors
+ * as attnqat_fwd. */
 ATTNQAT_API int attnqat_fwd_packed(const attnqat_problem* p, const void* q,
                                    const uint8_t* k_codes, const uint8_t* k_scales,
                                    const uint8_t* v_codes, const uint8_t* v_scales, void* o_hp,

@@ -313,7 +313,8 @@ def attnqat_bwd_noalloc(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv,
 
 
 def attnqat_fwd_timed(p: attnqat_problem, q, k, v, o_hp, lse, workspace, events, stream=None):
-    """``events``: a ctypes array of 3 hipEvent_t handles (attnqat_instrument.h)."""
+    """``events``: a ctypes array of 4 hipEvent_t handles, a start/stop pair
+    per launch (attnqat_instrument.h)."""
     _check_attention(p, q, k, v, o_hp=o_hp, lse=lse, workspace=workspace)
     _check(_lib.attnqat_fwd_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),
                                   _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream),
@@ -322,7 +323,8 @@ def attnqat_fwd_timed(p: attnqat_problem, q, k, v, o_hp, lse, workspace, events,
 
 def attnqat_fwd_quantized_timed(p: attnqat_problem, q, k, v, o_hp, lse, o, workspace, events,
                                 stream=None):
-    """``events``: a ctypes array of 4 hipEvent_t handles (attnqat_instrument.h)."""
+    """``events``: a ctypes array of 6 hipEvent_t handles, a start/stop pair
+    per launch (attnqat_instrument.h)."""
     _check_attention(p, q, k, v, o_hp=o_hp, lse=lse, o=o, workspace=workspace)
     _check(_lib.attnqat_fwd_quantized_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(o_hp), _ptr(lse), _ptr(o), _ptr(workspace),
@@ -332,7 +334,8 @@ def attnqat_fwd_quantized_timed(p: attnqat_problem, q, k, v, o_hp, lse, o, works
 
 def attnqat_bwd_timed(p: attnqat_problem, q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace,
                       events, stream=None):
-    """``events``: a ctypes array of 5 hipEvent_t handles (attnqat_instrument.h)."""
+    """``events``: a ctypes array of 6 hipEvent_t handles, a start/stop pair
+    per launch (attnqat_instrument.h)."""
     _check_attention(p, q, k, v, o_hp=o_hp, d_o=d_o, lse=lse, dq=dq, dk=dk, dv=dv,
                      workspace=workspace)
     _check(_lib.attnqat_bwd_timed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_hp),

@@ -45,8 +45,25 @@ int validate_problem(const attnqat_problem* p) {
 }
 
 struct Layout {
-  size_t q_hat, k_hat, v_hat, q_scale, k_scale, v_scale, delta, total;
+  size_t q_hat, k_hat, v_hat, q_scale, k_scale, v_scale, delta, o_part, ml_part, total;
+  int kv_splits;
 };
+
+// Key splits of the forward.  When the query tiles (128 queries each) of all
+// heads cannot fill the chip's 256 CUs and the problem is non-causal -- few
+// queries against long K/V -- the keys are split so that about 512
+// workgroups run, with at least 4 key tiles (128 keys) per split; the
+// partial results (unnormalized O in fp32, row max and sum) take
+// bh * splits * Nq * (4 D + 8) bytes of the forward workspace.
+int fwd_kv_splits(const attnqat_problem* p) {
+  if (p->causal) return 1;
+  const int64_t wgs = (int64_t)p->batch * p->heads * ((p->seqlen_q + 127) / 128);
+  if (wgs >= 256) return 1;
+  const int64_t ktiles = ((int64_t)p->seqlen_kv + 31) / 32;
+  const int64_t want = (512 + wgs - 1) / wgs;
+  const int64_t s = want < ktiles / 4 ? want : ktiles / 4;
+  return s >= 2 ? (int)s : 1;
+}
 
 Layout make_layout(const attnqat_problem* p, bool bwd) {
   const size_t bh = (size_t)p->batch * p->heads;
@@ -60,11 +77,20 @@ Layout make_layout(const attnqat_problem* p, bool bwd) {
   L.q_scale = off; off = align_up(off + nq * D / 16);
   L.k_scale = off; off = align_up(off + nkv * D / 16);
   L.v_scale = off; off = align_up(off + nkv * D / 16);
+  L.o_part = L.ml_part = SIZE_MAX;
+  L.kv_splits = 1;
   if (bwd) {
     L.delta = off;
     off = align_up(off + nq * 4);
   } else {
     L.delta = SIZE_MAX;
+    L.kv_splits = fwd_kv_splits(p);
+    if (L.kv_splits > 1) {
+      L.o_part = off;
+      off = align_up(off + nq * L.kv_splits * D * 4);
+      L.ml_part = off;
+      off = align_up(off + nq * L.kv_splits * 8);
+    }
   }
   L.total = off;
   return L;
@@ -233,6 +259,11 @@ int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   a.causal = p->causal;
   a.softmax_scale = p->softmax_scale;
   a.p_scale = p->p_scale;
+  a.kv_splits = L.kv_splits;
+  if (L.kv_splits > 1) {
+    a.o_part = at<float>(workspace, L.o_part);
+    a.ml_part = at<float>(workspace, L.ml_part);
+  }
   if (attnqat::launch_fwd(a, p->head_dim, stream, timing(ev, 1)) != hipSuccess)
     return ATTNQAT_ERR_HIP;
   if (with_o) {
@@ -280,6 +311,11 @@ int run_fwd_packed(const attnqat_problem* p, const void* q, const uint8_t* k_cod
   a.causal = p->causal;
   a.softmax_scale = p->softmax_scale;
   a.p_scale = p->p_scale;
+  a.kv_splits = L.kv_splits;
+  if (L.kv_splits > 1) {
+    a.o_part = at<float>(workspace, L.o_part);
+    a.ml_part = at<float>(workspace, L.ml_part);
+  }
   if (attnqat::launch_fwd_packed(a, p->head_dim, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
   return ATTNQAT_OK;
 }

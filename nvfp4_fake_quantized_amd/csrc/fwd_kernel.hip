@@ -27,7 +27,11 @@
 //  * causal: tiles with every key above the wave's last query are skipped
 //    (and the key loop ends at the workgroup's last query); the diagonal
 //    tile keeps the elementwise key <= query mask; keys >= Nkv are masked
-//    and rows >= Nq are never stored (non-aligned tails).
+//    and rows >= Nq are never stored (non-aligned tails);
+//  * split over keys (non-causal, when the query tiles alone cannot fill the
+//    chip: few queries against long K/V): blockIdx.y picks a run of key
+//    tiles; each split stores its unnormalized O^T (fp32) with its row max
+//    and sum, and k_fwd_combine merges the splits into O_hp and lse.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -168,9 +172,10 @@ __device__ __forceinline__ void fwd_softmax_pv(const f32x16& s, float& m, float&
   m = mnew;
 }
 
-template <int D, bool CAUSAL, bool PACKED>
+template <int D, bool CAUSAL, bool PACKED, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_FWD_WAVES, 8)))
 void k_fwd(AttnArgs a) {
+  static_assert(!(CAUSAL && SPLIT), "the split over keys is for non-causal attention");
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int BN = 32;              // keys per tile
@@ -208,7 +213,13 @@ void k_fwd(AttnArgs a) {
   const RowOffsets<D> ro(lane);
   const ColOffsets<D> co(4 * h, 4 * h + 8, lane);
   const int kend = CAUSAL ? min(nkv, qblk0 + kFwdBM) : nkv;
-  const int ntiles = (kend + BN - 1) / BN;
+  // key tiles t0 .. t0 + ntiles - 1 (all of them unless split over keys)
+  int t0 = 0, ntiles = (kend + BN - 1) / BN;
+  if constexpr (SPLIT) {
+    const int per = (ntiles + a.kv_splits - 1) / a.kv_splits;
+    t0 = (int)blockIdx.y * per;
+    ntiles = max(0, min(ntiles, t0 + per) - t0);
+  }
 
   // K^/V^ tiles go global -> LDS directly. Copy instruction c of this wave
   // fills LDS chunk slots 64*(CH*wave + c) + lane; slot (row r, position j)
@@ -220,7 +231,7 @@ void k_fwd(AttnArgs a) {
     goff[c] = (uint32_t)swz<D>(p / CPR, 8 * (p % CPR)) * 2u;
   }
   auto issue_tile = [&](int it) __attribute__((always_inline)) {
-    const int k0 = it * BN;
+    const int k0 = (t0 + it) * BN;
     const int buf = it % NB;
     // rows past nkv arrive as zeros (masked out later)
     const uint32_t bytes = (uint32_t)(min(nkv - k0, BN) * D) * 2u;
@@ -249,7 +260,7 @@ void k_fwd(AttnArgs a) {
   u32x2 pkc = {0u, 0u}, pvc = {0u, 0u};
   uint32_t pks = 0u, pvs = 0u;
   auto load_packed = [&](int it) __attribute__((always_inline)) {
-    const int k0 = it * BN;
+    const int k0 = (t0 + it) * BN;
     const int rows = min(nkv - k0, BN);  // rows past nkv read as zeros
     const auto rkc = make_rsrc(KC + (size_t)k0 * (D / 2), (uint32_t)rows * (D / 2));
     const auto rvc = make_rsrc(VC + (size_t)k0 * (D / 2), (uint32_t)rows * (D / 2));
@@ -281,7 +292,7 @@ void k_fwd(AttnArgs a) {
 
   // Leading tiles are interior (branch-free); masks start at the first tile
   // that reaches past nkv or above the workgroup's first query (causal).
-  int it_hi = min(ntiles, nkv / BN);
+  int it_hi = min(ntiles, max(0, nkv / BN - t0));
   if (CAUSAL) it_hi = min(it_hi, (qblk0 + 1) / BN);
 
   if constexpr (PACKED) {
@@ -305,7 +316,7 @@ void k_fwd(AttnArgs a) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = it % NB;
     const int pbuf = (it + NB - 1) % NB;
-    const int k0 = it * BN;
+    const int k0 = (t0 + it) * BN;
     if constexpr (!PACKED) {
       if (it + 2 < ntiles) issue_tile(it + 2);
     }
@@ -357,6 +368,25 @@ void k_fwd(AttnArgs a) {
   }
 
   const float lt = l + xor32(l);
+  if constexpr (SPLIT) {
+    // this split's unnormalized O^T row, its max (log2 units) and its sum;
+    // a split without keys stores m = -inf, l = 0 and O = 0
+    if (qi < nq) {
+      const size_t row = ((size_t)bh * a.kv_splits + blockIdx.y) * nq + qi;
+      float* op = a.o_part + row * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 w = {o[db][4 * g4], o[db][4 * g4 + 1], o[db][4 * g4 + 2],
+                           o[db][4 * g4 + 3]};
+          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * g4 + 4 * h) = w;
+        }
+      }
+      if (h == 0) *reinterpret_cast<f32x2*>(a.ml_part + 2 * row) = f32x2{m, lt};
+    }
+    return;
+  }
   if (qi < nq) {
     const float inv = 1.0f / lt;
     uint16_t* O = a.o_hp + (size_t)bh * nq * D + (size_t)qi * D;
@@ -373,17 +403,74 @@ void k_fwd(AttnArgs a) {
   }
 }
 
+// Merge of the key splits of k_fwd<..., SPLIT>: per query row, with M the
+// largest split max and w_s = exp2(m_s - M), O_hp = sum_s w_s O_s / L and
+// lse = (M + log2 L) ln 2, L = sum_s w_s l_s.  One thread per 4 columns of a
+// row (D/4 threads per row); the splits are visited in order.
+template <int D>
+__global__ __launch_bounds__(256) void k_fwd_combine(AttnArgs a, int64_t rows) {
+  constexpr int TPR = D / 4;  // threads per row
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = g / TPR;  // bh * nq + q
+  if (row >= rows) return;
+  const int c4 = (int)(g % TPR);
+  const int S = a.kv_splits;
+  const int64_t bh = row / a.nq, q = row % a.nq;
+  const float* ml = a.ml_part + ((size_t)bh * S * a.nq + q) * 2;
+  const size_t sstride = (size_t)a.nq * 2;  // split stride in ml_part
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s * sstride]);
+  const float base = M == -INFINITY ? 0.0f : M;
+  const float* op = a.o_part + ((size_t)bh * S * a.nq + q) * D + 4 * c4;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float L = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const f32x2 mls = *reinterpret_cast<const f32x2*>(ml + s * sstride);
+    const float w = fast_exp2(mls[0] - base);
+    L = __builtin_fmaf(w, mls[1], L);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(op + (size_t)s * a.nq * D);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
+  }
+  const float inv = 1.0f / L;
+  uint16_t* O = a.o_hp + (size_t)row * D + 4 * c4;
+  *reinterpret_cast<u32x2*>(O) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                       pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (c4 == 0) a.lse_out[row] = (M + __builtin_log2f(L)) * kLn2;
+}
+
 }  // namespace
 
 template <bool PACKED>
 hipError_t launch_fwd_t(const AttnArgs& a, int head_dim, hipStream_t stream,
                         const LaunchEvents* ev) {
-  const dim3 grid((unsigned)(((a.nq + kFwdBM - 1) / kFwdBM) * a.bh)), block(256);
+  const unsigned qtiles = (unsigned)(((a.nq + kFwdBM - 1) / kFwdBM) * a.bh);
+  const dim3 block(256);
+  if (a.kv_splits > 1 && !a.causal) {
+    // split over keys, then the merge (timed as one span: start of the
+    // first launch to the end of the second)
+    const dim3 grid(qtiles, (unsigned)a.kv_splits);
+    const LaunchEvents e0 = {ev ? ev->start : nullptr, nullptr};
+    const LaunchEvents e1 = {nullptr, ev ? ev->stop : nullptr};
+    const hipError_t st = head_dim == 128
+                              ? launch(k_fwd<128, false, PACKED, true>, grid, block, stream,
+                                       ev ? &e0 : nullptr, a)
+                              : launch(k_fwd<64, false, PACKED, true>, grid, block, stream,
+                                       ev ? &e0 : nullptr, a);
+    if (st != hipSuccess) return st;
+    const int64_t rows = (int64_t)a.bh * a.nq;
+    const int64_t threads = rows * (head_dim / 4);
+    const dim3 cgrid((unsigned)((threads + 255) / 256));
+    return head_dim == 128
+               ? launch(k_fwd_combine<128>, cgrid, block, stream, ev ? &e1 : nullptr, a, rows)
+               : launch(k_fwd_combine<64>, cgrid, block, stream, ev ? &e1 : nullptr, a, rows);
+  }
+  const dim3 grid(qtiles);
   if (head_dim == 128)
-    return a.causal ? launch(k_fwd<128, true, PACKED>, grid, block, stream, ev, a)
-                    : launch(k_fwd<128, false, PACKED>, grid, block, stream, ev, a);
-  return a.causal ? launch(k_fwd<64, true, PACKED>, grid, block, stream, ev, a)
-                  : launch(k_fwd<64, false, PACKED>, grid, block, stream, ev, a);
+    return a.causal ? launch(k_fwd<128, true, PACKED, false>, grid, block, stream, ev, a)
+                    : launch(k_fwd<128, false, PACKED, false>, grid, block, stream, ev, a);
+  return a.causal ? launch(k_fwd<64, true, PACKED, false>, grid, block, stream, ev, a)
+                  : launch(k_fwd<64, false, PACKED, false>, grid, block, stream, ev, a);
 }
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream,

@@ -60,6 +60,11 @@ struct AttnArgs {
   const uint8_t* k_scales;  // (BH, nkv, D/16)
   const uint8_t* v_codes;
   const uint8_t* v_scales;
+  // forward split over keys (kv_splits > 1): per split, unnormalized O^T
+  // (fp32) and the row max and sum, merged by a second kernel
+  float* o_part;          // (BH, kv_splits, nq, D)
+  float* ml_part;         // (BH, kv_splits, nq, 2): max (log2 units), sum
+  int kv_splits;          // 0 or 1: no split
   int bh;                 // batch * heads
   int nq, nkv;
   int causal;
