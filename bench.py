@@ -351,9 +351,10 @@ def run_probes(reps=5):
     return {"issue_mix": mix, "lds_write": lds}
 
 
-def fwd_split_study(nq_list=(1, 16, 64, 128), nkv=65536, heads=16, d=128, reps=10):
-    """Few queries against long K/V (the forward's split over keys), from
-    bf16 K/V and from packed NVFP4 K/V (one JSON line).  Per query count:
+def fwd_split_study(nq_list=(1, 8, 16, 32, 64, 128), nkv=65536, heads=16, d=128, reps=20):
+    """Few queries against long K/V (32-query tiles up to 32 queries, the
+    split over keys above), from bf16 K/V and from packed NVFP4 K/V (one JSON
+    line).  Per query count:
     the forward from bf16 K/V (its attention launches alone, and the whole
     call with the Q/K/V fake-quant), the forward from packed K/V (whole call:
     Q fake-quant and attention), and the K/V bytes each attention pass reads."""

@@ -153,26 +153,33 @@ ATTNQAT_API int attnqat_nvfp4_pack(const void* x, uint8_t* codes, uint8_t* scale
  * In: q (B,H,Nq,D), k, v (B,H,Nkv,D) bf16.  Out: o_hp (B,H,Nq,D) bf16,
  * lse (B,H,Nq) fp32.  The workspace (>= attnqat_fwd_workspace_bytes) holds
  * Q^/K^/V^ and their scales afterwards (attnqat_workspace_layout).
- * Few queries against long K/V: when the problem is non-causal and its
- * 128-query tiles over all heads number fewer than 256, the keys are split
- * over workgroups (splits = min(ceil(512 / tiles), key tiles of 32 / 4),
- * used when >= 2) and a second launch merges the splits; the workspace
- * size then includes the partial results (B*H*Nq*splits*(4*D + 8) bytes,
- * after the parts named by attnqat_workspace_layout).  The results are the
- * same forward up to the fp32 rounding order. */
+ * Few queries against long K/V (non-causal only): with at most 32 queries
+ * per head, a kernel with 32-query tiles deals the key tiles of each head
+ * out to `splits` = min(ceil(512 / (B*H)), max(1, key tiles of 32 / 8))
+ * workgroups; otherwise, when the 128-query tiles over all heads number
+ * fewer than 256, the keys are split over workgroups (splits =
+ * min(ceil(512 / tiles), key tiles / 4), used when >= 2).  Either way a
+ * second launch merges the partial results, and the workspace size then
+ * includes them (B*H*Nq*splits*(4*D + 8) bytes, after the parts named by
+ * attnqat_workspace_layout).  The results are the same forward up to the
+ * fp32 rounding order. */
 ATTNQAT_API int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k,
                             const void* v, void* o_hp, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
 /* attnqat_fwd with K^ and V^ given in packed NVFP4 storage (for instance a
  * cache written by attnqat_nvfp4_pack): k_codes, v_codes (B,H,Nkv,D/2) and
- * k_scales, v_scales (B,H,Nkv,D/16).  The kernel dequantizes them to bf16
- * exactly while staging its tiles, so it computes attnqat_fwd's o_hp and lse
- * from the same K^/V^ values (equal up to the fp32 rounding order of the
- * softmax sums) on the K and V the codes were made from.  q is fake-quantized
- * as in attnqat_fwd (the workspace holds Q^ and its scales afterwards; its
- * K^/V^ parts are not written).  Splits the keys as attnqat_fwd does.  With
- * few queries against long K/V, where the forward reads mostly K and V, the
+ * k_scales, v_scales (B,H,Nkv,D/16).  The kernels dequantize them exactly
+ * (to bf16, or to fp16 with at most 32 queries per head, where Q^, K^ and
+ * V^ are multiplied in fp16: every E2M1 code times an E4M3 scale is exact
+ * in both), so they compute attnqat_fwd's o_hp and lse from the same K^/V^
+ * values on the K and V the codes were made from: lse equal up to the fp32
+ * rounding order, o_hp too, except that with at most 32 queries per head
+ * the probabilities enter P V^ rounded to fp16 instead of bf16 (o_hp then
+ * differs by up to that bf16 rounding).  q is fake-quantized as in
+ * attnqat_fwd (the workspace holds Q^ and its scales afterwards; its K^/V^
+ * parts are not written).  Covers the keys as attnqat_fwd does.  With few
+ * queries against long K/V, where the forward reads mostly K and V, the
  * packed storage moves 72 instead of 256 bytes per key and head at D = 128.
  * q, the code arrays, o_hp, lse and the workspace 16-byte aligned; errors
  * as attnqat_fwd. */

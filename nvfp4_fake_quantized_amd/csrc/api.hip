@@ -47,22 +47,38 @@ int validate_problem(const attnqat_problem* p) {
 struct Layout {
   size_t q_hat, k_hat, v_hat, q_scale, k_scale, v_scale, delta, o_part, ml_part, total;
   int kv_splits;
+  int kv_decode;
 };
 
-// Key splits of the forward.  When the query tiles (128 queries each) of all
-// heads cannot fill the chip's 256 CUs and the problem is non-causal -- few
-// queries against long K/V -- the keys are split so that about 512
-// workgroups run, with at least 4 key tiles (128 keys) per split; the
-// partial results (unnormalized O in fp32, row max and sum) take
-// bh * splits * Nq * (4 D + 8) bytes of the forward workspace.
-int fwd_kv_splits(const attnqat_problem* p) {
-  if (p->causal) return 1;
-  const int64_t wgs = (int64_t)p->batch * p->heads * ((p->seqlen_q + 127) / 128);
-  if (wgs >= 256) return 1;
+// How the forward covers the keys (non-causal problems only; a causal
+// forward always runs one workgroup per 128 queries over all its keys):
+//  * at most 32 queries per head: the 32-query-tile forward, its key tiles
+//    dealt out to `splits` workgroups of 4 waves per head, enough for about
+//    512 workgroups (two per CU) with at least 2 key tiles (64 keys) per
+//    wave;
+//  * otherwise, when the 128-query tiles of all heads cannot fill the chip's
+//    256 CUs: the keys are split so that about 512 workgroups run, with at
+//    least 4 key tiles (128 keys) per split;
+// Both write per-run partial results (unnormalized O in fp32, row max and
+// sum) of bh * splits * Nq * (4 D + 8) bytes to the forward workspace.
+struct FwdPlan {
+  int splits;
+  int decode;
+};
+FwdPlan fwd_plan(const attnqat_problem* p) {
+  if (p->causal) return {1, 0};
+  const int64_t bh = (int64_t)p->batch * p->heads;
   const int64_t ktiles = ((int64_t)p->seqlen_kv + 31) / 32;
+  if (p->seqlen_q <= 32) {
+    const int64_t want = (512 + bh - 1) / bh;
+    const int64_t cap = ktiles / 8 > 1 ? ktiles / 8 : 1;
+    return {(int)(want < cap ? want : cap), 1};
+  }
+  const int64_t wgs = bh * ((p->seqlen_q + 127) / 128);
+  if (wgs >= 256) return {1, 0};
   const int64_t want = (512 + wgs - 1) / wgs;
   const int64_t s = want < ktiles / 4 ? want : ktiles / 4;
-  return s >= 2 ? (int)s : 1;
+  return {s >= 2 ? (int)s : 1, 0};
 }
 
 Layout make_layout(const attnqat_problem* p, bool bwd) {
@@ -79,13 +95,16 @@ Layout make_layout(const attnqat_problem* p, bool bwd) {
   L.v_scale = off; off = align_up(off + nkv * D / 16);
   L.o_part = L.ml_part = SIZE_MAX;
   L.kv_splits = 1;
+  L.kv_decode = 0;
   if (bwd) {
     L.delta = off;
     off = align_up(off + nq * 4);
   } else {
     L.delta = SIZE_MAX;
-    L.kv_splits = fwd_kv_splits(p);
-    if (L.kv_splits > 1) {
+    const FwdPlan plan = fwd_plan(p);
+    L.kv_splits = plan.splits;
+    L.kv_decode = plan.decode;
+    if (L.kv_splits > 1 || L.kv_decode) {
       L.o_part = off;
       off = align_up(off + nq * L.kv_splits * D * 4);
       L.ml_part = off;
@@ -260,7 +279,8 @@ int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   a.softmax_scale = p->softmax_scale;
   a.p_scale = p->p_scale;
   a.kv_splits = L.kv_splits;
-  if (L.kv_splits > 1) {
+  a.kv_decode = L.kv_decode;
+  if (L.kv_splits > 1 || L.kv_decode) {
     a.o_part = at<float>(workspace, L.o_part);
     a.ml_part = at<float>(workspace, L.ml_part);
   }
@@ -312,7 +332,8 @@ int run_fwd_packed(const attnqat_problem* p, const void* q, const uint8_t* k_cod
   a.softmax_scale = p->softmax_scale;
   a.p_scale = p->p_scale;
   a.kv_splits = L.kv_splits;
-  if (L.kv_splits > 1) {
+  a.kv_decode = L.kv_decode;
+  if (L.kv_splits > 1 || L.kv_decode) {
     a.o_part = at<float>(workspace, L.o_part);
     a.ml_part = at<float>(workspace, L.ml_part);
   }

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace attnqat {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -69,6 +71,21 @@ template <bool B>
 struct BoolTag {
   static constexpr bool value = B;
 };
+
+// Compile-time integer carried through generic lambdas, and a loop whose
+// body sees its index as one (f(IntTag<0>()), ..., f(IntTag<N-1>())).
+template <int N>
+struct IntTag {
+  static constexpr int value = N;
+};
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(IntTag<I>()), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {

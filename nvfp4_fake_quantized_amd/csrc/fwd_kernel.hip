@@ -403,13 +403,15 @@ void k_fwd(AttnArgs a) {
   }
 }
 
-// Merge of the key splits of k_fwd<..., SPLIT>: per query row, with M the
-// largest split max and w_s = exp2(m_s - M), O_hp = sum_s w_s O_s / L and
-// lse = (M + log2 L) ln 2, L = sum_s w_s l_s.  One thread per 4 columns of a
-// row (D/4 threads per row); the splits are visited in order.
+// Merge of the key runs of k_fwd<..., SPLIT> and k_fwd_dec: per query row,
+// with M the largest run max and w_s = exp2(m_s - M), O_hp = sum_s w_s O_s / L
+// and lse = (M + log2 L) ln 2, L = sum_s w_s l_s.  One thread per 4 columns
+// of a row (D/4 threads per row); the runs are read 8 at a time (their loads
+// in flight together) and folded into a running max with rescaled sums.
 template <int D>
 __global__ __launch_bounds__(256) void k_fwd_combine(AttnArgs a, int64_t rows) {
   constexpr int TPR = D / 4;  // threads per row
+  constexpr int B8 = 8;       // runs per batch
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = g / TPR;  // bh * nq + q
   if (row >= rows) return;
@@ -417,26 +419,441 @@ __global__ __launch_bounds__(256) void k_fwd_combine(AttnArgs a, int64_t rows) {
   const int S = a.kv_splits;
   const int64_t bh = row / a.nq, q = row % a.nq;
   const float* ml = a.ml_part + ((size_t)bh * S * a.nq + q) * 2;
-  const size_t sstride = (size_t)a.nq * 2;  // split stride in ml_part
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s * sstride]);
-  const float base = M == -INFINITY ? 0.0f : M;
+  const size_t sstride = (size_t)a.nq * 2;  // run stride in ml_part
   const float* op = a.o_part + ((size_t)bh * S * a.nq + q) * D + 4 * c4;
+  float M = -INFINITY, L = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  float L = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const f32x2 mls = *reinterpret_cast<const f32x2*>(ml + s * sstride);
-    const float w = fast_exp2(mls[0] - base);
-    L = __builtin_fmaf(w, mls[1], L);
-    const f32x4 v = *reinterpret_cast<const f32x4*>(op + (size_t)s * a.nq * D);
+  for (int s0 = 0; s0 < S; s0 += B8) {
+    f32x2 mls[B8];
+    f32x4 v[B8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
+    for (int k = 0; k < B8; ++k) {
+      const bool in = s0 + k < S;
+      mls[k] = in ? *reinterpret_cast<const f32x2*>(ml + (s0 + k) * sstride) : f32x2{-INFINITY, 0.0f};
+      v[k] = in ? *reinterpret_cast<const f32x4*>(op + (size_t)(s0 + k) * a.nq * D)
+                : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float bm = M;
+#pragma unroll
+    for (int k = 0; k < B8; ++k) bm = fmaxf(bm, mls[k][0]);
+    const float base = bm == -INFINITY ? 0.0f : bm;
+    const float r = fast_exp2(M - base);  // 0 while M is -inf (L and acc are 0 then)
+    L *= r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= r;
+#pragma unroll
+    for (int k = 0; k < B8; ++k) {
+      const float w = fast_exp2(mls[k][0] - base);
+      L = __builtin_fmaf(w, mls[k][1], L);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, v[k][e], acc[e]);
+    }
+    M = bm;
   }
   const float inv = 1.0f / L;
   uint16_t* O = a.o_hp + (size_t)row * D + 4 * c4;
   *reinterpret_cast<u32x2*>(O) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
                                        pack_bf16x2(acc[2] * inv, acc[3] * inv)};
   if (c4 == 0) a.lse_out[row] = (M + __builtin_log2f(L)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Forward for few queries against long K/V (non-causal, Nq <= 32 per head):
+// the same QAT forward with 32-query tiles, so that a decode-like problem
+// does not compute 128-query tiles that are mostly padding, and so that the
+// K/V stream (bf16 or packed NVFP4) is what bounds it.
+//  * a workgroup of 4 waves owns 32 queries of one head; its waves work on
+//    their own (no barrier in the key loop).  The W = 4 * splits waves of a
+//    head deal the key tiles out round-robin (wave g takes tiles g, g + W,
+//    ...), so that at any time the waves of a head stream neighbouring tiles
+//    (DRAM pages stay open) rather than W distant runs; each wave visits its
+//    tiles from the last one down, so the only partial tile of the head
+//    comes first and only that step evaluates a mask;
+//  * the workgroup's Q^ rows sit in LDS and are read as the B operand of
+//    S^T = K^ Q^T;
+//  * bf16 K^ rows go global -> registers (A operands) one tile ahead, V^
+//    tiles global -> LDS directly one tile ahead;
+//  * packed K^/V^: codes and scale bytes of two tiles ahead in registers,
+//    dequantized to fp16 (exact: see dec_scale) and multiplied on fp16 MFMAs
+//    (Q^ staged in fp16, also exact; P^T rounded to fp16, finer than the bf16
+//    of the other paths).  K^ operands are dequantized beside the S^T MFMAs
+//    (the head dimension is split between the lane halves as h*D/2 + 8j + e
+//    for MFMA j, the order of a dot product's terms being free, so that a
+//    lane's codes of a key row are one contiguous run); V^ is dequantized
+//    beside the O^T MFMAs of the previous tile and written with 16-byte
+//    stores whose rows are chosen so that each group of 8 lanes hits 8
+//    different bank groups;
+//  * V^ is read from a per-wave pair of LDS tiles in the swizzled layout of
+//    k_fwd with transpose reads;
+//  * at the end the 4 waves are merged in LDS (max over the waves,
+//    exp2-weighted sums) into one unnormalized partial (O, row max, row sum)
+//    per workgroup, which k_fwd_combine merges over the workgroups.
+constexpr int kDecBQ = 32;  // queries per workgroup
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Every E2M1 code times an E4M3 scale is exact in fp16 (at most 6
+// significant bits, magnitudes 2^-10 .. 2688).  gfx950's FP4 conversion
+// applies only the power-of-two part of its f32 scale operand, so a scale
+// s = 2^e * f (1 <= f < 2 with 3 fraction bits) is applied in two exact
+// steps: the conversion with 2^e, then a packed fp16 multiply by f.
+struct DecScale {
+  float p2;     // 2^e (f32; 0 for a zero scale, whose codes are all zero)
+  uint32_t f2;  // f as an fp16 pair
+};
+// (the scale byte is byte SEL of the word `bytes`)
+template <int SEL>
+__device__ __forceinline__ DecScale dec_scale(uint32_t bytes) {
+  const uint32_t b = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)bytes, SEL));
+  return {__uint_as_float(b & 0xFF800000u), (0x3C00u | ((b >> 13) & 0x3FFu)) * 0x10001u};
+}
+
+// fp16 x8 of the 8 E2M1 codes of one dword (byte b: element 2b in the low
+// nibble, 2b+1 in the high one) times the scale.
+__device__ __forceinline__ u32x4 dec_dequant8(uint32_t cw, DecScale sc) {
+  const f16x2 f = __builtin_bit_cast(f16x2, sc.f2);
+  u32x4 w;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f16x2 c;
+    switch (b) {  // the byte select is an instruction immediate
+      case 0: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc.p2, 0); break;
+      case 1: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc.p2, 1); break;
+      case 2: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc.p2, 2); break;
+      default: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc.p2, 3); break;
+    }
+    w[b] = __builtin_bit_cast(uint32_t, c * f);
+  }
+  return w;
+}
+
+// 32x32x16 MFMA on bf16 or fp16 operands (passed as 16-byte words).
+template <bool F16>
+__device__ __forceinline__ f32x16 dec_mfma(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Row of the V^ tile whose D/2 columns (half hh = lane / 32) lane `lane`
+// dequantizes (packed): within each group of 8 lanes the swizzle phases of
+// the rows differ in their low 3 bits, so 16-byte stores of one chunk column
+// by 8 lanes fall into 8 different 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int dec_v_row(int lane) {
+  const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
+  const int b3 = (lane >> 3) & 1, b4 = (lane >> 4) & 1;
+  if constexpr (D == 128) return b0 + 4 * b1 + 8 * b2 + 2 * b3 + 16 * b4;
+  else return 2 * b0 + 4 * b1 + 8 * b2 + b3 + 16 * b4;
+}
+
+template <int D, bool PACKED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_fwd_dec(AttnArgs a) {
+  constexpr int KB = D / 16;       // MFMAs per S^T tile
+  constexpr int DB = D / 32;
+  constexpr int NQ = 2 * DB;       // MFMAs per O^T tile
+  constexpr int BN = 32;           // keys per tile
+  constexpr int VT = BN * D;       // bf16 elements per V^ tile
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int CH = VT / 8 / 64;  // 16-byte V^ copies per lane per tile (bf16)
+  constexpr int CW = D / 64;       // 16-byte code loads per lane per tensor per tile (packed)
+  constexpr int GPR = D / 16;      // scale bytes per row
+  constexpr int MS = D + 4;        // merge row stride (floats): conflict-free 16-byte stores
+  constexpr int QS = D + 8;        // Q^ row stride (elements): conflict-free 16-byte reads
+  constexpr int RING = 4 * 2 * VT * 2;
+  constexpr int MERGE = 4 * kDecBQ * MS * 4;
+  constexpr int LDS = RING > MERGE ? RING : MERGE;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[kDecBQ * QS];
+  __shared__ float s_m[4][kDecBQ], s_l[4][kDecBQ];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int S = a.kv_splits;
+  const int bh = (int)blockIdx.x / S, sp = (int)blockIdx.x % S;
+  const int nq = a.nq, nkv = a.nkv;
+  const int q0 = (int)blockIdx.y * kDecBQ;
+  const int qi = q0 + l32;
+  uint16_t* ring = reinterpret_cast<uint16_t*>(smem) + wave * 2 * VT;
+
+  // this wave's key tiles: g, g + W, ... (W waves per head), last one first
+  const int ntiles_all = (nkv + BN - 1) / BN;
+  const int W = 4 * S, g = 4 * sp + wave;
+  const int n = g < ntiles_all ? (ntiles_all - 1 - g) / W + 1 : 0;
+  auto tile_k0 = [&](int it) __attribute__((always_inline)) { return (g + W * (n - 1 - it)) * BN; };
+
+  // Q^ rows of the workgroup (rows past nq as zeros; fp16 for packed K^/V^)
+  {
+    const uint16_t* Q = a.q_hat + (size_t)bh * nq * D;
+#pragma unroll
+    for (int c = 0; c < kDecBQ * CPR / 256; ++c) {
+      const int p = 256 * c + tid, r = p / CPR, col = 8 * (p % CPR);
+      const bf16x8 v = (q0 + r < nq) ? ld_bf16x8(Q + (size_t)(q0 + r) * D + col) : zero_bf16x8();
+      if constexpr (PACKED) {
+        f16x8 hv;  // exact: Q^ values are E2M1 codes times E4M3 scales
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = (_Float16)(float)v[e];
+        *reinterpret_cast<f16x8*>(sQ + r * QS + col) = hv;
+      } else {
+        st_bf16x8(sQ + r * QS + col, v);
+      }
+    }
+  }
+  // head-dimension column of element 0 of MFMA j's operands in lane half h
+  const uint16_t* qrow = sQ + l32 * QS + (PACKED ? h * (D / 2) : 8 * h);
+  constexpr int QJ = PACKED ? 8 : 16;  // column step per MFMA
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = zero_f32x16();
+  float m = -INFINITY, l = 0.0f;
+  bool pending = false;
+  float alpha = 1.0f;
+  const float sl2 = a.softmax_scale * kLog2e;
+  const ColOffsets<D> co(4 * h, 4 * h + 8, lane);
+
+  // ---- bf16 K^ rows (registers) and V^ tiles (LDS copies)
+  const uint16_t* K = a.k_hat + (size_t)bh * nkv * D;
+  const uint16_t* V = a.v_hat + (size_t)bh * nkv * D;
+  bf16x8 kr[PACKED ? 1 : KB];
+  auto load_k = [&](int it) __attribute__((always_inline)) {
+    const int k0 = tile_k0(it);
+    const auto r = make_rsrc(K + (size_t)k0 * D, (uint32_t)(min(nkv - k0, BN) * D) * 2u);
+    const uint32_t off = (uint32_t)(l32 * D + 8 * h) * 2u;
+#pragma unroll
+    for (int j = 0; j < (PACKED ? 1 : KB); ++j)
+      kr[j] = __builtin_bit_cast(bf16x8, buf_ld16(r, off + 32u * j));
+  };
+  auto copy_v = [&](int it) __attribute__((always_inline)) {
+    const int k0 = tile_k0(it);
+    const u32x4 d = buf_desc(V + (size_t)k0 * D, (uint32_t)(min(nkv - k0, BN) * D) * 2u);
+    uint16_t* dst = ring + (it & 1) * VT;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // slot 64c + lane of the tile holds row p / CPR, column chunk swz(p)
+      const int p = 64 * c + lane;
+      buf_ld16_lds(d, (uint32_t)swz<D>(p / CPR, 8 * (p % CPR)) * 2u,
+                   __builtin_amdgcn_readfirstlane(lds_addr(dst + 512 * c)));
+    }
+  };
+
+  // ---- packed K^/V^: codes and scale bytes of two tiles in registers
+  const uint8_t* KC = a.k_codes + (size_t)bh * nkv * (D / 2);
+  const uint8_t* KS = a.k_scales + (size_t)bh * nkv * GPR;
+  const uint8_t* VC = a.v_codes + (size_t)bh * nkv * (D / 2);
+  const uint8_t* VS = a.v_scales + (size_t)bh * nkv * GPR;
+  const int vr = dec_v_row<D>(lane);  // V^ row this lane dequantizes
+  u32x4 kc[2][CW], vc[2][CW];
+  uint32_t ks[2], vs[2];
+  auto load_codes = [&](int it, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int sl = decltype(slot_tag)::value;
+    const int k0 = tile_k0(it);
+    const uint32_t rows = (uint32_t)min(nkv - k0, BN);  // rows past nkv read as zeros
+    const auto rkc = make_rsrc(KC + (size_t)k0 * (D / 2), rows * (D / 2));
+    const auto rks = make_rsrc(KS + (size_t)k0 * GPR, rows * GPR);
+    const auto rvc = make_rsrc(VC + (size_t)k0 * (D / 2), rows * (D / 2));
+    const auto rvs = make_rsrc(VS + (size_t)k0 * GPR, rows * GPR);
+    const uint32_t ko = (uint32_t)(l32 * (D / 2) + h * (D / 4));
+    const uint32_t vo = (uint32_t)(vr * (D / 2) + h * (D / 4));
+#pragma unroll
+    for (int c = 0; c < CW; ++c) kc[sl][c] = buf_ld16(rkc, ko + 16u * c);
+    if constexpr (D == 128)
+      ks[sl] = __builtin_amdgcn_raw_buffer_load_b32(rks, (uint32_t)(l32 * GPR + 4 * h), 0, 0);
+    else
+      ks[sl] = __builtin_amdgcn_raw_buffer_load_b16(rks, (uint32_t)(l32 * GPR + 2 * h), 0, 0);
+#pragma unroll
+    for (int c = 0; c < CW; ++c) vc[sl][c] = buf_ld16(rvc, vo + 16u * c);
+    if constexpr (D == 128)
+      vs[sl] = __builtin_amdgcn_raw_buffer_load_b32(rvs, (uint32_t)(vr * GPR + 4 * h), 0, 0);
+    else
+      vs[sl] = __builtin_amdgcn_raw_buffer_load_b16(rvs, (uint32_t)(vr * GPR + 2 * h), 0, 0);
+  };
+  // K^ operand j of the tile in slot sl: codes dword j of the lane's run,
+  // scale byte j/2 of the lane's scale bytes
+  auto k_op_packed = [&](auto j_tag, auto slot_tag) __attribute__((always_inline)) -> u32x4 {
+    constexpr int j = decltype(j_tag)::value;
+    constexpr int sl = decltype(slot_tag)::value;
+    return dec_dequant8(kc[sl][j / 4][j % 4], dec_scale<j / 2>(ks[sl]));
+  };
+  // V^ piece c of the tile in slot sl (row vr, columns h*D/2 + 8c ..) into dst
+  auto v_store_packed = [&](auto c_tag, auto slot_tag, uint16_t* dst) __attribute__((always_inline)) {
+    constexpr int c = decltype(c_tag)::value;
+    constexpr int sl = decltype(slot_tag)::value;
+    *reinterpret_cast<u32x4*>(dst + swz<D>(vr, h * (D / 2) + 8 * c)) =
+        dec_dequant8(vc[sl][c / 4][c % 4], dec_scale<c / 2>(vs[sl]));
+  };
+
+  // one key tile: S^T, the online softmax, O^T += V^T P^T from the tile's
+  // LDS tile.  The next tile's V^ goes into the other LDS tile (it held
+  // tile it-1, whose reads finished in the previous step).
+  auto step = [&](int it, auto slot_tag, auto mask_tag) __attribute__((always_inline)) {
+    constexpr int sl = decltype(slot_tag)::value;
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int k0 = tile_k0(it);
+    const bool more = it + 1 < n;
+    f32x16 s;
+    u32x4 qb[KB];
+    auto ldq = [&](int j) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4*>(qrow + QJ * j);
+    };
+    if constexpr (PACKED) {
+      u32x4 ka[KB];
+      ka[0] = k_op_packed(IntTag<0>(), slot_tag);
+      qb[0] = ldq(0);
+      static_for<KB>([&](auto jt) __attribute__((always_inline)) {
+        constexpr int j = decltype(jt)::value;
+        if constexpr (j + 1 < KB) {
+          ka[j + 1] = k_op_packed(IntTag<j + 1>(), slot_tag);
+          qb[j + 1] = ldq(j + 1);
+        }
+        s = dec_mfma<true>(ka[j], qb[j], j == 0 ? zero_f32x16() : s);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // slot sl is free now (K^ of tile it consumed, V^ of tile it in LDS)
+      if (it + 2 < n) load_codes(it + 2, slot_tag);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kFwdAhead; ++k) qb[k] = ldq(k);
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (j + kFwdAhead < KB) qb[j + kFwdAhead] = ldq(j + kFwdAhead);
+        s = dec_mfma<false>(__builtin_bit_cast(u32x4, kr[j]), qb[j], j == 0 ? zero_f32x16() : s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // V^ of tile it+1 before K^ of tile it+1: loads complete in issue
+      // order, so the wait for K^ at the next step also covers this copy
+      if (more) {
+        copy_v(it + 1);
+        load_k(it + 1);
+      }
+    }
+
+    // online softmax (S^T rows = keys 8*(i/4) + 4h + i%4, one query per lane)
+    float xs[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xs[i] = s[i] * sl2;
+    if constexpr (MASK) {
+      const int rem = nkv - k0 - 4 * h;  // keys of this lane half left in the tile
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) >= rem) xs[i] = -INFINITY;
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, xs[i]);
+    tmax = fmaxf(tmax, xor32(tmax));
+    const float mnew = fmaxf(m, tmax);
+    const float base = (mnew == -INFINITY) ? 0.0f : mnew;
+    float psum = 0.0f;
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p0 = fast_exp2(xs[2 * e] - base), p1 = fast_exp2(xs[2 * e + 1] - base);
+      psum += p0 + p1;
+      if constexpr (PACKED)
+        w[e] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)p0, (_Float16)p1});
+      else
+        w[e] = pack_bf16x2(p0, p1);
+    }
+    const u32x4 b[2] = {u32x4{w[0], w[1], w[2], w[3]}, u32x4{w[4], w[5], w[6], w[7]}};
+    if (__any(mnew > m)) {
+      alpha = fast_exp2(m - base);
+      l *= alpha;
+      pending = true;
+    }
+    l += psum;
+    m = mnew;
+    fwd_rescale<D>(o, pending, alpha);
+
+    const uint16_t* sVb = ring + (it & 1) * VT;
+    uint16_t* nxt = ring + ((it + 1) & 1) * VT;
+    u32x4 c[NQ];
+#pragma unroll
+    for (int k = 0; k < kFwdAhead; ++k) c[k] = __builtin_bit_cast(u32x4, fwd_v_op<D>(sVb, co, k));
+    static_for<NQ>([&](auto kt) __attribute__((always_inline)) {
+      constexpr int k = decltype(kt)::value;
+      if constexpr (k + kFwdAhead < NQ)
+        c[k + kFwdAhead] = __builtin_bit_cast(u32x4, fwd_v_op<D>(sVb, co, k + kFwdAhead));
+      o[k % DB] = dec_mfma<PACKED>(c[k], b[k / DB], o[k % DB]);
+      if constexpr (PACKED) {
+        if (more) v_store_packed(IntTag<k>(), IntTag<1 - sl>(), nxt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  __syncthreads();  // Q^ staged
+  if constexpr (PACKED) {
+    if (n > 0) {
+      load_codes(0, IntTag<0>());
+      static_for<KB>([&](auto ct) __attribute__((always_inline)) {
+        v_store_packed(ct, IntTag<0>(), ring);
+      });
+    }
+    if (n > 1) load_codes(1, IntTag<1>());
+  } else {
+    if (n > 0) {
+      copy_v(0);
+      load_k(0);
+    }
+  }
+  // tile 0 is the only one that can reach past nkv; the rest in slot pairs
+  if (n > 0) step(0, IntTag<0>(), BoolTag<true>());
+  for (int it = 1; it < n; it += 2) {
+    step(it, IntTag<1>(), BoolTag<false>());
+    if (it + 1 < n) step(it + 1, IntTag<0>(), BoolTag<false>());
+  }
+
+  // merge of the 4 waves: M = max of the wave maxima, each wave's O^T and
+  // row sum weighted by exp2(m_w - M) (0 for a wave without keys)
+  const float lt = l + xor32(l);
+  __syncthreads();  // the merge buffer overlaps the V^ tiles
+  if (h == 0) s_m[wave][l32] = m;
+  __syncthreads();
+  {
+    const float M = fmaxf(fmaxf(s_m[0][l32], s_m[1][l32]), fmaxf(s_m[2][l32], s_m[3][l32]));
+    const float f = fast_exp2(m - (M == -INFINITY ? 0.0f : M));
+    float* mw = reinterpret_cast<float*>(smem) + (wave * kDecBQ + l32) * MS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 v = {o[db][4 * g4] * f, o[db][4 * g4 + 1] * f, o[db][4 * g4 + 2] * f,
+                         o[db][4 * g4 + 3] * f};
+        *reinterpret_cast<f32x4*>(mw + 32 * db + 8 * g4 + 4 * h) = v;
+      }
+    }
+    if (h == 0) s_l[wave][l32] = lt * f;
+  }
+  __syncthreads();
+  // thread -> query row tid % 32, columns (tid / 32) * D/8 ..
+  const int q = tid & 31, part = tid >> 5;
+  if (q0 + q < nq) {
+    const size_t row = ((size_t)bh * S + sp) * nq + q0 + q;
+    const float* src = reinterpret_cast<const float*>(smem) + q * MS + part * (D / 8);
+    float* dst = a.o_part + row * D + part * (D / 8);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      f32x4 acc = *reinterpret_cast<const f32x4*>(src + 4 * i);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + w * kDecBQ * MS + 4 * i);
+        acc += v;
+      }
+      *reinterpret_cast<f32x4*>(dst + 4 * i) = acc;
+    }
+    if (part == 0) {
+      const float M = fmaxf(fmaxf(s_m[0][q], s_m[1][q]), fmaxf(s_m[2][q], s_m[3][q]));
+      const float L = (s_l[0][q] + s_l[1][q]) + (s_l[2][q] + s_l[3][q]);
+      *reinterpret_cast<f32x2*>(a.ml_part + 2 * row) = f32x2{M, L};
+    }
+  }
 }
 
 }  // namespace
@@ -446,21 +863,31 @@ hipError_t launch_fwd_t(const AttnArgs& a, int head_dim, hipStream_t stream,
                         const LaunchEvents* ev) {
   const unsigned qtiles = (unsigned)(((a.nq + kFwdBM - 1) / kFwdBM) * a.bh);
   const dim3 block(256);
+  const int64_t rows = (int64_t)a.bh * a.nq;
+  const dim3 cgrid((unsigned)((rows * (head_dim / 4) + 255) / 256));
+  const LaunchEvents e0 = {ev ? ev->start : nullptr, nullptr};
+  const LaunchEvents e1 = {nullptr, ev ? ev->stop : nullptr};
+  if (a.kv_decode && !a.causal) {
+    // 32-query tiles over key runs, then the merge (one timed span)
+    const dim3 grid((unsigned)(a.bh * a.kv_splits), (unsigned)((a.nq + kDecBQ - 1) / kDecBQ));
+    const hipError_t st =
+        head_dim == 128 ? launch(k_fwd_dec<128, PACKED>, grid, block, stream, ev ? &e0 : nullptr, a)
+                        : launch(k_fwd_dec<64, PACKED>, grid, block, stream, ev ? &e0 : nullptr, a);
+    if (st != hipSuccess) return st;
+    return head_dim == 128
+               ? launch(k_fwd_combine<128>, cgrid, block, stream, ev ? &e1 : nullptr, a, rows)
+               : launch(k_fwd_combine<64>, cgrid, block, stream, ev ? &e1 : nullptr, a, rows);
+  }
   if (a.kv_splits > 1 && !a.causal) {
     // split over keys, then the merge (timed as one span: start of the
     // first launch to the end of the second)
     const dim3 grid(qtiles, (unsigned)a.kv_splits);
-    const LaunchEvents e0 = {ev ? ev->start : nullptr, nullptr};
-    const LaunchEvents e1 = {nullptr, ev ? ev->stop : nullptr};
     const hipError_t st = head_dim == 128
                               ? launch(k_fwd<128, false, PACKED, true>, grid, block, stream,
                                        ev ? &e0 : nullptr, a)
                               : launch(k_fwd<64, false, PACKED, true>, grid, block, stream,
                                        ev ? &e0 : nullptr, a);
     if (st != hipSuccess) return st;
-    const int64_t rows = (int64_t)a.bh * a.nq;
-    const int64_t threads = rows * (head_dim / 4);
-    const dim3 cgrid((unsigned)((threads + 255) / 256));
     return head_dim == 128
                ? launch(k_fwd_combine<128>, cgrid, block, stream, ev ? &e1 : nullptr, a, rows)
                : launch(k_fwd_combine<64>, cgrid, block, stream, ev ? &e1 : nullptr, a, rows);

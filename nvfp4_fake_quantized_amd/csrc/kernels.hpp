@@ -65,6 +65,7 @@ struct AttnArgs {
   float* o_part;          // (BH, kv_splits, nq, D)
   float* ml_part;         // (BH, kv_splits, nq, 2): max (log2 units), sum
   int kv_splits;          // 0 or 1: no split
+  int kv_decode;          // 1: 32-query tiles (k_fwd_dec), kv_splits >= 1 key runs
   int bh;                 // batch * heads
   int nq, nkv;
   int causal;

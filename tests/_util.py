@@ -57,3 +57,22 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     bits = f32.view(np.uint32)
     assert np.all((bits & 0xFFFF) == 0), "value not exactly representable in bf16"
     return (bits >> 16).astype(np.uint16)
+
+
+def fwd_plan(b: int, h: int, nq: int, nkv: int, causal: bool):
+    """The library's documented key coverage of a forward: (key runs, whether
+    the 32-query-tile path runs).  Non-causal with at most 32 queries per
+    head: 32-query tiles, the key tiles dealt out to
+    min(ceil(512 / bh), max(1, key tiles / 8)) workgroups per head.  Otherwise the keys are split when fewer than 256 query tiles of
+    128 exist, with at least 4 key tiles of 32 per split, for about 512
+    workgroups."""
+    if causal:
+        return 1, False
+    bh, ktiles = b * h, (nkv + 31) // 32
+    if nq <= 32:
+        return min((512 + bh - 1) // bh, max(1, ktiles // 8)), True
+    wgs = bh * ((nq + 127) // 128)
+    if wgs >= 256:
+        return 1, False
+    s = min((512 + wgs - 1) // wgs, ktiles // 4)
+    return (s if s >= 2 else 1), False

@@ -16,6 +16,7 @@ import re
 import pytest
 
 from nvfp4_fake_quantized_amd import binding as B
+from tests._util import fwd_plan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
@@ -288,30 +289,25 @@ def test_instrumentation_entry_points_reject_bad_arguments_before_launch():
 
 
 def test_forward_workspace_holds_the_key_split_partials():
-    """The forward splits the keys (non-causal, fewer than 256 query tiles of
-    128, at least 4 key tiles of 32 per split, about 512 workgroups); its
-    workspace then grows by bh * splits * Nq * (4 D + 8) bytes (each part
-    256-byte aligned), and only then."""
-    def splits(b, h, nq, nkv, causal):
-        wgs = b * h * ((nq + 127) // 128)
-        if causal or wgs >= 256:
-            return 1
-        s = min((512 + wgs - 1) // wgs, ((nkv + 31) // 32) // 4)
-        return s if s >= 2 else 1
-
+    """The forward's workspace grows by the partial results of its key runs,
+    bh * splits * Nq * (4 D + 8) bytes (each part 256-byte aligned), when it
+    splits the keys or takes the 32-query-tile path, and only then."""
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     cases = [(1, 2, 16, 4100, 128, False), (1, 4, 64, 3001, 64, False), (2, 3, 100, 8192, 128, False),
              (1, 1, 1, 20000, 128, False), (1, 1, 40, 300, 64, False), (1, 1, 40, 200, 64, False),
              (1, 16, 4096, 4096, 128, False), (1, 1, 128, 128, 64, False),
-             (1, 2, 300, 300, 128, True), (2, 40, 8192, 8192, 128, True)]
+             (1, 2, 300, 300, 128, True), (2, 40, 8192, 8192, 128, True),
+             (1, 1, 32, 100, 64, False), (64, 16, 1, 65536, 128, False), (1, 1, 33, 5000, 128, False),
+             (1, 1, 16, 16, 128, True)]
     seen = set()
     for b, h, nq, nkv, d, causal in cases:
         p = B.make_problem(b, h, nq, nkv, d, causal, d ** -0.5)
-        S = splits(b, h, nq, nkv, causal)
-        seen.add(S > 1)
+        S, dec = fwd_plan(b, h, nq, nkv, causal)
+        kind = "decode" if dec else ("split" if S > 1 else "plain")
+        seen.add(kind)
         bh = b * h
         base = (al(bh * nq * d * 2) + 2 * al(bh * nkv * d * 2) + al(bh * nq * d // 16)
                 + 2 * al(bh * nkv * d // 16))
-        extra = (al(bh * nq * S * d * 4) + al(bh * nq * S * 8)) if S > 1 else 0
-        assert B.attnqat_fwd_workspace_bytes(p) == base + extra, (b, h, nq, nkv, d, causal, S)
-    assert seen == {True, False}
+        extra = (al(bh * nq * S * d * 4) + al(bh * nq * S * 8)) if kind != "plain" else 0
+        assert B.attnqat_fwd_workspace_bytes(p) == base + extra, (b, h, nq, nkv, d, causal, S, kind)
+    assert seen == {"decode", "split", "plain"}

@@ -1,16 +1,17 @@
-"""The forward split over keys: few queries against long K/V.
+"""The forward over few queries: split over keys, or in 32-query tiles.
 
 When the 128-query tiles of all heads cannot fill the chip and the problem is
 non-causal, attnqat_fwd and attnqat_fwd_packed split the keys over
-workgroups and merge the splits' partial results (unnormalized O, row max
-and row sum) into O_hp and lse.  The result is the same QAT forward
-("NVFP4 Attention QAT Backward", §Overview formula block; lse natural log,
-§Tensor contract), so it is checked against the oracle forward at the
-stated bar (relative Frobenius error 5e-3, elementwise 2e-2 * max|ref|),
-from bf16 K/V and from packed NVFP4 K/V (the storage of the Attn-QAT
-summary's "FP4 only where it's free").  The cases include a single query,
-ragged key counts (tails inside the last split), splits without keys and
-both head sizes.
+workgroups; with at most 32 queries per head they run 32-query tiles whose
+four waves take separate key runs.  Either way the runs' partial results
+(unnormalized O, row max and row sum) are merged into O_hp and lse.  The
+result is the same QAT forward ("NVFP4 Attention QAT Backward", §Overview
+formula block; lse natural log, §Tensor contract), so it is checked against
+the oracle forward at the stated bar (relative Frobenius error 5e-3,
+elementwise 2e-2 * max|ref|), from bf16 K/V and from packed NVFP4 K/V (the
+storage of the Attn-QAT summary's "FP4 only where it's free").  The cases
+include a single query, a single key, ragged key counts (tails inside the
+last run), runs and waves without keys, and both head sizes.
 """
 from __future__ import annotations
 
@@ -19,21 +20,10 @@ import torch
 
 from nvfp4_fake_quantized_amd import binding as B
 from oracle.attention import qat_forward_head, quantize_qkv
-from tests._util import check_close
+from tests._util import check_close, fwd_plan
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-
-
-def _splits(b, h, nq, nkv):
-    """The library's documented split policy (non-causal): enough splits for
-    about 512 workgroups when fewer than 256 query tiles exist, at least 4
-    key tiles of 32 keys per split."""
-    wgs = b * h * ((nq + 127) // 128)
-    if wgs >= 256:
-        return 1
-    s = min((512 + wgs - 1) // wgs, ((nkv + 31) // 32) // 4)
-    return s if s >= 2 else 1
 
 
 def _inputs(b, h, nq, nkv, d, seed):
@@ -47,22 +37,30 @@ def _inputs(b, h, nq, nkv, d, seed):
 
 
 CASES = [  # b, h, nq, nkv, d
-    (1, 2, 16, 4100, 128),    # 129 key tiles in 32 splits of 5: the last 6 splits are empty
+    # split over keys (more than 32 queries)
     (1, 4, 64, 3001, 64),
     (2, 3, 100, 8192, 128),
-    (1, 1, 1, 20000, 128),    # a single query
     (1, 2, 130, 2500, 128),   # two query tiles, ragged keys
     (1, 1, 40, 300, 64),      # two splits of 5 tiles, the last tile 12 keys
+    # 32-query tiles (at most 32 queries)
+    (1, 2, 16, 4100, 128),    # 64 waves per head over 129 tiles: wave 0 takes three, the tail among them
+    (1, 1, 1, 20000, 128),    # a single query
+    (1, 3, 32, 1000, 64),     # a full query tile
+    (2, 2, 5, 77, 128),       # one workgroup per head: three waves of one tile (the last 13 keys), one idle
+    (1, 1, 17, 1, 64),        # a single key (three idle waves)
+    (3, 5, 9, 2049, 128),     # the last tile holds one key
+    (1, 1, 24, 65536, 64),    # long keys
 ]
 
 
 @pytest.mark.parametrize("b,h,nq,nkv,d", CASES)
-def test_split_forward_matches_oracle(b, h, nq, nkv, d):
+def test_few_query_forward_matches_oracle(b, h, nq, nkv, d):
     scale = d ** -0.5
     q, k, v = _inputs(b, h, nq, nkv, d, seed=nq * 7 + nkv)
-    S = _splits(b, h, nq, nkv)
-    assert S > 1, "the case must take the split path"
-    print(f"[split fwd] B{b} H{h} Nq{nq} Nkv{nkv} D{d}: {S} key splits", flush=True)
+    S, dec = fwd_plan(b, h, nq, nkv, False)
+    assert dec or S > 1, "the case must split the keys or take the 32-query tiles"
+    kind = "32-query tiles" if dec else "split"
+    print(f"[few-query fwd] B{b} H{h} Nq{nq} Nkv{nkv} D{d}: {kind}, {S} key runs", flush=True)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     p = B.problem_for(qd, kd, False, scale)
     ws = torch.empty(B.attnqat_fwd_workspace_bytes(p), dtype=torch.uint8, device=DEV)
@@ -80,7 +78,7 @@ def test_split_forward_matches_oracle(b, h, nq, nkv, d):
             qh, kh, vh = quantize_qkv(q[bi, hi].double().numpy(), k[bi, hi].double().numpy(),
                                       v[bi, hi].double().numpy())
             o64, l64 = qat_forward_head(qh, kh, vh, scale, False, quantize=False)
-            tag = f"split Nq{nq} Nkv{nkv} D{d}"
+            tag = f"{kind} Nq{nq} Nkv{nkv} D{d}"
             check_close(o[bi, hi].cpu(), o64, f"{tag} O_hp[{bi},{hi}]")
             check_close(lse[bi, hi].cpu(), l64, f"{tag} lse[{bi},{hi}]")
             check_close(o2[bi, hi].cpu(), o64, f"{tag} packed O_hp[{bi},{hi}]")

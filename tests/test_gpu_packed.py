@@ -20,7 +20,7 @@ import torch
 from nvfp4_fake_quantized_amd import binding as B
 from oracle.attention import qat_forward_head
 from oracle.nvfp4 import fake_nvfp4
-from tests._util import check_close, rel_fro
+from tests._util import REL_FRO_TOL, check_close, rel_fro
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -98,7 +98,11 @@ def _synthetic(n, d, seed, nk=None, heads=2):
 
 def _check_packed_forward(q, k, v, causal, scale, heads, label):
     """Packed forward against the oracle forward on the given heads, and
-    against attnqat_fwd to within fp32 rounding order."""
+    against attnqat_fwd: lse to within the fp32 rounding order; O_hp to
+    within one bf16 rounding of O_hp and the fp32 rounding order, except
+    with at most 32 non-causal queries per head, where the packed kernel
+    rounds P to fp16 instead of bf16 before P V^ (then both are held to the
+    stated bar against each other, as each is against the oracle)."""
     o1, l1 = _fwd(q, k, v, causal, scale, packed=False)
     o2, l2 = _fwd(q, k, v, causal, scale, packed=True)
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
@@ -107,7 +111,9 @@ def _check_packed_forward(q, k, v, causal, scale, heads, label):
         check_close(o2[b_, h].cpu(), o64, f"{label} packed O_hp[{b_},{h}]")
         check_close(l2[b_, h].cpu(), l64, f"{label} packed lse[{b_},{h}]")
     # one bf16 rounding of O_hp, fp32 rounding order of the softmax sums
-    assert rel_fro(o2, o1) <= 1e-3, (label, rel_fro(o2, o1))
+    # (bf16 against fp16 probabilities on the 32-query-tile path)
+    fp16_p = not causal and q.shape[2] <= 32
+    assert rel_fro(o2, o1) <= (REL_FRO_TOL if fp16_p else 1e-3), (label, rel_fro(o2, o1))
     assert rel_fro(l2, l1) <= 1e-6, (label, rel_fro(l2, l1))
 
 
