@@ -209,7 +209,17 @@ ATTNQAT_API int attnqat_fwd_quantized(const attnqat_problem* p, const void* q, c
  * In: q, o_hp, d_o (B,H,Nq,D) bf16; k, v (B,H,Nkv,D) bf16; lse (B,H,Nq)
  * fp32 from the matching forward.  Out: dq (B,H,Nq,D), dk, dv (B,H,Nkv,D)
  * bf16.  The workspace (>= attnqat_bwd_workspace_bytes) holds Q^/K^/V^,
- * their scales and delta afterwards. */
+ * their scales and delta afterwards.
+ * Small problems: when the key blocks of 128 (over all heads) number fewer
+ * than 256, the dK/dV kernel splits its query loop over s_kv =
+ * min(ceil(256 / key blocks), query sub-tiles of 32 / 4) workgroups (when
+ * >= 2); when the query blocks of 128 number fewer than 256, the dQ kernel
+ * splits its key loop over s_q = min(ceil(512 / query blocks), key tiles
+ * of 32 / 4) workgroups (when >= 2).  The splits write fp32 partial sums
+ * (s_q*B*H*Nq*D*4 and s_kv*2*B*H*Nkv*D*4 bytes of the workspace, after the
+ * parts named by attnqat_workspace_layout) that a reduction adds up in a
+ * fixed order, so results stay deterministic; they equal the unsplit
+ * results up to the fp32 rounding order. */
 ATTNQAT_API int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k,
                             const void* v, const void* o_hp, const void* d_o,
                             const float* lse, void* dq, void* dk, void* dv, void* workspace,
@@ -221,8 +231,10 @@ ATTNQAT_API int attnqat_bwd(const attnqat_problem* p, const void* q, const void*
  * a static device array of ATTNQAT_NOALLOC_MAX_WORKSPACE_BYTES that the
  * library holds on every GPU it runs on until the process ends (its address
  * is looked up once per device, on the first call there).  The call itself
- * allocates nothing.  Problems whose attnqat_bwd_workspace_bytes exceed that
- * size return ATTNQAT_ERR_UNSUPPORTED.  All calls on one GPU share its array:
+ * allocates nothing.  Where attnqat_bwd_workspace_bytes exceeds that size
+ * only because of the small-problem split loops' partial sums, the loops
+ * run unsplit; problems that do not fit even so return
+ * ATTNQAT_ERR_UNSUPPORTED.  All calls on one GPU share its array:
  * calls that overlap on one GPU (different streams or threads) race and must
  * be serialized by the caller; the array keeps the last call's contents,
  * which no call depends on.  Other arguments and errors as attnqat_bwd. */

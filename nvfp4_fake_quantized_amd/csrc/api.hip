@@ -45,10 +45,44 @@ int validate_problem(const attnqat_problem* p) {
 }
 
 struct Layout {
-  size_t q_hat, k_hat, v_hat, q_scale, k_scale, v_scale, delta, o_part, ml_part, total;
+  size_t q_hat, k_hat, v_hat, q_scale, k_scale, v_scale, delta, o_part, ml_part, dq_part,
+      dkdv_part, total;
   int kv_splits;
   int kv_decode;
+  int dq_splits, dkdv_splits;
 };
+
+// Backward over few tiles.  k_dkdv runs one workgroup of 128 keys per CU and
+// k_dq two of 128 queries; when a problem has fewer key blocks (or query
+// blocks) than CUs the chip is underfilled, so the query loop of k_dkdv is
+// split over up to ceil(256 / key blocks) workgroups (at least 4 sub-tiles
+// of 32 queries each) and the key loop of k_dq over up to
+// ceil(512 / query blocks) (at least 4 key tiles of 32 each).  (Measured:
+// the splits pay on the smallest grids; at 256 query blocks, one per CU,
+// a dQ split already costs more in partial sums than it gains.)  Their fp32 partial sums take splits * B*H*N*D*4 bytes (dK and dV:
+// twice that) of the backward workspace.
+struct BwdPlan {
+  int dq_splits, dkdv_splits;
+};
+BwdPlan bwd_plan(const attnqat_problem* p) {
+  const int64_t bh = (int64_t)p->batch * p->heads;
+  const int64_t kblocks = bh * (((int64_t)p->seqlen_kv + 127) / 128);
+  const int64_t qblocks = bh * (((int64_t)p->seqlen_q + 127) / 128);
+  const int64_t qsub = ((int64_t)p->seqlen_q + 31) / 32;   // query sub-tiles of a key block
+  const int64_t ktiles = ((int64_t)p->seqlen_kv + 31) / 32;  // key tiles of a query block
+  BwdPlan b = {1, 1};
+  if (kblocks < 256) {
+    const int64_t want = (256 + kblocks - 1) / kblocks, cap = qsub / 4;
+    const int64_t s = want < cap ? want : cap;
+    b.dkdv_splits = s >= 2 ? (int)s : 1;
+  }
+  if (qblocks < 256) {
+    const int64_t want = (512 + qblocks - 1) / qblocks, cap = ktiles / 4;
+    const int64_t s = want < cap ? want : cap;
+    b.dq_splits = s >= 2 ? (int)s : 1;
+  }
+  return b;
+}
 
 // How the forward covers the keys (non-causal problems only; a causal
 // forward always runs one workgroup per 128 queries over all its keys):
@@ -81,7 +115,8 @@ FwdPlan fwd_plan(const attnqat_problem* p) {
   return {s >= 2 ? (int)s : 1, 0};
 }
 
-Layout make_layout(const attnqat_problem* p, bool bwd) {
+// split_ok = false: the backward without split loops (no partial sums).
+Layout make_layout(const attnqat_problem* p, bool bwd, bool split_ok = true) {
   const size_t bh = (size_t)p->batch * p->heads;
   const size_t nq = bh * p->seqlen_q, nkv = bh * p->seqlen_kv;
   const size_t D = p->head_dim;
@@ -93,12 +128,24 @@ Layout make_layout(const attnqat_problem* p, bool bwd) {
   L.q_scale = off; off = align_up(off + nq * D / 16);
   L.k_scale = off; off = align_up(off + nkv * D / 16);
   L.v_scale = off; off = align_up(off + nkv * D / 16);
-  L.o_part = L.ml_part = SIZE_MAX;
+  L.o_part = L.ml_part = L.dq_part = L.dkdv_part = SIZE_MAX;
   L.kv_splits = 1;
   L.kv_decode = 0;
+  L.dq_splits = L.dkdv_splits = 1;
   if (bwd) {
     L.delta = off;
     off = align_up(off + nq * 4);
+    const BwdPlan plan = split_ok ? bwd_plan(p) : BwdPlan{1, 1};
+    L.dq_splits = plan.dq_splits;
+    L.dkdv_splits = plan.dkdv_splits;
+    if (L.dq_splits > 1) {
+      L.dq_part = off;
+      off = align_up(off + (size_t)L.dq_splits * nq * D * 4);
+    }
+    if (L.dkdv_splits > 1) {
+      L.dkdv_part = off;
+      off = align_up(off + (size_t)L.dkdv_splits * 2 * nkv * D * 4);
+    }
   } else {
     L.delta = SIZE_MAX;
     const FwdPlan plan = fwd_plan(p);
@@ -344,7 +391,7 @@ int run_fwd_packed(const attnqat_problem* p, const void* q, const uint8_t* k_cod
 int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
             const void* o_hp, const void* d_o, const float* lse, void* dq, void* dk, void* dv,
             void* workspace, size_t workspace_bytes, hipStream_t stream,
-            const attnqat::LaunchEvents* ev) {
+            const attnqat::LaunchEvents* ev, bool split_ok = true) {
   int st = validate_problem(p);
   if (st != ATTNQAT_OK) return st;
   const void* ptrs[] = {q, k, v, o_hp, d_o, lse, dq, dk, dv, workspace};
@@ -352,7 +399,7 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
     if (ptr == nullptr) return ATTNQAT_ERR_INVALID_ARGUMENT;
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return ATTNQAT_ERR_MISALIGNED;
-  const Layout L = make_layout(p, true);
+  const Layout L = make_layout(p, true, split_ok);
   if (workspace_bytes < L.total) return ATTNQAT_ERR_WORKSPACE_TOO_SMALL;
   st = device_status();
   if (st != ATTNQAT_OK) return st;
@@ -395,7 +442,11 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   a.causal = p->causal;
   a.softmax_scale = p->softmax_scale;
   a.p_scale = p->p_scale;
-  // 3) dQ and 4) dK/dV
+  a.dq_splits = L.dq_splits;
+  a.dkdv_splits = L.dkdv_splits;
+  if (L.dq_splits > 1) a.dq_part = at<float>(workspace, L.dq_part);
+  if (L.dkdv_splits > 1) a.dkdv_part = at<float>(workspace, L.dkdv_part);
+  // 3) dQ and 4) dK/dV (each with its reduction when split)
   if (attnqat::launch_bwd_dq(a, p->head_dim, stream, timing(ev, 1)) != hipSuccess)
     return ATTNQAT_ERR_HIP;
   if (attnqat::launch_bwd_dkdv(a, p->head_dim, stream, timing(ev, 2)) != hipSuccess)
@@ -523,12 +574,15 @@ extern "C" int attnqat_bwd_noalloc(const attnqat_problem* p, const void* q, cons
                                    hipStream_t stream) {
   const int st = validate_problem(p);
   if (st != ATTNQAT_OK) return st;
-  if (make_layout(p, true).total > kScratchBytes) return ATTNQAT_ERR_UNSUPPORTED;
+  // the split loops' partial sums only where they fit beside the rest
+  const bool split_ok = make_layout(p, true).total <= kScratchBytes;
+  if (make_layout(p, true, split_ok).total > kScratchBytes) return ATTNQAT_ERR_UNSUPPORTED;
   const int dst = device_status();
   if (dst != ATTNQAT_OK) return dst;
   void* ws = scratch_on_current_device();
   if (ws == nullptr) return ATTNQAT_ERR_HIP;
-  return run_bwd(p, q, k, v, o_hp, d_o, lse, dq, dk, dv, ws, kScratchBytes, stream, nullptr);
+  return run_bwd(p, q, k, v, o_hp, d_o, lse, dq, dk, dv, ws, kScratchBytes, stream, nullptr,
+                 split_ok);
 }
 
 extern "C" int attnqat_probe_issue_mix(int mode, int valu_per_mfma, int agpr, const void* in,

@@ -19,7 +19,9 @@
 // diagonal) evaluate masks; causal tiles entirely above the diagonal are
 // skipped per wave, the diagonal tile keeps the elementwise key <= query
 // mask, keys >= Nkv get P = 0, loads beyond the ends read zeros and stores
-// stop at the ends.
+// stop at the ends.  When the query blocks cannot fill the chip, the key
+// tiles of each block are split over blockIdx.y: each split writes its fp32
+// dQ^T partial, and k_sum_parts adds the splits in order (deterministic).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -211,7 +213,12 @@ void k_dq(AttnArgs a) {
   for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
   // keys above the workgroup's last query are masked (causal)
   const int kend = CAUSAL ? min(nkv, qblk0 + kDqBM) : nkv;
-  const int ntiles = (kend + BN - 1) / BN;
+  // this workgroup's key tiles t0 .. t0 + ntiles - 1 (all unless split)
+  const int ntiles_all = (kend + BN - 1) / BN;
+  const int KSPL = a.dq_splits > 1 ? a.dq_splits : 1;
+  const int per = (ntiles_all + KSPL - 1) / KSPL;
+  const int t0 = (int)blockIdx.y * per;  // blockIdx.y < KSPL
+  const int ntiles = KSPL > 1 ? max(0, min(ntiles_all - t0, per)) : ntiles_all;
 
   // K^/V^ tiles go global -> LDS directly (no registers). Copy instruction c
   // of this wave fills LDS chunk slots 64*(CH*wave + c) + lane; slot (row r,
@@ -224,7 +231,7 @@ void k_dq(AttnArgs a) {
     goff[c] = (uint32_t)swz<D>(p / CPR, 8 * (p % CPR)) * 2u;
   }
   auto issue_tile = [&](int it) __attribute__((always_inline)) {
-    const int k0 = it * BN;
+    const int k0 = (t0 + it) * BN;
     const int buf = it % NB;
     // rows past nkv arrive as zeros (masked out later)
     const uint32_t bytes = (uint32_t)(min(nkv - k0, BN) * D) * 2u;
@@ -241,8 +248,9 @@ void k_dq(AttnArgs a) {
 
   // Leading tiles are interior (branch-free); masks start at the first tile
   // that reaches past nkv or above the workgroup's first query (causal).
-  int it_hi = min(ntiles, nkv / BN);
+  int it_hi = min(ntiles_all, nkv / BN);
   if (CAUSAL) it_hi = min(it_hi, (qblk0 + 1) / BN);
+  it_hi = max(0, min(ntiles, it_hi - t0));
 
   if (ntiles > 0) issue_tile(0);
   if (ntiles > 1) issue_tile(1);
@@ -257,7 +265,7 @@ void k_dq(AttnArgs a) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = it % NB;
     const int pbuf = (it + NB - 1) % NB;
-    const int k0 = it * BN;
+    const int k0 = (t0 + it) * BN;
     if (it + 2 < ntiles) issue_tile(it + 2);
     // (boundary tiles only) every key above every query of this wave: skip;
     // every later tile is then skipped too
@@ -296,6 +304,21 @@ void k_dq(AttnArgs a) {
   // the last block's dQ^T (its tile is still resident)
   if (have_prev) dq_acc<D>(acc, b_prev, sK[(ntiles - 1) % NB], co);
 
+  if (KSPL > 1) {
+    // this split's unscaled dQ^T row (a split without keys stores zeros)
+    if (qok) {
+      float* out = a.dq_part + (((size_t)blockIdx.y * a.bh + bh) * nq + qi) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4*>(out + 32 * db + 8 * g4 + 4 * h) =
+              f32x4{acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2],
+                    acc[db][4 * g4 + 3]};
+      }
+    }
+    return;
+  }
   if (qok) {
     const float sc = a.softmax_scale;
     uint16_t* out = a.dq + (size_t)bh * nq * D + (size_t)qi * D;
@@ -311,10 +334,54 @@ void k_dq(AttnArgs a) {
   }
 }
 
+// out[i] = bf16(scale * sum over s of part[s * stride + i]) for i < n (n a
+// multiple of 4), the splits added in order; 4 values per thread, the
+// splits read 8 at a time so that their loads are in flight together.
+__global__ __launch_bounds__(256) void k_sum_parts(const float* part, int splits, int64_t stride,
+                                                   int64_t n, float scale, uint16_t* out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = s0 + k < splits ? *reinterpret_cast<const f32x4*>(part + (s0 + k) * stride + i)
+                             : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += v[k];
+  }
+  *reinterpret_cast<u32x2*>(out + i) = u32x2{pack_bf16x2(acc[0] * scale, acc[1] * scale),
+                                             pack_bf16x2(acc[2] * scale, acc[3] * scale)};
+}
+
 }  // namespace
+
+hipError_t launch_sum_parts(const float* part, int splits, int64_t stride, int64_t n, float scale,
+                            uint16_t* out, hipStream_t stream, const LaunchEvents* ev) {
+  const dim3 grid((unsigned)((n / 4 + 255) / 256)), block(256);
+  return launch(k_sum_parts, grid, block, stream, ev, part, splits, stride, n, scale, out);
+}
 
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream,
                          const LaunchEvents* ev) {
+  if (a.dq_splits > 1) {
+    // split over keys, then the reduction (timed as one span)
+    const dim3 grid((unsigned)(((a.nq + kDqBM - 1) / kDqBM) * a.bh), (unsigned)a.dq_splits);
+    const dim3 block(256);
+    const LaunchEvents e0 = {ev ? ev->start : nullptr, nullptr};
+    const LaunchEvents e1 = {nullptr, ev ? ev->stop : nullptr};
+    const hipError_t st =
+        head_dim == 128
+            ? (a.causal ? launch(k_dq<128, true>, grid, block, stream, ev ? &e0 : nullptr, a)
+                        : launch(k_dq<128, false>, grid, block, stream, ev ? &e0 : nullptr, a))
+            : (a.causal ? launch(k_dq<64, true>, grid, block, stream, ev ? &e0 : nullptr, a)
+                        : launch(k_dq<64, false>, grid, block, stream, ev ? &e0 : nullptr, a));
+    if (st != hipSuccess) return st;
+    const int64_t n = (int64_t)a.bh * a.nq * head_dim;
+    return launch_sum_parts(a.dq_part, a.dq_splits, n, n, a.softmax_scale, a.dq, stream,
+                            ev ? &e1 : nullptr);
+  }
   const dim3 grid((unsigned)(((a.nq + kDqBM - 1) / kDqBM) * a.bh)), block(256);
   if (head_dim == 128)
     return a.causal ? launch(k_dq<128, true>, grid, block, stream, ev, a)

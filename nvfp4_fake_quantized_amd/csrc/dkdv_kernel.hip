@@ -40,6 +40,10 @@
 // nkv) evaluate them, in X (P = 0, hence dS = 0 and P^F = 0); causal
 // sub-tiles entirely above the diagonal are skipped by both waves.  Loads
 // beyond the ends read zeros and stores stop at the ends.
+//
+// When the key blocks cannot fill the chip, the query sub-tiles of each
+// block are split over blockIdx.y: each split writes its fp32 dK and dV
+// partials, and k_sum_parts adds the splits in order (deterministic).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -150,11 +154,17 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
 
   // sub-tiles: queries below the workgroup's first key are masked (causal)
   const int qfirst = CAUSAL ? kblk0 : 0;
-  const int nsub = qfirst < nq ? (nq - qfirst + kSub - 1) / kSub : 0;
+  const int nsub_all = qfirst < nq ? (nq - qfirst + kSub - 1) / kSub : 0;
+  // this workgroup's sub-tiles: all of them, or run blockIdx.y of the split
+  const int QSPL = a.dkdv_splits > 1 ? a.dkdv_splits : 1;
+  const int per = (nsub_all + QSPL - 1) / QSPL;
+  const int js0 = QSPL > 1 ? (int)blockIdx.y * per : 0;
+  const int nsub = QSPL > 1 ? max(0, min(nsub_all - js0, per)) : nsub_all;
+  const int qstart = qfirst + kSub * js0;  // first query of sub-tile 0
   const int nsteps = nsub > 0 ? nsub + 1 : 0;
   // a sub-tile entirely above the pair's keys (causal) is skipped by both waves
   auto skipped = [&](int j) __attribute__((always_inline)) {
-    return CAUSAL && qfirst + kSub * j + kSub - 1 < kw0;
+    return CAUSAL && qstart + kSub * j + kSub - 1 < kw0;
   };
 
   auto ring = [&](int slot, int tensor) __attribute__((always_inline)) {
@@ -208,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
     }
     auto issue_sub = [&](int j, auto stag) __attribute__((always_inline)) {
       constexpr int S = decltype(stag)::value;  // ring slot
-      const int q0 = qfirst + kSub * j;
+      const int q0 = qstart + kSub * j;
       const int rows = min(nq - q0, kSub);
       const uint32_t bytes = (uint32_t)(rows * D) * 2u;  // rows past nq arrive as zeros
       const u32x4 dq_ = buf_desc(Q + (size_t)q0 * D, bytes);
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
         // this lane: query qj, keys kw0 + 16h + v; under MASK key v is valid
         // when v < lim (below nkv, not above the query, query below nq)
         if (MASK) {
-          const int qj = qfirst + kSub * j + l32;
+          const int qj = qstart + kSub * j + l32;
           lim = (CAUSAL ? min(nkv, qj + 1) : nkv) - (kw0 + 16 * h);
           lim = qj < nq ? lim : 0;
         }
@@ -378,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
       if (stage) issue_sub(j + 2, IntTag<(R + 2) % kRing>());
       const bool do_m = j + 1 < nsub && !skipped(j + 1);
       const bool do_v = j < nsub && !skipped(j);
-      const int q0 = qfirst + kSub * j;
+      const int q0 = qstart + kSub * j;
       // masks: keys past nkv, the query tail, the causal diagonal
       const bool mask = keys_tail || q0 + kSub > nq || (CAUSAL && q0 < kw0 + 31);
       if (do_m && do_v) {
@@ -479,6 +489,24 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
     }
 
     // accumulators: lane -> d = 32*db + l32, VGPR v -> key kw0 + 8*(v/4) + 4h + v%4
+    if (QSPL > 1) {
+      // this split's unscaled dK and dV rows (a split without queries stores zeros)
+      const size_t tstride = (size_t)a.bh * nkv * D;  // one tensor of the split
+      float* PK = a.dkdv_part + 2 * (size_t)blockIdx.y * tstride + (size_t)bh * nkv * D;
+      float* PV = PK + tstride;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kw0 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (key < nkv) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            PK[(size_t)key * D + 32 * db + l32] = dk[db][v];
+            PV[(size_t)key * D + 32 * db + l32] = dv[db][v];
+          }
+        }
+      }
+      return;
+    }
     const float vsc = UNIT_P ? 1.0f : 1.0f / a.p_scale;
     const float ksc = a.softmax_scale;
     uint16_t* DV = a.dv + (size_t)bh * nkv * D;
@@ -499,7 +527,26 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_d(const AttnArgs& a, hipStream_t stream, const LaunchEvents* ev) {
-  const dim3 grid((unsigned)(((a.nkv + kKeys - 1) / kKeys) * a.bh)), block(kThreads);
+  const dim3 block(kThreads);
+  const unsigned kblocks = (unsigned)(((a.nkv + kKeys - 1) / kKeys) * a.bh);
+  if (a.dkdv_splits > 1) {
+    // split over queries, then the reductions of dK and dV (one timed span)
+    const dim3 grid(kblocks, (unsigned)a.dkdv_splits);
+    const LaunchEvents e0 = {ev ? ev->start : nullptr, nullptr};
+    const LaunchEvents e1 = {nullptr, ev ? ev->stop : nullptr};
+    const hipError_t st =
+        a.p_scale == 1.0f
+            ? launch(k_dkdv<D, CAUSAL, true>, grid, block, stream, ev ? &e0 : nullptr, a)
+            : launch(k_dkdv<D, CAUSAL, false>, grid, block, stream, ev ? &e0 : nullptr, a);
+    if (st != hipSuccess) return st;
+    const int64_t n = (int64_t)a.bh * a.nkv * D;
+    const hipError_t sk = launch_sum_parts(a.dkdv_part, a.dkdv_splits, 2 * n, n, a.softmax_scale,
+                                           a.dk, stream, nullptr);
+    if (sk != hipSuccess) return sk;
+    return launch_sum_parts(a.dkdv_part + n, a.dkdv_splits, 2 * n, n, 1.0f / a.p_scale, a.dv,
+                            stream, ev ? &e1 : nullptr);
+  }
+  const dim3 grid(kblocks);
   if (a.p_scale == 1.0f) return launch(k_dkdv<D, CAUSAL, true>, grid, block, stream, ev, a);
   return launch(k_dkdv<D, CAUSAL, false>, grid, block, stream, ev, a);
 }

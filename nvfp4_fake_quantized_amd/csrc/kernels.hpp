@@ -66,6 +66,13 @@ struct AttnArgs {
   float* ml_part;         // (BH, kv_splits, nq, 2): max (log2 units), sum
   int kv_splits;          // 0 or 1: no split
   int kv_decode;          // 1: 32-query tiles (k_fwd_dec), kv_splits >= 1 key runs
+  // backward over few tiles: the key loop of k_dq split over dq_splits
+  // workgroups and the query loop of k_dkdv over dkdv_splits, each writing
+  // fp32 partial sums that a reduction adds up in a fixed order
+  float* dq_part;         // (dq_splits, BH, nq, D)
+  float* dkdv_part;       // (dkdv_splits, 2, BH, nkv, D): dK, then dV, unscaled
+  int dq_splits;          // 0 or 1: no split
+  int dkdv_splits;
   int bh;                 // batch * heads
   int nq, nkv;
   int causal;
@@ -111,6 +118,9 @@ hipError_t launch_fwd_out(const AttnArgs& a, int head_dim, hipStream_t stream,
                           const LaunchEvents* ev = nullptr);
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream,
                          const LaunchEvents* ev = nullptr);
+// out[i] = bf16(scale * sum_s part[s * stride + i]), i < n (n % 4 == 0).
+hipError_t launch_sum_parts(const float* part, int splits, int64_t stride, int64_t n, float scale,
+                            uint16_t* out, hipStream_t stream, const LaunchEvents* ev = nullptr);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream,
                            const LaunchEvents* ev = nullptr);
 // Sustained bf16 MFMA rate probe: blocks of 256 threads, each thread reading

@@ -76,3 +76,22 @@ def fwd_plan(b: int, h: int, nq: int, nkv: int, causal: bool):
         return 1, False
     s = min((512 + wgs - 1) // wgs, ktiles // 4)
     return (s if s >= 2 else 1), False
+
+
+def bwd_plan(b: int, h: int, nq: int, nkv: int):
+    """The library's documented split of the backward loops for small
+    problems: (dQ key-loop splits, dK/dV query-loop splits).  dK/dV splits
+    when the key blocks of 128 over all heads number fewer than 256, into
+    min(ceil(256 / key blocks), query sub-tiles of 32 / 4); dQ when the query
+    blocks of 128 number fewer than 256, into min(ceil(512 / query blocks),
+    key tiles of 32 / 4); a split below 2 is none."""
+    bh = b * h
+    kblocks, qblocks = bh * ((nkv + 127) // 128), bh * ((nq + 127) // 128)
+    dq = dkdv = 1
+    if kblocks < 256:
+        s = min((256 + kblocks - 1) // kblocks, ((nq + 31) // 32) // 4)
+        dkdv = s if s >= 2 else 1
+    if qblocks < 256:
+        s = min((512 + qblocks - 1) // qblocks, ((nkv + 31) // 32) // 4)
+        dq = s if s >= 2 else 1
+    return dq, dkdv

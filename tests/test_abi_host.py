@@ -16,7 +16,7 @@ import re
 import pytest
 
 from nvfp4_fake_quantized_amd import binding as B
-from tests._util import fwd_plan
+from tests._util import bwd_plan, fwd_plan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
@@ -286,6 +286,30 @@ def test_instrumentation_entry_points_reject_bad_arguments_before_launch():
                  (0, out, 1, 1 << 21)]:
         assert lib.attnqat_probe_lds_write(*args, None) == B.ERR_INVALID_ARGUMENT, args
     assert lib.attnqat_probe_lds_write(0, _vp(0x40008), 1, 1, None) == B.ERR_MISALIGNED
+
+
+def test_backward_workspace_holds_the_split_partials():
+    """The backward's workspace grows by the fp32 partial sums of its split
+    loops on small problems: s_q * B*H*Nq*D*4 bytes for dQ and
+    s_kv * 2 * B*H*Nkv*D*4 for dK/dV (each part 256-byte aligned), and only
+    then; large problems (the reference shape, the long workloads) split
+    nothing."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    cases = [(1, 16, 1024, 1024, 128, False), (1, 4, 1024, 1024, 64, True), (1, 1, 128, 128, 64, False),
+             (1, 2, 333, 333, 128, True), (1, 16, 4096, 4096, 128, False), (2, 40, 8192, 8192, 128, True),
+             (1, 40, 32760, 32760, 128, False), (1, 2, 100, 260, 128, False), (1, 1, 1, 5, 128, False),
+             (2, 3, 640, 1000, 64, False)]
+    kinds = set()
+    for b, h, nq, nkv, d, causal in cases:
+        p = B.make_problem(b, h, nq, nkv, d, causal, d ** -0.5)
+        sq, skv = bwd_plan(b, h, nq, nkv)
+        kinds.add((sq > 1, skv > 1))
+        bh = b * h
+        base = (al(bh * nq * d * 2) + 2 * al(bh * nkv * d * 2) + al(bh * nq * d // 16)
+                + 2 * al(bh * nkv * d // 16) + al(bh * nq * 4))
+        extra = (al(sq * bh * nq * d * 4) if sq > 1 else 0) + (al(skv * 2 * bh * nkv * d * 4) if skv > 1 else 0)
+        assert B.attnqat_bwd_workspace_bytes(p) == base + extra, (b, h, nq, nkv, d, causal, sq, skv)
+    assert kinds == {(True, True), (False, False), (True, False)}
 
 
 def test_forward_workspace_holds_the_key_split_partials():
