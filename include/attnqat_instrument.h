@@ -23,13 +23,14 @@ extern "C" {
  * hipEventElapsedTime(events[2i], events[2i+1]) without synchronizing inside
  * the call and without extra packets or gaps between the kernels.
  * attnqat_fwd_timed: 4 events; kernel 0 the Q/K/V fake-quant, kernel 1 the
- *   attention forward (when the forward splits the keys -- see attnqat_fwd --
- *   its pair spans the split launch and the merge launch).
+ *   attention forward (when the forward covers the keys in runs -- see
+ *   attnqat_fwd -- its pair spans the attention launch and the merge launch).
  * attnqat_fwd_quantized_timed: 6 events; kernels 0 and 1 as above, kernel 2
  *   the second (quantized-output) pass.
  * attnqat_bwd_timed: 6 events; kernel 0 the preprocessing (Q fake-quant fused
  *   with delta, and K/V fake-quant, in one launch), kernel 1 dQ, kernel 2
- *   dK/dV.
+ *   dK/dV (on small problems with split loops -- see attnqat_bwd -- its pair
+ *   also spans the launch that adds the partial sums of dQ, dK and dV).
  * A NULL array or NULL event is ATTNQAT_ERR_INVALID_ARGUMENT. */
 ATTNQAT_API int attnqat_fwd_timed(const attnqat_problem* p, const void* q, const void* k,
                                   const void* v, void* o_hp, float* lse, void* workspace,

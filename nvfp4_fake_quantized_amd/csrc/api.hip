@@ -446,10 +446,27 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   a.dkdv_splits = L.dkdv_splits;
   if (L.dq_splits > 1) a.dq_part = at<float>(workspace, L.dq_part);
   if (L.dkdv_splits > 1) a.dkdv_part = at<float>(workspace, L.dkdv_part);
-  // 3) dQ and 4) dK/dV (each with its reduction when split)
+  // 3) dQ and 4) dK/dV; on small problems their split loops leave fp32
+  // partial sums, added by one k_sum_parts launch (timed with dK/dV)
+  attnqat::SumJob sums[3];
+  int nsums = 0;
+  const int64_t nqd = bh * p->seqlen_q * D, nkd = bh * p->seqlen_kv * D;
+  if (L.dq_splits > 1)
+    sums[nsums++] = {a.dq_part, a.dq, nqd, nqd, L.dq_splits, p->softmax_scale};
+  if (L.dkdv_splits > 1) {
+    sums[nsums++] = {a.dkdv_part, a.dk, 2 * nkd, nkd, L.dkdv_splits, p->softmax_scale};
+    sums[nsums++] = {a.dkdv_part + nkd, a.dv, 2 * nkd, nkd, L.dkdv_splits, 1.0f / p->p_scale};
+  }
+  const attnqat::LaunchEvents* e2 = timing(ev, 2);
+  const attnqat::LaunchEvents e2a = {e2 ? e2->start : nullptr, nullptr};
+  const attnqat::LaunchEvents e2b = {nullptr, e2 ? e2->stop : nullptr};
   if (attnqat::launch_bwd_dq(a, p->head_dim, stream, timing(ev, 1)) != hipSuccess)
     return ATTNQAT_ERR_HIP;
-  if (attnqat::launch_bwd_dkdv(a, p->head_dim, stream, timing(ev, 2)) != hipSuccess)
+  if (attnqat::launch_bwd_dkdv(a, p->head_dim, stream, nsums > 0 && e2 ? &e2a : e2) !=
+      hipSuccess)
+    return ATTNQAT_ERR_HIP;
+  if (nsums > 0 &&
+      attnqat::launch_sum_parts(sums, nsums, stream, e2 ? &e2b : nullptr) != hipSuccess)
     return ATTNQAT_ERR_HIP;
   return ATTNQAT_OK;
 }

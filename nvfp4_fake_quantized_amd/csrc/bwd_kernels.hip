@@ -21,7 +21,8 @@
 // mask, keys >= Nkv get P = 0, loads beyond the ends read zeros and stores
 // stop at the ends.  When the query blocks cannot fill the chip, the key
 // tiles of each block are split over blockIdx.y: each split writes its fp32
-// dQ^T partial, and k_sum_parts adds the splits in order (deterministic).
+// dQ^T partial, and k_sum_parts (launched after k_dkdv, with its sums) adds
+// the splits in order (deterministic).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -334,11 +335,18 @@ void k_dq(AttnArgs a) {
   }
 }
 
-// out[i] = bf16(scale * sum over s of part[s * stride + i]) for i < n (n a
-// multiple of 4), the splits added in order; 4 values per thread, the
-// splits read 8 at a time so that their loads are in flight together.
-__global__ __launch_bounds__(256) void k_sum_parts(const float* part, int splits, int64_t stride,
-                                                   int64_t n, float scale, uint16_t* out) {
+// The sums of SumJob, job blockIdx.y: 4 values per thread, the splits added
+// in order and read 8 at a time so that their loads are in flight together.
+struct SumJobs {
+  SumJob j[3];
+};
+__global__ __launch_bounds__(256) void k_sum_parts(SumJobs jobs) {
+  const SumJob& jb = jobs.j[blockIdx.y];
+  const float* part = jb.part;
+  const int splits = jb.splits;
+  const int64_t stride = jb.stride, n = jb.n;
+  const float scale = jb.scale;
+  uint16_t* out = jb.out;
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -357,32 +365,25 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* part, int splits
 
 }  // namespace
 
-hipError_t launch_sum_parts(const float* part, int splits, int64_t stride, int64_t n, float scale,
-                            uint16_t* out, hipStream_t stream, const LaunchEvents* ev) {
-  const dim3 grid((unsigned)((n / 4 + 255) / 256)), block(256);
-  return launch(k_sum_parts, grid, block, stream, ev, part, splits, stride, n, scale, out);
+hipError_t launch_sum_parts(const SumJob* jobs, int njobs, hipStream_t stream,
+                            const LaunchEvents* ev) {
+  if (njobs < 1 || njobs > 3) return hipErrorInvalidValue;
+  SumJobs js = {};
+  int64_t nmax = 0;
+  for (int i = 0; i < njobs; ++i) {
+    js.j[i] = jobs[i];
+    nmax = jobs[i].n > nmax ? jobs[i].n : nmax;
+  }
+  const dim3 grid((unsigned)((nmax / 4 + 255) / 256), (unsigned)njobs), block(256);
+  return launch(k_sum_parts, grid, block, stream, ev, js);
 }
 
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream,
                          const LaunchEvents* ev) {
-  if (a.dq_splits > 1) {
-    // split over keys, then the reduction (timed as one span)
-    const dim3 grid((unsigned)(((a.nq + kDqBM - 1) / kDqBM) * a.bh), (unsigned)a.dq_splits);
-    const dim3 block(256);
-    const LaunchEvents e0 = {ev ? ev->start : nullptr, nullptr};
-    const LaunchEvents e1 = {nullptr, ev ? ev->stop : nullptr};
-    const hipError_t st =
-        head_dim == 128
-            ? (a.causal ? launch(k_dq<128, true>, grid, block, stream, ev ? &e0 : nullptr, a)
-                        : launch(k_dq<128, false>, grid, block, stream, ev ? &e0 : nullptr, a))
-            : (a.causal ? launch(k_dq<64, true>, grid, block, stream, ev ? &e0 : nullptr, a)
-                        : launch(k_dq<64, false>, grid, block, stream, ev ? &e0 : nullptr, a));
-    if (st != hipSuccess) return st;
-    const int64_t n = (int64_t)a.bh * a.nq * head_dim;
-    return launch_sum_parts(a.dq_part, a.dq_splits, n, n, a.softmax_scale, a.dq, stream,
-                            ev ? &e1 : nullptr);
-  }
-  const dim3 grid((unsigned)(((a.nq + kDqBM - 1) / kDqBM) * a.bh)), block(256);
+  // split over keys: fp32 partials, summed by the caller's k_sum_parts launch
+  const dim3 grid((unsigned)(((a.nq + kDqBM - 1) / kDqBM) * a.bh),
+                  (unsigned)(a.dq_splits > 1 ? a.dq_splits : 1));
+  const dim3 block(256);
   if (head_dim == 128)
     return a.causal ? launch(k_dq<128, true>, grid, block, stream, ev, a)
                     : launch(k_dq<128, false>, grid, block, stream, ev, a);

@@ -43,7 +43,8 @@
 //
 // When the key blocks cannot fill the chip, the query sub-tiles of each
 // block are split over blockIdx.y: each split writes its fp32 dK and dV
-// partials, and k_sum_parts adds the splits in order (deterministic).
+// partials, and k_sum_parts (launched next, with dQ's sums) adds the splits
+// in order (deterministic).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -527,26 +528,10 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_d(const AttnArgs& a, hipStream_t stream, const LaunchEvents* ev) {
+  // split over queries: fp32 partials, summed by the caller's k_sum_parts launch
   const dim3 block(kThreads);
-  const unsigned kblocks = (unsigned)(((a.nkv + kKeys - 1) / kKeys) * a.bh);
-  if (a.dkdv_splits > 1) {
-    // split over queries, then the reductions of dK and dV (one timed span)
-    const dim3 grid(kblocks, (unsigned)a.dkdv_splits);
-    const LaunchEvents e0 = {ev ? ev->start : nullptr, nullptr};
-    const LaunchEvents e1 = {nullptr, ev ? ev->stop : nullptr};
-    const hipError_t st =
-        a.p_scale == 1.0f
-            ? launch(k_dkdv<D, CAUSAL, true>, grid, block, stream, ev ? &e0 : nullptr, a)
-            : launch(k_dkdv<D, CAUSAL, false>, grid, block, stream, ev ? &e0 : nullptr, a);
-    if (st != hipSuccess) return st;
-    const int64_t n = (int64_t)a.bh * a.nkv * D;
-    const hipError_t sk = launch_sum_parts(a.dkdv_part, a.dkdv_splits, 2 * n, n, a.softmax_scale,
-                                           a.dk, stream, nullptr);
-    if (sk != hipSuccess) return sk;
-    return launch_sum_parts(a.dkdv_part + n, a.dkdv_splits, 2 * n, n, 1.0f / a.p_scale, a.dv,
-                            stream, ev ? &e1 : nullptr);
-  }
-  const dim3 grid(kblocks);
+  const dim3 grid((unsigned)(((a.nkv + kKeys - 1) / kKeys) * a.bh),
+                  (unsigned)(a.dkdv_splits > 1 ? a.dkdv_splits : 1));
   if (a.p_scale == 1.0f) return launch(k_dkdv<D, CAUSAL, true>, grid, block, stream, ev, a);
   return launch(k_dkdv<D, CAUSAL, false>, grid, block, stream, ev, a);
 }

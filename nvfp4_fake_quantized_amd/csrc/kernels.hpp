@@ -118,9 +118,18 @@ hipError_t launch_fwd_out(const AttnArgs& a, int head_dim, hipStream_t stream,
                           const LaunchEvents* ev = nullptr);
 hipError_t launch_bwd_dq(const AttnArgs& a, int head_dim, hipStream_t stream,
                          const LaunchEvents* ev = nullptr);
-// out[i] = bf16(scale * sum_s part[s * stride + i]), i < n (n % 4 == 0).
-hipError_t launch_sum_parts(const float* part, int splits, int64_t stride, int64_t n, float scale,
-                            uint16_t* out, hipStream_t stream, const LaunchEvents* ev = nullptr);
+// One sum of split partials: out[i] = bf16(scale * sum_s part[s * stride + i])
+// for i < n (n % 4 == 0), s = 0 .. splits-1 in order.
+struct SumJob {
+  const float* part;
+  uint16_t* out;
+  int64_t stride, n;
+  int splits;
+  float scale;
+};
+// Up to three sums (dQ, dK, dV) in one launch.
+hipError_t launch_sum_parts(const SumJob* jobs, int njobs, hipStream_t stream,
+                            const LaunchEvents* ev = nullptr);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int head_dim, hipStream_t stream,
                            const LaunchEvents* ev = nullptr);
 // Sustained bf16 MFMA rate probe: blocks of 256 threads, each thread reading
