@@ -153,11 +153,11 @@ ATTNQAT_API int attnqat_nvfp4_pack(const void* x, uint8_t* codes, uint8_t* scale
  * In: q (B,H,Nq,D), k, v (B,H,Nkv,D) bf16.  Out: o_hp (B,H,Nq,D) bf16,
  * lse (B,H,Nq) fp32.  The workspace (>= attnqat_fwd_workspace_bytes) holds
  * Q^/K^/V^ and their scales afterwards (attnqat_workspace_layout).
- * Few queries against long K/V (non-causal only): with at most 32 queries
- * per head, a kernel with 32-query tiles deals the key tiles of each head
- * out to `splits` = min(ceil(512 / (B*H)), max(1, key tiles of 32 / 8))
- * workgroups; otherwise, when the 128-query tiles over all heads number
- * fewer than 256, the keys are split over workgroups (splits =
+ * Few queries, or a short problem: non-causal with at most 32 queries per
+ * head, a kernel with 32-query tiles deals the key tiles of each head out
+ * to `splits` = min(ceil(512 / (B*H)), max(1, key tiles of 32 / 8))
+ * workgroups; otherwise (causal too), when the 128-query tiles over all
+ * heads number fewer than 256, the keys are split over workgroups (splits =
  * min(ceil(512 / tiles), key tiles / 4), used when >= 2).  Either way a
  * second launch merges the partial results, and the workspace size then
  * includes them (B*H*Nq*splits*(4*D + 8) bytes, after the parts named by

@@ -84,15 +84,15 @@ BwdPlan bwd_plan(const attnqat_problem* p) {
   return b;
 }
 
-// How the forward covers the keys (non-causal problems only; a causal
-// forward always runs one workgroup per 128 queries over all its keys):
-//  * at most 32 queries per head: the 32-query-tile forward, its key tiles
+// How the forward covers the keys:
+//  * non-causal, at most 32 queries per head: the 32-query-tile forward, its key tiles
 //    dealt out to `splits` workgroups of 4 waves per head, enough for about
 //    512 workgroups (two per CU) with at least 2 key tiles (64 keys) per
 //    wave;
-//  * otherwise, when the 128-query tiles of all heads cannot fill the chip's
-//    256 CUs: the keys are split so that about 512 workgroups run, with at
-//    least 4 key tiles (128 keys) per split;
+//  * otherwise (causal too), when the 128-query tiles of all heads cannot
+//    fill the chip's 256 CUs: the keys are split so that about 512
+//    workgroups run, with at least 4 key tiles (128 keys) per split (causal:
+//    of the last query tile's keys; earlier tiles' later splits get none);
 // Both write per-run partial results (unnormalized O in fp32, row max and
 // sum) of bh * splits * Nq * (4 D + 8) bytes to the forward workspace.
 struct FwdPlan {
@@ -100,10 +100,9 @@ struct FwdPlan {
   int decode;
 };
 FwdPlan fwd_plan(const attnqat_problem* p) {
-  if (p->causal) return {1, 0};
   const int64_t bh = (int64_t)p->batch * p->heads;
   const int64_t ktiles = ((int64_t)p->seqlen_kv + 31) / 32;
-  if (p->seqlen_q <= 32) {
+  if (!p->causal && p->seqlen_q <= 32) {
     const int64_t want = (512 + bh - 1) / bh;
     const int64_t cap = ktiles / 8 > 1 ? ktiles / 8 : 1;
     return {(int)(want < cap ? want : cap), 1};

@@ -28,10 +28,12 @@
 //    (and the key loop ends at the workgroup's last query); the diagonal
 //    tile keeps the elementwise key <= query mask; keys >= Nkv are masked
 //    and rows >= Nq are never stored (non-aligned tails);
-//  * split over keys (non-causal, when the query tiles alone cannot fill the
-//    chip: few queries against long K/V): blockIdx.y picks a run of key
-//    tiles; each split stores its unnormalized O^T (fp32) with its row max
-//    and sum, and k_fwd_combine merges the splits into O_hp and lse.
+//  * split over keys (when the query tiles alone cannot fill the chip: few
+//    queries against long K/V, or a short causal problem): blockIdx.y picks
+//    a run of the workgroup's key tiles; each split stores its unnormalized
+//    O^T (fp32) with its row max and sum (a split whose keys all lie above
+//    the causal diagonal stores max -inf and sum 0), and k_fwd_combine
+//    merges the splits into O_hp and lse.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -175,7 +177,6 @@ __device__ __forceinline__ void fwd_softmax_pv(const f32x16& s, float& m, float&
 template <int D, bool CAUSAL, bool PACKED, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTNQAT_FWD_WAVES, 8)))
 void k_fwd(AttnArgs a) {
-  static_assert(!(CAUSAL && SPLIT), "the split over keys is for non-causal attention");
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int BN = 32;              // keys per tile
@@ -293,7 +294,7 @@ void k_fwd(AttnArgs a) {
   // Leading tiles are interior (branch-free); masks start at the first tile
   // that reaches past nkv or above the workgroup's first query (causal).
   int it_hi = min(ntiles, max(0, nkv / BN - t0));
-  if (CAUSAL) it_hi = min(it_hi, (qblk0 + 1) / BN);
+  if (CAUSAL) it_hi = min(it_hi, max(0, (qblk0 + 1) / BN - t0));
 
   if constexpr (PACKED) {
     if (ntiles > 0) {
@@ -878,15 +879,17 @@ hipError_t launch_fwd_t(const AttnArgs& a, int head_dim, hipStream_t stream,
                ? launch(k_fwd_combine<128>, cgrid, block, stream, ev ? &e1 : nullptr, a, rows)
                : launch(k_fwd_combine<64>, cgrid, block, stream, ev ? &e1 : nullptr, a, rows);
   }
-  if (a.kv_splits > 1 && !a.causal) {
+  if (a.kv_splits > 1) {
     // split over keys, then the merge (timed as one span: start of the
     // first launch to the end of the second)
     const dim3 grid(qtiles, (unsigned)a.kv_splits);
-    const hipError_t st = head_dim == 128
-                              ? launch(k_fwd<128, false, PACKED, true>, grid, block, stream,
-                                       ev ? &e0 : nullptr, a)
-                              : launch(k_fwd<64, false, PACKED, true>, grid, block, stream,
-                                       ev ? &e0 : nullptr, a);
+    const LaunchEvents* es = ev ? &e0 : nullptr;
+    const hipError_t st =
+        head_dim == 128
+            ? (a.causal ? launch(k_fwd<128, true, PACKED, true>, grid, block, stream, es, a)
+                        : launch(k_fwd<128, false, PACKED, true>, grid, block, stream, es, a))
+            : (a.causal ? launch(k_fwd<64, true, PACKED, true>, grid, block, stream, es, a)
+                        : launch(k_fwd<64, false, PACKED, true>, grid, block, stream, es, a));
     if (st != hipSuccess) return st;
     return head_dim == 128
                ? launch(k_fwd_combine<128>, cgrid, block, stream, ev ? &e1 : nullptr, a, rows)

@@ -63,13 +63,12 @@ def fwd_plan(b: int, h: int, nq: int, nkv: int, causal: bool):
     """The library's documented key coverage of a forward: (key runs, whether
     the 32-query-tile path runs).  Non-causal with at most 32 queries per
     head: 32-query tiles, the key tiles dealt out to
-    min(ceil(512 / bh), max(1, key tiles / 8)) workgroups per head.  Otherwise the keys are split when fewer than 256 query tiles of
-    128 exist, with at least 4 key tiles of 32 per split, for about 512
-    workgroups."""
-    if causal:
-        return 1, False
+    min(ceil(512 / bh), max(1, key tiles / 8)) workgroups per head.
+    Otherwise (causal too) the keys are split when fewer than 256 query
+    tiles of 128 exist, with at least 4 key tiles of 32 per split, for about
+    512 workgroups."""
     bh, ktiles = b * h, (nkv + 31) // 32
-    if nq <= 32:
+    if not causal and nq <= 32:
         return min((512 + bh - 1) // bh, max(1, ktiles // 8)), True
     wgs = bh * ((nq + 127) // 128)
     if wgs >= 256:

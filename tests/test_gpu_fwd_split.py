@@ -1,9 +1,11 @@
-"""The forward over few queries: split over keys, or in 32-query tiles.
+"""The forward over few queries or a short problem: split over keys, or in
+32-query tiles.
 
-When the 128-query tiles of all heads cannot fill the chip and the problem is
-non-causal, attnqat_fwd and attnqat_fwd_packed split the keys over
-workgroups; with at most 32 queries per head they run 32-query tiles whose
-four waves take separate key runs.  Either way the runs' partial results
+When the 128-query tiles of all heads cannot fill the chip, attnqat_fwd and
+attnqat_fwd_packed split the keys over workgroups (causal problems too: a
+split whose keys all lie above a query tile's diagonal contributes nothing);
+non-causal problems with at most 32 queries per head run 32-query tiles
+whose four waves take separate key runs.  Either way the runs' partial results
 (unnormalized O, row max and row sum) are merged into O_hp and lse.  The
 result is the same QAT forward ("NVFP4 Attention QAT Backward", §Overview
 formula block; lse natural log, §Tensor contract), so it is checked against
@@ -53,16 +55,32 @@ CASES = [  # b, h, nq, nkv, d
 ]
 
 
+CAUSAL_CASES = [  # b, h, n, d: short causal problems, split over keys
+    (1, 4, 1024, 64),   # 8 splits: the first query tiles' later splits get no keys
+    (1, 2, 300, 128),   # 2 splits, ragged tail
+]
+
+
+@pytest.mark.parametrize("b,h,n,d", CAUSAL_CASES)
+def test_short_causal_forward_matches_oracle(b, h, n, d):
+    _run(b, h, n, n, d, causal=True)
+
+
 @pytest.mark.parametrize("b,h,nq,nkv,d", CASES)
 def test_few_query_forward_matches_oracle(b, h, nq, nkv, d):
+    _run(b, h, nq, nkv, d, causal=False)
+
+
+def _run(b, h, nq, nkv, d, causal):
     scale = d ** -0.5
     q, k, v = _inputs(b, h, nq, nkv, d, seed=nq * 7 + nkv)
-    S, dec = fwd_plan(b, h, nq, nkv, False)
+    S, dec = fwd_plan(b, h, nq, nkv, causal)
     assert dec or S > 1, "the case must split the keys or take the 32-query tiles"
     kind = "32-query tiles" if dec else "split"
-    print(f"[few-query fwd] B{b} H{h} Nq{nq} Nkv{nkv} D{d}: {kind}, {S} key runs", flush=True)
+    print(f"[few-query fwd] B{b} H{h} Nq{nq} Nkv{nkv} D{d} causal={causal}: {kind}, "
+          f"{S} key runs", flush=True)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
-    p = B.problem_for(qd, kd, False, scale)
+    p = B.problem_for(qd, kd, causal, scale)
     ws = torch.empty(B.attnqat_fwd_workspace_bytes(p), dtype=torch.uint8, device=DEV)
     o = torch.empty_like(qd)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=DEV)
@@ -77,8 +95,8 @@ def test_few_query_forward_matches_oracle(b, h, nq, nkv, d):
         for hi in range(h):
             qh, kh, vh = quantize_qkv(q[bi, hi].double().numpy(), k[bi, hi].double().numpy(),
                                       v[bi, hi].double().numpy())
-            o64, l64 = qat_forward_head(qh, kh, vh, scale, False, quantize=False)
-            tag = f"{kind} Nq{nq} Nkv{nkv} D{d}"
+            o64, l64 = qat_forward_head(qh, kh, vh, scale, causal, quantize=False)
+            tag = f"{kind} Nq{nq} Nkv{nkv} D{d} causal={causal}"
             check_close(o[bi, hi].cpu(), o64, f"{tag} O_hp[{bi},{hi}]")
             check_close(lse[bi, hi].cpu(), l64, f"{tag} lse[{bi},{hi}]")
             check_close(o2[bi, hi].cpu(), o64, f"{tag} packed O_hp[{bi},{hi}]")
