@@ -49,7 +49,7 @@ def test_split_backward_matches_oracle(b, h, nq, nkv, d, causal, heads):
     assert sq > 1 or skv > 1, "the case must split a backward loop"
     q, k, v, do = _synthetic(b, h, nq, nkv, d, seed=7 * nq + nkv + d)
     run_full_case(q, k, v, do, causal, 1.0 / math.sqrt(d), heads=heads,
-                  label=f"split dQ x{sq} dKdV x{skv}")
+                  label=f"split loops q{sq} kv{skv}")
 
 
 def test_split_backward_is_bitwise_repeatable():
