@@ -361,9 +361,17 @@ int run_fwd_packed(const attnqat_problem* p, const void* q, const uint8_t* k_cod
 
   const int64_t bh = (int64_t)p->batch * p->heads;
   uint16_t* qh = at<uint16_t>(workspace, L.q_hat);
-  QuantJob job = {q, qh, at<uint8_t>(workspace, L.q_scale), bh * p->seqlen_q * p->head_dim / 16};
-  if (attnqat::launch_quant_bf16(&job, 1, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  uint8_t* qs = at<uint8_t>(workspace, L.q_scale);
   AttnArgs a = {};
+  if (L.kv_decode) {
+    // the 32-query-tile kernel fake-quantizes Q itself (one launch fewer)
+    a.q_in = static_cast<const uint16_t*>(q);
+    a.q_hat_out = qh;
+    a.q_scale_out = qs;
+  } else {
+    QuantJob job = {q, qh, qs, bh * p->seqlen_q * p->head_dim / 16};
+    if (attnqat::launch_quant_bf16(&job, 1, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
+  }
   a.q_hat = qh;
   a.k_codes = k_codes;
   a.k_scales = k_scales;

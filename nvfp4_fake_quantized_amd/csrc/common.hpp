@@ -164,6 +164,39 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
   return k | ((__float_as_uint(x) >> 31) << 3);
 }
 
+// 16 bf16 values (two 16-byte words) as floats, and back (values exact in
+// bf16, so the low halves are dropped exactly).
+__device__ __forceinline__ void unpack_bf16x16(u32x4 lo, u32x4 hi, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_bits_to_f32(lo[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_bits_to_f32(lo[i] >> 16);
+    x[8 + 2 * i] = bf16_bits_to_f32(hi[i] & 0xFFFFu);
+    x[8 + 2 * i + 1] = bf16_bits_to_f32(hi[i] >> 16);
+  }
+}
+
+__device__ __forceinline__ void pack_bf16x16(const float* x, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // values are exact in bf16: truncation of the low half is exact
+    lo[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xFFFF0000u);
+    hi[i] = (__float_as_uint(x[8 + 2 * i]) >> 16) |
+            (__float_as_uint(x[8 + 2 * i + 1]) & 0xFFFF0000u);
+  }
+}
+
+// Quantizes 16 floats in place; returns the scale.
+__device__ __forceinline__ float fq16(float* x) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float s = e4m3_scale_from_amax(amax);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = e2m1_dequant(x[i], s);
+  return s;
+}
+
 // Faster exact path for non-negative fp32 values (the probabilities P), used
 // where the scale is shared by the 16 values one lane holds:
 //   q  = |x|/s from a two-term reciprocal: r_hi = rcp(s) and

@@ -407,12 +407,13 @@ void k_fwd(AttnArgs a) {
 // Merge of the key runs of k_fwd<..., SPLIT> and k_fwd_dec: per query row,
 // with M the largest run max and w_s = exp2(m_s - M), O_hp = sum_s w_s O_s / L
 // and lse = (M + log2 L) ln 2, L = sum_s w_s l_s.  One thread per 4 columns
-// of a row (D/4 threads per row); the runs are read 8 at a time (their loads
-// in flight together) and folded into a running max with rescaled sums.
+// of a row (D/4 threads per row); the runs are read 32 at a time (their
+// loads in flight together: one memory round trip for up to 32 runs) and
+// folded into a running max with rescaled sums.
 template <int D>
 __global__ __launch_bounds__(256) void k_fwd_combine(AttnArgs a, int64_t rows) {
   constexpr int TPR = D / 4;  // threads per row
-  constexpr int B8 = 8;       // runs per batch
+  constexpr int B8 = 32;      // runs per batch
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = g / TPR;  // bh * nq + q
   if (row >= rows) return;
@@ -590,7 +591,38 @@ void k_fwd_dec(AttnArgs a) {
   auto tile_k0 = [&](int it) __attribute__((always_inline)) { return (g + W * (n - 1 - it)) * BN; };
 
   // Q^ rows of the workgroup (rows past nq as zeros; fp16 for packed K^/V^)
-  {
+  if (PACKED && a.q_in != nullptr) {
+    // fake-quantize the raw Q rows here (one 16-value group per thread, the
+    // codec's arithmetic); the first key run writes Q^ and the scale bytes
+    constexpr int NGRP = kDecBQ * GPR;  // groups of the tile
+    for (int g = tid; g < NGRP; g += 256) {
+      const int r = g / GPR, col = 16 * (g % GPR);
+      const bool in = q0 + r < nq;
+      const size_t off = ((size_t)bh * nq + q0 + r) * D + col;
+      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+      if (in) {
+        lo = *reinterpret_cast<const u32x4*>(a.q_in + off);
+        hi = *reinterpret_cast<const u32x4*>(a.q_in + off + 8);
+      }
+      float x[16];
+      unpack_bf16x16(lo, hi, x);
+      const float sc = fq16(x);
+      if (in && sp == 0) {
+        pack_bf16x16(x, lo, hi);
+        *reinterpret_cast<u32x4*>(a.q_hat_out + off) = lo;
+        *reinterpret_cast<u32x4*>(a.q_hat_out + off + 8) = hi;
+        a.q_scale_out[off / 16] = (uint8_t)e4m3_byte(sc);
+      }
+      f16x8 h0, h1;  // exact: E2M1 codes times E4M3 scales
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        h0[e] = (_Float16)x[e];
+        h1[e] = (_Float16)x[8 + e];
+      }
+      *reinterpret_cast<f16x8*>(sQ + r * QS + col) = h0;
+      *reinterpret_cast<f16x8*>(sQ + r * QS + col + 8) = h1;
+    }
+  } else {
     const uint16_t* Q = a.q_hat + (size_t)bh * nq * D;
 #pragma unroll
     for (int c = 0; c < kDecBQ * CPR / 256; ++c) {

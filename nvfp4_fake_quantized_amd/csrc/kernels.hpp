@@ -66,6 +66,12 @@ struct AttnArgs {
   float* ml_part;         // (BH, kv_splits, nq, 2): max (log2 units), sum
   int kv_splits;          // 0 or 1: no split
   int kv_decode;          // 1: 32-query tiles (k_fwd_dec), kv_splits >= 1 key runs
+  // k_fwd_dec from packed K/V: when q_in is set, the kernel fake-quantizes
+  // its Q rows itself and the first key run of each query tile writes Q^ and
+  // its scale bytes to q_hat_out / q_scale_out
+  const uint16_t* q_in;   // (BH, nq, D) bf16
+  uint16_t* q_hat_out;
+  uint8_t* q_scale_out;   // (BH, nq, D/16)
   // backward over few tiles: the key loop of k_dq split over dq_splits
   // workgroups and the query loop of k_dkdv over dkdv_splits, each writing
   // fp32 partial sums that a reduction adds up in a fixed order

@@ -21,37 +21,6 @@ struct QuantJobs3 {
   QuantJob job[3];
 };
 
-__device__ __forceinline__ void unpack_bf16x16(u32x4 lo, u32x4 hi, float* x) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_bits_to_f32(lo[i] & 0xFFFFu);
-    x[2 * i + 1] = bf16_bits_to_f32(lo[i] >> 16);
-    x[8 + 2 * i] = bf16_bits_to_f32(hi[i] & 0xFFFFu);
-    x[8 + 2 * i + 1] = bf16_bits_to_f32(hi[i] >> 16);
-  }
-}
-
-__device__ __forceinline__ void pack_bf16x16(const float* x, u32x4& lo, u32x4& hi) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // values are exact in bf16: truncation of the low half is exact
-    lo[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xFFFF0000u);
-    hi[i] = (__float_as_uint(x[8 + 2 * i]) >> 16) |
-            (__float_as_uint(x[8 + 2 * i + 1]) & 0xFFFF0000u);
-  }
-}
-
-// Quantizes 16 floats in place; returns the scale.
-__device__ __forceinline__ float fq16(float* x) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  const float s = e4m3_scale_from_amax(amax);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = e2m1_dequant(x[i], s);
-  return s;
-}
-
 // fake_nvfp4 of group g of job J (g < J.groups)
 __device__ __forceinline__ void quant_group(const QuantJob& J, int64_t g) {
   const u32x4* src = reinterpret_cast<const u32x4*>(J.src) + 2 * g;

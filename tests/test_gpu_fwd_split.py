@@ -17,12 +17,14 @@ last run), runs and waves without keys, and both head sizes.
 """
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
 from nvfp4_fake_quantized_amd import binding as B
 from oracle.attention import qat_forward_head, quantize_qkv
-from tests._util import check_close, fwd_plan
+from oracle.nvfp4 import fake_nvfp4
+from tests._util import check_close, f64_to_bf16_bits, fwd_plan
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -89,12 +91,20 @@ def _run(b, h, nq, nkv, d, causal):
     kc, ks = B.attnqat_nvfp4_pack(kd)
     vc, vs = B.attnqat_nvfp4_pack(vd)
     o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
-    B.attnqat_fwd_packed(p, qd, kc, ks, vc, vs, o2, lse2, ws)
+    ws2 = torch.full_like(ws, 0xFF)  # the packed call must write Q^ and its scales itself
+    B.attnqat_fwd_packed(p, qd, kc, ks, vc, vs, o2, lse2, ws2)
     torch.cuda.synchronize()
+    L = B.attnqat_workspace_layout(p, B.WS_FWD)
+    nqh = b * h * nq * d
+    qhat = ws2[L["q_hat"]:L["q_hat"] + 2 * nqh].view(torch.int16).view(b, h, nq, d).cpu()
+    qsc = ws2[L["q_scale"]:L["q_scale"] + nqh // 16].view(b, h, nq, d // 16).cpu()
     for bi in range(b):
         for hi in range(h):
             qh, kh, vh = quantize_qkv(q[bi, hi].double().numpy(), k[bi, hi].double().numpy(),
                                       v[bi, hi].double().numpy())
+            ref_q, _, ref_sc, _ = fake_nvfp4(q[bi, hi].double().numpy())
+            assert np.array_equal(qhat[bi, hi].numpy().view(np.uint16), f64_to_bf16_bits(ref_q))
+            assert np.array_equal(qsc[bi, hi].numpy(), ref_sc)
             o64, l64 = qat_forward_head(qh, kh, vh, scale, causal, quantize=False)
             tag = f"{kind} Nq{nq} Nkv{nkv} D{d} causal={causal}"
             check_close(o[bi, hi].cpu(), o64, f"{tag} O_hp[{bi},{hi}]")
