@@ -468,11 +468,14 @@ __global__ __launch_bounds__(256) void k_fwd_combine(AttnArgs a, int64_t rows) {
 //    their own (no barrier in the key loop).  The W = 4 * splits waves of a
 //    head deal the key tiles out round-robin (wave g takes tiles g, g + W,
 //    ...), so that at any time the waves of a head stream neighbouring tiles
-//    (DRAM pages stay open) rather than W distant runs; each wave visits its
-//    tiles from the last one down, so the only partial tile of the head
-//    comes first and only that step evaluates a mask;
+//    rather than W distant runs (measured no faster than contiguous runs,
+//    and no slower); each wave visits its tiles from the last one down, so
+//    the only partial tile of the head comes first and only that step
+//    evaluates a mask;
 //  * the workgroup's Q^ rows sit in LDS and are read as the B operand of
-//    S^T = K^ Q^T;
+//    S^T = K^ Q^T (for packed K/V the kernel fake-quantizes the raw Q rows
+//    itself when given them, and the first key run writes Q^ and its scale
+//    bytes to the workspace);
 //  * bf16 K^ rows go global -> registers (A operands) one tile ahead, V^
 //    tiles global -> LDS directly one tile ahead;
 //  * packed K^/V^: codes and scale bytes of two tiles ahead in registers,
