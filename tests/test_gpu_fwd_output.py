@@ -99,6 +99,8 @@ def test_video_dit_workload_sampled():
     (200, 64, True, None), (333, 128, False, None), (77, 64, True, None), (130, 128, True, None),
     (100, 128, False, 260), (300, 64, False, 40), (17, 64, False, None), (16, 128, True, None),
     (1, 64, True, None), (1, 128, False, 5),
+    # few queries against long keys: the first pass takes the 32-query tiles
+    (16, 128, False, 5000), (24, 64, False, 3000),
 ])
 def test_ragged_and_degenerate_shapes(n, d, causal, nk):
     q, k, v = _synthetic(n, d, seed=n * 5 + d, nk=nk, heads=2)

@@ -54,6 +54,8 @@ CASES = [  # b, h, nq, nkv, d
     (1, 1, 17, 1, 64),        # a single key (three idle waves)
     (3, 5, 9, 2049, 128),     # the last tile holds one key
     (1, 1, 24, 65536, 64),    # long keys
+    (8, 32, 4, 2000, 128),    # 256 heads: two key runs per head
+    (4, 8, 30, 3000, 64),     # 32 heads, D = 64
 ]
 
 
