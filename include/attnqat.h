@@ -27,6 +27,10 @@
  *    whose size comes from the *_workspace_bytes queries.
  *  - Calls are asynchronous on the given stream (0 = the null stream).
  *    Buffers belong to the call until the stream has passed it.
+ *  - A call only launches kernels on its stream (no allocation, memset or
+ *    host synchronization), so calls can be recorded into a HIP graph by
+ *    stream capture and replayed; make one call on the device before the
+ *    capture (the first call looks up the device's architecture).
  *  - Arguments are validated on the host before anything is enqueued; on
  *    error nothing is launched and outputs are untouched.
  *  - Outputs are fully overwritten, never accumulated into.  Results are
