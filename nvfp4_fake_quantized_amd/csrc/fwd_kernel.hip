@@ -19,9 +19,11 @@
 //    VGPRs), so the online-softmax row statistics are per lane (plus one
 //    exchange with the lane 32 away), and P^T feeds the B operand of
 //    O^T = V^T P^T straight from registers;
-//  * the running max only triggers a rescale of the accumulator when it
-//    moved for some row of the wave (otherwise the factor is exactly 1),
-//    applied just before the next tile's P^T V^ is added;
+//  * the exponent base m (a running max) moves only when some row's tile
+//    max exceeds it by more than 2^8 (until then P stays below 256, which
+//    bf16 holds with the same relative rounding); the rescale of the
+//    accumulator that a move needs is applied just before the next tile's
+//    P^T V^ is added;
 //  * only boundary tiles (the last key tiles: tail, causal diagonal) evaluate
 //    masks; the leading tiles run a branch-free loop;
 //  * causal: tiles with every key above the wave's last query are skipped
@@ -48,6 +50,14 @@ constexpr int kFwdBM = 128;  // queries per workgroup
 #define ATTNQAT_FWD_AHEAD 2
 #endif
 constexpr int kFwdAhead = ATTNQAT_FWD_AHEAD;  // MFMA operand reads issued this many MFMAs ahead
+#ifndef ATTNQAT_FWD_RESCALE_LOG2
+#define ATTNQAT_FWD_RESCALE_LOG2 8
+#endif
+// The running max m used as the exponent base moves only when some row's
+// tile max exceeds it by more than this (log2 units); until then P = 2^(x - m)
+// may reach 2^kRescaleLog2 (exact in bf16's range, same relative rounding),
+// and O, l and the stored max stay consistent with the base actually used.
+constexpr float kRescaleLog2 = ATTNQAT_FWD_RESCALE_LOG2;
 
 // S^T = K^ Q^T of one 32-key tile (A operands read kFwdAhead MFMAs ahead).
 template <int D>
@@ -101,12 +111,13 @@ __device__ __forceinline__ void fwd_rescale(f32x16* o, bool& pending, float alph
   }
 }
 
-// Online-softmax update of (m, l) with the S^T of one tile (m: running row
-// max in log2 units), producing P^T in bf16 (b), interleaved with the O^T
-// MFMAs of the previous tile (b_prev, sVp) when ACC.  O^T then holds every
-// earlier tile against the old max; when the max moved (for some row of the
-// wave), the factor exp2(m_old - m_new) is left pending in (pending, alpha)
-// and applied to O^T before this tile's P^T V^ is added.
+// Online-softmax update of (m, l) with the S^T of one tile (m: the exponent
+// base in log2 units, at least the row max minus kRescaleLog2), producing
+// P^T in bf16 (b), interleaved with the O^T MFMAs of the previous tile
+// (b_prev, sVp) when ACC.  O^T then holds every earlier tile against the old
+// base; when the base moved (for some row of the wave), the factor
+// exp2(m_old - m_new) is left pending in (pending, alpha) and applied to O^T
+// before this tile's P^T V^ is added.
 template <int D, bool CAUSAL, bool MASK, bool ACC>
 __device__ __forceinline__ void fwd_softmax_pv(const f32x16& s, float& m, float& l, bf16x8* b,
                                                f32x16* o, const bf16x8* b_prev,
@@ -125,11 +136,14 @@ __device__ __forceinline__ void fwd_softmax_pv(const f32x16& s, float& m, float&
     for (int k = 0; k < kFwdAhead; ++k) c[k] = fwd_v_op<D>(sVp, co, k);
   }
   float tmax = -INFINITY, mnew = m, base = 0.0f, psum = 0.0f;
+  bool up = false;
   float xs[16], pv[16];
   uint32_t w[8];
   auto item = [&](int i) __attribute__((always_inline)) {
     if (i < 16) {
-      float x = s[i] * sl2;
+      // the max of the raw scores (sl2 > 0: the max of the scaled ones after
+      // one multiply, with the same rounding)
+      float x = s[i];
       if (MASK) {
         const int key = k0 + 8 * (i >> 2) + 4 * h + (i & 3);
         const bool ok = key < nkv && (!CAUSAL || key <= qi);
@@ -138,12 +152,13 @@ __device__ __forceinline__ void fwd_softmax_pv(const f32x16& s, float& m, float&
       xs[i] = x;
       tmax = fmaxf(tmax, x);
     } else if (i == 16) {
-      tmax = fmaxf(tmax, xor32(tmax));
-      mnew = fmaxf(m, tmax);
+      tmax = fmaxf(tmax, xor32(tmax)) * sl2;
+      up = __any(tmax > m + kRescaleLog2);
+      mnew = up ? fmaxf(m, tmax) : m;
       base = (mnew == -INFINITY) ? 0.0f : mnew;
     } else if (i < 33) {
       const int e = i - 17;
-      pv[e] = fast_exp2(xs[e] - base);
+      pv[e] = fast_exp2(fmaf(xs[e], sl2, -base));
       psum += pv[e];
     } else {
       const int e = i - 33;
@@ -164,8 +179,8 @@ __device__ __forceinline__ void fwd_softmax_pv(const f32x16& s, float& m, float&
   }
   b[0] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
   b[1] = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
-  // rescale only when some row's max moved; otherwise alpha would be exactly 1
-  if (__any(mnew > m)) {
+  // rescale only when the base moved for some row; otherwise alpha would be exactly 1
+  if (up) {
     alpha = fast_exp2(m - base);
     l *= alpha;
     pending = true;
@@ -231,9 +246,8 @@ void k_fwd(AttnArgs a) {
     const int p = 64 * (CH * wave + c) + lane;
     goff[c] = (uint32_t)swz<D>(p / CPR, 8 * (p % CPR)) * 2u;
   }
-  auto issue_tile = [&](int it) __attribute__((always_inline)) {
+  auto issue_tile = [&](int it, int buf) __attribute__((always_inline)) {
     const int k0 = (t0 + it) * BN;
-    const int buf = it % NB;
     // rows past nkv arrive as zeros (masked out later)
     const uint32_t bytes = (uint32_t)(min(nkv - k0, BN) * D) * 2u;
     const u32x4 dk = buf_desc(K + (size_t)k0 * D, bytes);
@@ -303,8 +317,8 @@ void k_fwd(AttnArgs a) {
     }
     if (ntiles > 1) load_packed(1);
   } else {
-    if (ntiles > 0) issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
+    if (ntiles > 0) issue_tile(0, 0);
+    if (ntiles > 1) issue_tile(1, 1);
     vmem_wait_all();
   }
   __syncthreads();
@@ -313,13 +327,14 @@ void k_fwd(AttnArgs a) {
   bool have_prev = false;
   bool pending = false;  // O^T rescale by alpha before the next P^T V^ (see fwd_softmax_pv)
   float alpha = 1.0f;
-  auto step = [&](int it, auto mask_tag) __attribute__((always_inline)) {
+  // buf = it % NB (a constant in the loop unrolled by NB: LDS addresses are
+  // then the lane's offset plus an immediate)
+  auto step = [&](int it, int buf, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = it % NB;
-    const int pbuf = (it + NB - 1) % NB;
+    const int pbuf = (buf + NB - 1) % NB;
     const int k0 = (t0 + it) * BN;
     if constexpr (!PACKED) {
-      if (it + 2 < ntiles) issue_tile(it + 2);
+      if (it + 2 < ntiles) issue_tile(it + 2, (buf + 2) % NB);
     }
     // (boundary tiles only) every key above every query of this wave: skip;
     // every later tile is then skipped too
@@ -347,7 +362,7 @@ void k_fwd(AttnArgs a) {
     }
     if constexpr (PACKED) {
       // buffer (it+1) % NB last held tile it-3
-      if (it + 1 < ntiles) store_packed((it + 1) % NB);
+      if (it + 1 < ntiles) store_packed((buf + 1) % NB);
       if (it + 2 < ntiles) load_packed(it + 2);
     } else {
       // tile it+1 has landed (this wave's copies; the barrier covers the
@@ -360,8 +375,15 @@ void k_fwd(AttnArgs a) {
     __syncthreads();
   };
   int it = 0;
-  for (; it < it_hi; ++it) step(it, BoolTag<false>());
-  for (; it < ntiles; ++it) step(it, BoolTag<true>());
+  if constexpr (D == 128) {  // (at D = 64 the unrolled loop costs occupancy and is slower)
+    for (; it + NB <= it_hi; it += NB) {
+      static_for<NB>([&](auto j) __attribute__((always_inline)) {
+        step(it + decltype(j)::value, decltype(j)::value, BoolTag<false>());
+      });
+    }
+  }
+  for (; it < it_hi; ++it) step(it, it % NB, BoolTag<false>());
+  for (; it < ntiles; ++it) step(it, it % NB, BoolTag<true>());
   // the last tile's O^T (its tile is still resident)
   if (have_prev) {
     fwd_rescale<D>(o, pending, alpha);
@@ -771,9 +793,11 @@ void k_fwd_dec(AttnArgs a) {
     }
 
     // online softmax (S^T rows = keys 8*(i/4) + 4h + i%4, one query per lane)
+    // (the max of the raw scores, then one multiply by sl2 > 0; the base
+    // moves only past kRescaleLog2, as in k_fwd)
     float xs[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) xs[i] = s[i] * sl2;
+    for (int i = 0; i < 16; ++i) xs[i] = s[i];
     if constexpr (MASK) {
       const int rem = nkv - k0 - 4 * h;  // keys of this lane half left in the tile
 #pragma unroll
@@ -783,14 +807,16 @@ void k_fwd_dec(AttnArgs a) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, xs[i]);
-    tmax = fmaxf(tmax, xor32(tmax));
-    const float mnew = fmaxf(m, tmax);
+    tmax = fmaxf(tmax, xor32(tmax)) * sl2;
+    const bool up = __any(tmax > m + kRescaleLog2);
+    const float mnew = up ? fmaxf(m, tmax) : m;
     const float base = (mnew == -INFINITY) ? 0.0f : mnew;
     float psum = 0.0f;
     uint32_t w[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p0 = fast_exp2(xs[2 * e] - base), p1 = fast_exp2(xs[2 * e + 1] - base);
+      const float p0 = fast_exp2(fmaf(xs[2 * e], sl2, -base));
+      const float p1 = fast_exp2(fmaf(xs[2 * e + 1], sl2, -base));
       psum += p0 + p1;
       if constexpr (PACKED)
         w[e] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)p0, (_Float16)p1});
@@ -798,7 +824,7 @@ void k_fwd_dec(AttnArgs a) {
         w[e] = pack_bf16x2(p0, p1);
     }
     const u32x4 b[2] = {u32x4{w[0], w[1], w[2], w[3]}, u32x4{w[4], w[5], w[6], w[7]}};
-    if (__any(mnew > m)) {
+    if (up) {
       alpha = fast_exp2(m - base);
       l *= alpha;
       pending = true;

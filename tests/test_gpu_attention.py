@@ -190,6 +190,44 @@ def test_ref_shape_workload():
         check_close(dv[0, h, keys].cpu(), rv, f"ref_shape dV groups h={h}")
 
 
+def test_ref_shape_dq_rows_within_the_bf16_ds_rounding_bound():
+    """Where the sampled dQ rows' error comes from.  The kernels round dS to
+    bf16 before dQ = s dS K^ (and dQ itself to bf16 at the end); with K^ exact
+    in bf16, the row error is then bounded by
+        u s || |dS_r| |K^| || + u ||dQ_r||,   u = 2^-8 (bf16 unit roundoff),
+    up to fp32 terms.  Every sampled row of every head of the reference shape
+    must satisfy it: an indexing, masking or accumulation fault would not.
+    (The bound adds 2^-12 s || |dS_r| |K^| || for the fp32 accumulation over
+    the keys, a worst case n u_32 with n = 4096, and 2^-16 times the size of
+    dS's fp32 inputs, for the fp32 rounding of P, dP and delta.)"""
+    w = WORKLOADS["ref_shape"]
+    q, k, v, do = make_inputs(w)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o_g, lse_g, _, _ = gpu_fwd(qd, kd, vd, w.causal, w.softmax_scale)
+    dq, _, _, _, _ = gpu_bwd(qd, kd, vd, o_g, do.to(DEV), lse_g, w.causal, w.softmax_scale)
+    rows = np.sort(np.random.default_rng(2).choice(w.seqlen, 48, replace=False))
+    u, s = 2.0 ** -8, w.softmax_scale
+    worst = 0.0
+    for h in range(w.heads):
+        qh, kh, vh = quantize_qkv(q[0, h].double().numpy(), k[0, h].double().numpy(),
+                                  v[0, h].double().numpy())
+        o = o_g[0, h].cpu().double().numpy()
+        lse = lse_g[0, h].cpu().double().numpy()
+        dO = do[0, h].double().numpy()
+        p = np.exp(s * qh[rows] @ kh.T - lse[rows, None])
+        delta = np.sum(o[rows] * dO[rows], axis=1)
+        ds = p * (dO[rows] @ vh.T - delta[:, None])
+        ref = s * ds @ kh
+        err = np.linalg.norm(dq[0, h, rows].cpu().double().numpy() - ref, axis=1)
+        mag = p * (np.abs(dO[rows]) @ np.abs(vh).T + np.abs(delta)[:, None])
+        bound = ((u + 2.0 ** -12) * s * np.linalg.norm(np.abs(ds) @ np.abs(kh), axis=1)
+                 + 1.01 * u * np.linalg.norm(ref, axis=1)
+                 + 2.0 ** -16 * s * np.linalg.norm(mag @ np.abs(kh), axis=1))
+        assert np.all(err <= bound), (h, np.max(err / bound))
+        worst = max(worst, float(np.max(err / bound)))
+    print(f"[ref_shape dQ rows] worst row error / bound: {worst:.3f}", flush=True)
+
+
 def _oracle_bwd_chunked(q, k, v, o_in, do, lse_in, scale, causal, rows, groups,
                         row_chunk=2048, group_chunk=256):
     """Oracle backward of one head over the given rows (dQ) and 16-key groups
