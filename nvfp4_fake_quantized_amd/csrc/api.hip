@@ -93,8 +93,9 @@ BwdPlan bwd_plan(const attnqat_problem* p) {
 //    fill the chip's 256 CUs: the keys are split so that about 512
 //    workgroups run, with at least 4 key tiles (128 keys) per split (causal:
 //    of the last query tile's keys; earlier tiles' later splits get none);
-// Both write per-run partial results (unnormalized O in fp32, row max and
-// sum) of bh * splits * Nq * (4 D + 8) bytes to the forward workspace.
+// Both write per-run partial results (unnormalized O in fp32, the run's
+// exponent base and sum) of bh * splits * Nq * (4 D + 8) bytes to the
+// forward workspace.
 struct FwdPlan {
   int splits;
   int decode;

@@ -139,8 +139,7 @@ __device__ __forceinline__ void dq_ds_acc(const f32x16& s, const f32x16& dp, int
       const float d0 = dq_ds<CAUSAL, MASK>(s[v], dp[v], v, k0, h, qi, qok, nkv, lse2, dl, sl2);
       const float d1 =
           dq_ds<CAUSAL, MASK>(s[v + 1], dp[v + 1], v + 1, k0, h, qi, qok, nkv, lse2, dl, sl2);
-      w[v >> 1] = pack_bf16x2(d0, d1);
-      pin(w[v >> 1]);
+      w[v >> 1] = pin_vgpr(pack_bf16x2(d0, d1));  // made here, in this MFMA's slot
     }
     __builtin_amdgcn_sched_barrier(0);
   }

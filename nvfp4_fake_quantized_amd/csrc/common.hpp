@@ -515,11 +515,4 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
-// Keeps the computation of x ahead of this point (an empty asm statement that
-// reads and writes x: no instruction).  Without it, code motion before
-// instruction scheduling sinks pure arithmetic whose result is used later
-// (the dS work of a step) past the scheduling barriers meant to interleave it
-// with MFMAs.
-__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
-
 }  // namespace attnqat

@@ -33,8 +33,8 @@
 //  * split over keys (when the query tiles alone cannot fill the chip: few
 //    queries against long K/V, or a short causal problem): blockIdx.y picks
 //    a run of the workgroup's key tiles; each split stores its unnormalized
-//    O^T (fp32) with its row max and sum (a split whose keys all lie above
-//    the causal diagonal stores max -inf and sum 0), and k_fwd_combine
+//    O^T (fp32) with its exponent base and sum (a split whose keys all lie
+//    above the causal diagonal stores base -inf and sum 0), and k_fwd_combine
 //    merges the splits into O_hp and lse.
 #include <hip/hip_runtime.h>
 
@@ -99,7 +99,7 @@ __device__ __forceinline__ void fwd_pv(f32x16* o, const bf16x8* b, const uint16_
   }
 }
 
-// O^T *= alpha when the row max moved at the previous tile (its pending
+// O^T *= alpha when the exponent base moved at the previous tile (its pending
 // factor); the caller applies it before adding that tile's P^T V^.
 template <int D>
 __device__ __forceinline__ void fwd_rescale(f32x16* o, bool& pending, float alpha) {
@@ -427,8 +427,9 @@ void k_fwd(AttnArgs a) {
 }
 
 // Merge of the key runs of k_fwd<..., SPLIT> and k_fwd_dec: per query row,
-// with M the largest run max and w_s = exp2(m_s - M), O_hp = sum_s w_s O_s / L
-// and lse = (M + log2 L) ln 2, L = sum_s w_s l_s.  One thread per 4 columns
+// with m_s a run's exponent base (O_s and l_s are sums of exp2(x - m_s)), M
+// the largest base and w_s = exp2(m_s - M), O_hp = sum_s w_s O_s / L and
+// lse = (M + log2 L) ln 2, L = sum_s w_s l_s.  One thread per 4 columns
 // of a row (D/4 threads per row); the runs are read 32 at a time (their
 // loads in flight together: one memory round trip for up to 32 runs) and
 // folded into a running max with rescaled sums.
@@ -512,9 +513,10 @@ __global__ __launch_bounds__(256) void k_fwd_combine(AttnArgs a, int64_t rows) {
 //    different bank groups;
 //  * V^ is read from a per-wave pair of LDS tiles in the swizzled layout of
 //    k_fwd with transpose reads;
-//  * at the end the 4 waves are merged in LDS (max over the waves,
-//    exp2-weighted sums) into one unnormalized partial (O, row max, row sum)
-//    per workgroup, which k_fwd_combine merges over the workgroups.
+//  * at the end the 4 waves are merged in LDS (the largest of the waves'
+//    exponent bases, exp2-weighted sums) into one unnormalized partial (O,
+//    base, row sum) per workgroup, which k_fwd_combine merges over the
+//    workgroups.
 constexpr int kDecBQ = 32;  // queries per workgroup
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));

@@ -61,9 +61,9 @@ struct AttnArgs {
   const uint8_t* v_codes;
   const uint8_t* v_scales;
   // forward split over keys (kv_splits > 1): per split, unnormalized O^T
-  // (fp32) and the row max and sum, merged by a second kernel
+  // (fp32) and the exponent base and sum, merged by a second kernel
   float* o_part;          // (BH, kv_splits, nq, D)
-  float* ml_part;         // (BH, kv_splits, nq, 2): max (log2 units), sum
+  float* ml_part;         // (BH, kv_splits, nq, 2): base (log2 units), sum
   int kv_splits;          // 0 or 1: no split
   int kv_decode;          // 1: 32-query tiles (k_fwd_dec), kv_splits >= 1 key runs
   // k_fwd_dec from packed K/V: when q_in is set, the kernel fake-quantizes
