@@ -53,26 +53,28 @@ __device__ __forceinline__ bf16x8 dq_row_op(const uint16_t* sKb, const uint16_t*
   return ld_bf16x8(((k & 1) ? sVb : sKb) + ro.o[k >> 1]);
 }
 
-// S^T/dP^T MFMA k into s (even k) or dp (odd k).
+// S^T/dP^T MFMA k into s (even k) or dp (odd k; the chain starts from dp0).
 __device__ __forceinline__ void dq_sdp_mfma(int k, const bf16x8& a, const bf16x8* qf,
-                                            const bf16x8* df, f32x16& s, f32x16& dp) {
+                                            const bf16x8* df, f32x16& s, f32x16& dp,
+                                            const f32x16& dp0) {
   if (k & 1)
-    dp = mfma32x32x16(a, df[k >> 1], k == 1 ? zero_f32x16() : dp);
+    dp = mfma32x32x16(a, df[k >> 1], k == 1 ? dp0 : dp);
   else
     s = mfma32x32x16(a, qf[k >> 1], k == 0 ? zero_f32x16() : s);
 }
 
-// dS^T element v: lane half h holds key k0 + 8*(v/4) + 4h + v%4 of query qi.
+// dS^T element v (dpv: dP - delta): lane half h holds key
+// k0 + 8*(v/4) + 4h + v%4 of query qi.
 template <bool CAUSAL, bool MASK>
 __device__ __forceinline__ float dq_ds(float sv, float dpv, int v, int k0, int h, int qi, bool qok,
-                                       int nkv, float lse2, float dl, float sl2) {
+                                       int nkv, float lse2, float sl2) {
   float x = __builtin_fmaf(sv, sl2, -lse2);
   if (MASK) {
     const int key = k0 + 8 * (v >> 2) + 4 * h + (v & 3);
     const bool ok = qok && key < nkv && (!CAUSAL || key <= qi);
     x = ok ? x : -INFINITY;
   }
-  return fast_exp2(x) * (dpv - dl);
+  return fast_exp2(x) * dpv;
 }
 
 // dS^T as the two bf16 B operands of dQ^T = K^T dS^T (16-key k-blocks kh:
@@ -93,7 +95,7 @@ __device__ __forceinline__ void dq_pack(const float* ds, bf16x8* b) {
 template <int D>
 __device__ __forceinline__ void dq_sdp(const bf16x8* qf, const bf16x8* df, const uint16_t* sKb,
                                        const uint16_t* sVb, const RowOffsets<D>& ro, f32x16& s,
-                                       f32x16& dp) {
+                                       f32x16& dp, const f32x16& dp0) {
   constexpr int NM = D / 8;
   bf16x8 a[NM];
 #pragma unroll
@@ -101,7 +103,7 @@ __device__ __forceinline__ void dq_sdp(const bf16x8* qf, const bf16x8* df, const
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
     if (k + kDqAhead < NM) a[k + kDqAhead] = dq_row_op<D>(sKb, sVb, ro, k + kDqAhead);
-    dq_sdp_mfma(k, a[k], qf, df, s, dp);
+    dq_sdp_mfma(k, a[k], qf, df, s, dp, dp0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -111,7 +113,7 @@ __device__ __forceinline__ void dq_sdp(const bf16x8* qf, const bf16x8* df, const
 // wave keeps the matrix pipe fed while it evaluates exp2.
 template <int D, bool CAUSAL, bool MASK, bool ACC>
 __device__ __forceinline__ void dq_ds_acc(const f32x16& s, const f32x16& dp, int k0, int h, int qi,
-                                          bool qok, int nkv, float lse2, float dl, float sl2,
+                                          bool qok, int nkv, float lse2, float sl2,
                                           bf16x8* b, f32x16* acc, const bf16x8* b_prev,
                                           const uint16_t* sKp, const ColOffsets<D>& co) {
   constexpr int DB = D / 32;
@@ -136,9 +138,9 @@ __device__ __forceinline__ void dq_ds_acc(const f32x16& s, const f32x16& dp, int
 #pragma unroll
     for (int e = 0; e < EPM; e += 2) {
       const int v = EPM * k + e;
-      const float d0 = dq_ds<CAUSAL, MASK>(s[v], dp[v], v, k0, h, qi, qok, nkv, lse2, dl, sl2);
+      const float d0 = dq_ds<CAUSAL, MASK>(s[v], dp[v], v, k0, h, qi, qok, nkv, lse2, sl2);
       const float d1 =
-          dq_ds<CAUSAL, MASK>(s[v + 1], dp[v + 1], v + 1, k0, h, qi, qok, nkv, lse2, dl, sl2);
+          dq_ds<CAUSAL, MASK>(s[v + 1], dp[v + 1], v + 1, k0, h, qi, qok, nkv, lse2, sl2);
       w[v >> 1] = pin_vgpr(pack_bf16x2(d0, d1));  // made here, in this MFMA's slot
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -205,6 +207,11 @@ void k_dq(AttnArgs a) {
   const float lse2 = qok ? a.lse[(size_t)bh * nq + qi] * kLog2e : 0.0f;
   const float dl = qok ? a.delta[(size_t)bh * nq + qi] : 0.0f;
   const float sl2 = a.softmax_scale * kLog2e;
+  // the dP^T chain starts from -delta (every element of the accumulator is
+  // this lane's query), so it yields dP - delta directly
+  f32x16 dp0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dp0[i] = -dl;
   // LDS offsets: row reads of K^/V^ and K^T column reads (k-block rows 4h.., 4h+8..)
   const RowOffsets<D> ro(lane);
   const ColOffsets<D> co(4 * h, 4 * h + 8, lane);
@@ -275,14 +282,14 @@ void k_dq(AttnArgs a) {
       // the MFMA-only phase runs at raised wave priority, so that the other
       // wave on the SIMD fills its gaps rather than competing for issue
       __builtin_amdgcn_s_setprio(1);
-      dq_sdp<D>(qf, df, sK[buf], sV[buf], ro, s, dp);
+      dq_sdp<D>(qf, df, sK[buf], sV[buf], ro, s, dp, dp0);
       __builtin_amdgcn_s_setprio(0);
       bf16x8 b[2];
       if (have_prev)
-        dq_ds_acc<D, CAUSAL, MASK, true>(s, dp, k0, h, qi, qok, nkv, lse2, dl, sl2, b, acc,
+        dq_ds_acc<D, CAUSAL, MASK, true>(s, dp, k0, h, qi, qok, nkv, lse2, sl2, b, acc,
                                          b_prev, sK[pbuf], co);
       else
-        dq_ds_acc<D, CAUSAL, MASK, false>(s, dp, k0, h, qi, qok, nkv, lse2, dl, sl2, b, acc,
+        dq_ds_acc<D, CAUSAL, MASK, false>(s, dp, k0, h, qi, qok, nkv, lse2, sl2, b, acc,
                                           b_prev, sK[pbuf], co);
       b_prev[0] = b[0];
       b_prev[1] = b[1];
