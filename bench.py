@@ -17,7 +17,7 @@ split and the roofline entry (each launch's dispatch records its own
 start/stop events, so the split adds no gaps), the full forward with the
 quantized output, the forward from packed K/V, the backward after a flush of
 the 256 MB Infinity Cache, the sustained MFMA rate probe on random and on
-uniform operands, and a plain device copy of the K/V codec's byte count.
+uniform operands, and a plain device copy of a K/V fake-quant's byte count.
 
 The reported metric is the backward's throughput: counted backward work
 10*B*H*N^2*D (halved when causal) divided by the median backward duration.
@@ -572,8 +572,8 @@ def main():
         del flush
         extras["mfma_probe_tflops"] = round(mfma_probe(B, dev, hip, stream), 1)
         extras["mfma_probe_uniform_tflops"] = round(mfma_probe(B, dev, hip, stream, uniform=True), 1)
-        # a plain device copy moving as many bytes as the backward's K/V
-        # fake-quant kernel reads and writes (context for the codec rates)
+        # a plain device copy moving as many bytes as a K/V fake-quant reads
+        # and writes (context for the codec rates)
         nb = 2 * kd.numel()  # bf16 elements of K and V
         csrc = torch.empty(nb, dtype=torch.bfloat16, device=dev)
         cdst = torch.empty_like(csrc)
@@ -609,8 +609,9 @@ def main():
         "bwd_dq": ("mfma", 6.0 * BH * N * N * D * half),
         "bwd_dkdv": ("mfma", 8.0 * BH * N * N * D * half),
         "fwd_quant_qkv": ("hbm", 3 * elems * (4 + 1 / 16)),
-        # Q + delta (reads Q, O_hp, dO; writes Q^, scales, delta) and K, V
-        "bwd_codec": ("hbm", elems * (8 + 1 / 16) + BH * N * 4 + 2 * elems * (4 + 1 / 16)),
+        # Q + delta (reads Q, O_hp, dO; writes Q^, scales, delta); K and V
+        # are fake-quantized inside the dK/dV kernel
+        "bwd_codec": ("hbm", elems * (8 + 1 / 16) + BH * N * 4),
     }
     dominant = max(per, key=per.get)
     bound, amount = work[dominant]

@@ -213,7 +213,9 @@ ATTNQAT_API int attnqat_fwd_quantized(const attnqat_problem* p, const void* q, c
  * In: q, o_hp, d_o (B,H,Nq,D) bf16; k, v (B,H,Nkv,D) bf16; lse (B,H,Nq)
  * fp32 from the matching forward.  Out: dq (B,H,Nq,D), dk, dv (B,H,Nkv,D)
  * bf16.  The workspace (>= attnqat_bwd_workspace_bytes) holds Q^/K^/V^,
- * their scales and delta afterwards.
+ * their scales and delta afterwards.  Launches: Q fake-quant fused with
+ * delta; dK/dV, whose workgroups also fake-quantize the K and V rows of
+ * their key block and write K^/V^; then dQ, which reads them.
  * Small problems: when the key blocks of 128 (over all heads) number fewer
  * than 256, the dK/dV kernel splits its query loop over s_kv =
  * min(ceil(256 / key blocks), query sub-tiles of 32 / 4) workgroups (when

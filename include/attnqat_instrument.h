@@ -28,9 +28,10 @@ extern "C" {
  * attnqat_fwd_quantized_timed: 6 events; kernels 0 and 1 as above, kernel 2
  *   the second (quantized-output) pass.
  * attnqat_bwd_timed: 6 events; kernel 0 the preprocessing (Q fake-quant fused
- *   with delta, and K/V fake-quant, in one launch), kernel 1 dQ, kernel 2
- *   dK/dV (on small problems with split loops -- see attnqat_bwd -- its pair
- *   also spans the launch that adds the partial sums of dQ, dK and dV).
+ *   with delta), kernel 1 dQ (on small problems with split loops -- see
+ *   attnqat_bwd -- its pair also spans the launch that adds the partial sums
+ *   of dQ, dK and dV), kernel 2 dK/dV with the K/V fake-quant (launched
+ *   before dQ).
  * A NULL array or NULL event is ATTNQAT_ERR_INVALID_ARGUMENT. */
 ATTNQAT_API int attnqat_fwd_timed(const attnqat_problem* p, const void* q, const void* k,
                                   const void* v, void* o_hp, float* lse, void* workspace,

@@ -420,8 +420,10 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   uint16_t* vh = at<uint16_t>(workspace, L.v_hat);
   float* delta = at<float>(workspace, L.delta);
 
-  // 1) Q fake-quantization fused with delta = rowsum(O_hp * dO), and 2) the
-  // K/V fake-quantization, in one launch
+  // 1) Q fake-quantization fused with delta = rowsum(O_hp * dO); 2) the K/V
+  // fake-quantization runs inside k_dkdv (below), whose workgroups each own a
+  // key block: they quantize its K and V rows and write K^, V^ and the scale
+  // bytes, which k_dq then reads
   const attnqat::QDeltaJob qd = {static_cast<const uint16_t*>(q),
                                  static_cast<const uint16_t*>(o_hp),
                                  static_cast<const uint16_t*>(d_o),
@@ -429,8 +431,8 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
                                  at<uint8_t>(workspace, L.q_scale),
                                  delta,
                                  bh * p->seqlen_q};
-  const QuantJob kj = {k, kh, at<uint8_t>(workspace, L.k_scale), bh * p->seqlen_kv * D / 16};
-  const QuantJob vj = {v, vh, at<uint8_t>(workspace, L.v_scale), bh * p->seqlen_kv * D / 16};
+  const QuantJob kj = {k, kh, at<uint8_t>(workspace, L.k_scale), 0};
+  const QuantJob vj = {v, vh, at<uint8_t>(workspace, L.v_scale), 0};
   if (attnqat::launch_bwd_codec(qd, kj, vj, p->head_dim, stream, timing(ev, 0)) != hipSuccess)
     return ATTNQAT_ERR_HIP;
 
@@ -452,10 +454,17 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
   a.p_scale = p->p_scale;
   a.dq_splits = L.dq_splits;
   a.dkdv_splits = L.dkdv_splits;
+  a.k_in = static_cast<const uint16_t*>(k);
+  a.v_in = static_cast<const uint16_t*>(v);
+  a.k_hat_out = kh;
+  a.v_hat_out = vh;
+  a.k_scale_out = at<uint8_t>(workspace, L.k_scale);
+  a.v_scale_out = at<uint8_t>(workspace, L.v_scale);
   if (L.dq_splits > 1) a.dq_part = at<float>(workspace, L.dq_part);
   if (L.dkdv_splits > 1) a.dkdv_part = at<float>(workspace, L.dkdv_part);
-  // 3) dQ and 4) dK/dV; on small problems their split loops leave fp32
-  // partial sums, added by one k_sum_parts launch (timed with dK/dV)
+  // 3) dK/dV (with the K/V fake-quant) and 4) dQ; on small problems their
+  // split loops leave fp32 partial sums, added by one k_sum_parts launch
+  // (timed with dQ)
   attnqat::SumJob sums[3];
   int nsums = 0;
   const int64_t nqd = bh * p->seqlen_q * D, nkd = bh * p->seqlen_kv * D;
@@ -465,16 +474,16 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
     sums[nsums++] = {a.dkdv_part, a.dk, 2 * nkd, nkd, L.dkdv_splits, p->softmax_scale};
     sums[nsums++] = {a.dkdv_part + nkd, a.dv, 2 * nkd, nkd, L.dkdv_splits, 1.0f / p->p_scale};
   }
-  const attnqat::LaunchEvents* e2 = timing(ev, 2);
-  const attnqat::LaunchEvents e2a = {e2 ? e2->start : nullptr, nullptr};
-  const attnqat::LaunchEvents e2b = {nullptr, e2 ? e2->stop : nullptr};
-  if (attnqat::launch_bwd_dq(a, p->head_dim, stream, timing(ev, 1)) != hipSuccess)
+  const attnqat::LaunchEvents* e1 = timing(ev, 1);
+  const attnqat::LaunchEvents e1a = {e1 ? e1->start : nullptr, nullptr};
+  const attnqat::LaunchEvents e1b = {nullptr, e1 ? e1->stop : nullptr};
+  if (attnqat::launch_bwd_dkdv(a, p->head_dim, stream, timing(ev, 2)) != hipSuccess)
     return ATTNQAT_ERR_HIP;
-  if (attnqat::launch_bwd_dkdv(a, p->head_dim, stream, nsums > 0 && e2 ? &e2a : e2) !=
+  if (attnqat::launch_bwd_dq(a, p->head_dim, stream, nsums > 0 && e1 ? &e1a : e1) !=
       hipSuccess)
     return ATTNQAT_ERR_HIP;
   if (nsums > 0 &&
-      attnqat::launch_sum_parts(sums, nsums, stream, e2 ? &e2b : nullptr) != hipSuccess)
+      attnqat::launch_sum_parts(sums, nsums, stream, e1 ? &e1b : nullptr) != hipSuccess)
     return ATTNQAT_ERR_HIP;
   return ATTNQAT_OK;
 }

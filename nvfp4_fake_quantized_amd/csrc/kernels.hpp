@@ -72,6 +72,15 @@ struct AttnArgs {
   const uint16_t* q_in;   // (BH, nq, D) bf16
   uint16_t* q_hat_out;
   uint8_t* q_scale_out;   // (BH, nq, D/16)
+  // k_dkdv: when k_in is set, the kernel fake-quantizes the K and V rows of
+  // its key block itself, and the first query run of each key block writes
+  // K^, V^ and their scale bytes (for k_dq, which runs after it)
+  const uint16_t* k_in;   // (BH, nkv, D) bf16
+  const uint16_t* v_in;
+  uint16_t* k_hat_out;
+  uint16_t* v_hat_out;
+  uint8_t* k_scale_out;   // (BH, nkv, D/16)
+  uint8_t* v_scale_out;
   // backward over few tiles: the key loop of k_dq split over dq_splits
   // workgroups and the query loop of k_dkdv over dkdv_splits, each writing
   // fp32 partial sums that a reduction adds up in a fixed order
@@ -102,7 +111,8 @@ hipError_t launch_pack_bf16(const QuantJob& job, uint8_t* codes, hipStream_t str
 // fake_nvfp4 over one fp32 tensor.
 hipError_t launch_quant_f32(const QuantJob& job, hipStream_t stream);
 // The backward's preprocessing in one launch: Q fake-quant fused with
-// delta = rowsum(O_hp * dO) (fp32), and K and V fake-quant; D in {64, 128}.
+// delta = rowsum(O_hp * dO) (fp32), and K and V fake-quant when their jobs
+// have groups (none: only Q + delta is launched); D in {64, 128}.
 struct QDeltaJob {
   const uint16_t* q;
   const uint16_t* o_hp;

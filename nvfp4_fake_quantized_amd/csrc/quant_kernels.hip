@@ -2,10 +2,12 @@
 //
 // One thread owns one group of 16 contiguous values ("NVFP4 Attention QAT
 // Backward", §Overview: one E4M3 scale per 16 values); a wave covers 64
-// consecutive groups, i.e. 2 KiB of contiguous bf16 input.  The backward's
-// preprocessing (same page, §Overview: the fused Q fake-quantization / delta
-// kernel and the K/V fake-quantization) runs as one launch, k_bwd_codec, whose
-// blockIdx.y selects Q + delta, K or V: one ramp-up and tail instead of two.
+// consecutive groups, i.e. 2 KiB of contiguous bf16 input.  k_bwd_codec
+// holds the backward's preprocessing (same page, §Overview: the fused Q
+// fake-quantization / delta kernel, and optionally the K/V fake-quantization
+// in the same grid: blockIdx.y selects Q + delta, K or V).  The backward
+// itself runs only its Q + delta part: its dK/dV kernel fake-quantizes K and V
+// (each workgroup the rows of its own key block).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -188,7 +190,9 @@ hipError_t launch_bwd_codec(const QDeltaJob& qd, const QuantJob& k, const QuantJ
   if (k.groups > maxg) maxg = k.groups;
   if (v.groups > maxg) maxg = v.groups;
   if (maxg == 0) return hipSuccess;
-  const dim3 grid(grid_for(maxg), 3);
+  // without K/V groups (the backward quantizes K and V inside k_dkdv) only
+  // the Q + delta part is launched
+  const dim3 grid(grid_for(maxg), (k.groups > 0 || v.groups > 0) ? 3 : 1);
   if (gpr == 8) return launch(k_bwd_codec<8>, grid, dim3(kThreads), stream, ev, qd, k, v);
   return launch(k_bwd_codec<4>, grid, dim3(kThreads), stream, ev, qd, k, v);
 }
