@@ -160,7 +160,8 @@ ATTNQAT_API int attnqat_nvfp4_pack(const void* x, uint8_t* codes, uint8_t* scale
  * Few queries, or a short problem: non-causal with at most 32 queries per
  * head, a kernel with 32-query tiles deals the key tiles of each head out
  * to `splits` = min(ceil(512 / (B*H)), max(1, key tiles of 32 / 8))
- * workgroups; otherwise (causal too), when the 128-query tiles over all
+ * workgroups, which also fake-quantize Q, K and V themselves (each key tile
+ * is read once; no separate quantization pass); otherwise (causal too), when the 128-query tiles over all
  * heads number fewer than 256, the keys are split over workgroups (splits =
  * min(ceil(512 / tiles), key tiles / 4), used when >= 2).  Either way a
  * second launch merges the partial results, and the workspace size then

@@ -22,9 +22,11 @@ extern "C" {
  * event (hipExtLaunchKernel), so per-kernel durations can be read with
  * hipEventElapsedTime(events[2i], events[2i+1]) without synchronizing inside
  * the call and without extra packets or gaps between the kernels.
- * attnqat_fwd_timed: 4 events; kernel 0 the Q/K/V fake-quant, kernel 1 the
- *   attention forward (when the forward covers the keys in runs -- see
- *   attnqat_fwd -- its pair spans the attention launch and the merge launch).
+ * attnqat_fwd_timed: 4 events; kernel 0 the Q/K/V fake-quant (an empty span
+ *   when the forward takes 32-query tiles, which quantize inside the
+ *   attention kernel), kernel 1 the attention forward (when the forward
+ *   covers the keys in runs -- see attnqat_fwd -- its pair spans the
+ *   attention launch and the merge launch).
  * attnqat_fwd_quantized_timed: 6 events; kernels 0 and 1 as above, kernel 2
  *   the second (quantized-output) pass.
  * attnqat_bwd_timed: 6 events; kernel 0 the preprocessing (Q fake-quant fused

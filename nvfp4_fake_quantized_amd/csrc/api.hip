@@ -310,10 +310,28 @@ int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* 
       {k, kh, at<uint8_t>(workspace, L.k_scale), bh * p->seqlen_kv * D / 16},
       {v, vh, at<uint8_t>(workspace, L.v_scale), bh * p->seqlen_kv * D / 16},
   };
-  if (attnqat::launch_quant_bf16(jobs, 3, stream, timing(ev, 0)) != hipSuccess)
-    return ATTNQAT_ERR_HIP;
-
   AttnArgs a = {};
+  if (L.kv_decode) {
+    // 32-query tiles: every key tile is read by one wave, which fake-quantizes
+    // it (and the workgroup its Q rows) in the attention kernel itself and
+    // writes Q^, K^, V^ and the scale bytes; no separate quantization pass
+    a.q_in = static_cast<const uint16_t*>(q);
+    a.q_hat_out = qh;
+    a.q_scale_out = at<uint8_t>(workspace, L.q_scale);
+    a.k_in = static_cast<const uint16_t*>(k);
+    a.v_in = static_cast<const uint16_t*>(v);
+    a.k_hat_out = kh;
+    a.v_hat_out = vh;
+    a.k_scale_out = at<uint8_t>(workspace, L.k_scale);
+    a.v_scale_out = at<uint8_t>(workspace, L.v_scale);
+    const attnqat::LaunchEvents* e0 = timing(ev, 0);  // an empty span
+    if (e0 != nullptr && (hipEventRecord(e0->start, stream) != hipSuccess ||
+                          hipEventRecord(e0->stop, stream) != hipSuccess))
+      return ATTNQAT_ERR_HIP;
+  } else if (attnqat::launch_quant_bf16(jobs, 3, stream, timing(ev, 0)) != hipSuccess) {
+    return ATTNQAT_ERR_HIP;
+  }
+
   a.q_hat = qh;
   a.k_hat = kh;
   a.v_hat = vh;

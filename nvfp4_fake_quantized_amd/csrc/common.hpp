@@ -259,6 +259,39 @@ struct FastP {
   }
 };
 
+// fake_nvfp4 of the 8 values a lane holds of a 16-value group whose other 8
+// the lane XOR positions away holds: one exchange of the amax, the codec's
+// E4M3 scale, and the exact E2M1 rounding of FastP applied to |x| (the sign
+// copied back; code * scale is exact in bf16).  Returns the quantized values;
+// sb receives the scale byte.
+template <int XOR>
+__device__ __forceinline__ bf16x8 fq_half_group(bf16x8 v, uint32_t& sb) {
+  const u32x4 w = __builtin_bit_cast(u32x4, v);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
+  am = fmaxf(am, __shfl_xor(am, XOR, 64));
+  const float s = e4m3_scale_from_amax(am);
+  const FastP fq(s);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float y0, y1;
+    fq.pair(fabsf(x[2 * i]), fabsf(x[2 * i + 1]), y0, y1);
+    o[i] = __builtin_amdgcn_perm(__float_as_uint(__builtin_copysignf(y1, x[2 * i + 1])),
+                                 __float_as_uint(__builtin_copysignf(y0, x[2 * i])),
+                                 0x07060302u);
+  }
+  sb = e4m3_byte(s);
+  return __builtin_bit_cast(bf16x8, o);
+}
+
 // ---------------------------------------------------------------------------
 // LDS transpose reads (ds_read_b64_tr_b16).
 //

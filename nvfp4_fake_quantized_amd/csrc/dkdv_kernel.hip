@@ -124,37 +124,6 @@ constexpr int x_item_slot(int i, int nslot) {
   return before * nslot / total;
 }
 
-// fake_nvfp4 of the 8 values a lane holds of a 16-value group whose other 8
-// the lane 32 away holds: one exchange of the amax, the codec's E4M3 scale,
-// and the exact E2M1 rounding of FastP applied to |x| (the sign copied back).
-// Returns the quantized values; sb receives the scale byte.
-__device__ __forceinline__ bf16x8 fq_half_group(bf16x8 v, uint32_t& sb) {
-  const u32x4 w = __builtin_bit_cast(u32x4, v);
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-  }
-  float am = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
-  am = fmaxf(am, xor32(am));
-  const float s = e4m3_scale_from_amax(am);
-  const FastP fq(s);
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float y0, y1;
-    fq.pair(fabsf(x[2 * i]), fabsf(x[2 * i + 1]), y0, y1);
-    // code * scale is exact in bf16
-    o[i] = pack_exact_bf16x2(__builtin_copysignf(y0, x[2 * i]),
-                             __builtin_copysignf(y1, x[2 * i + 1]));
-  }
-  sb = e4m3_byte(s);
-  return __builtin_bit_cast(bf16x8, o);
-}
-
 template <int D, bool CAUSAL, bool UNIT_P>
 __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
   using L = DkdvLds<D>;
@@ -237,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void k_dkdv(AttnArgs a) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           uint32_t sk, sv;
-          kf[kb] = fq_half_group(kf[kb], sk);
-          vf[kb] = fq_half_group(vf[kb], sv);
+          kf[kb] = fq_half_group<32>(kf[kb], sk);
+          vf[kb] = fq_half_group<32>(vf[kb], sv);
           if (wr) {
             *reinterpret_cast<bf16x8*>(a.k_hat_out + r * D + 16 * kb + 8 * h) = kf[kb];
             *reinterpret_cast<bf16x8*>(a.v_hat_out + r * D + 16 * kb + 8 * h) = vf[kb];

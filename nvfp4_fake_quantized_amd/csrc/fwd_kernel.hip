@@ -618,7 +618,7 @@ void k_fwd_dec(AttnArgs a) {
   auto tile_k0 = [&](int it) __attribute__((always_inline)) { return (g + W * (n - 1 - it)) * BN; };
 
   // Q^ rows of the workgroup (rows past nq as zeros; fp16 for packed K^/V^)
-  if (PACKED && a.q_in != nullptr) {
+  if (a.q_in != nullptr) {
     // fake-quantize the raw Q rows here (one 16-value group per thread, the
     // codec's arithmetic); the first key run writes Q^ and the scale bytes
     constexpr int NGRP = kDecBQ * GPR;  // groups of the tile
@@ -640,14 +640,20 @@ void k_fwd_dec(AttnArgs a) {
         *reinterpret_cast<u32x4*>(a.q_hat_out + off + 8) = hi;
         a.q_scale_out[off / 16] = (uint8_t)e4m3_byte(sc);
       }
-      f16x8 h0, h1;  // exact: E2M1 codes times E4M3 scales
+      if constexpr (PACKED) {
+        f16x8 h0, h1;  // exact: E2M1 codes times E4M3 scales
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        h0[e] = (_Float16)x[e];
-        h1[e] = (_Float16)x[8 + e];
+        for (int e = 0; e < 8; ++e) {
+          h0[e] = (_Float16)x[e];
+          h1[e] = (_Float16)x[8 + e];
+        }
+        *reinterpret_cast<f16x8*>(sQ + r * QS + col) = h0;
+        *reinterpret_cast<f16x8*>(sQ + r * QS + col + 8) = h1;
+      } else {
+        pack_bf16x16(x, lo, hi);
+        *reinterpret_cast<u32x4*>(sQ + r * QS + col) = lo;
+        *reinterpret_cast<u32x4*>(sQ + r * QS + col + 8) = hi;
       }
-      *reinterpret_cast<f16x8*>(sQ + r * QS + col) = h0;
-      *reinterpret_cast<f16x8*>(sQ + r * QS + col + 8) = h1;
     }
   } else {
     const uint16_t* Q = a.q_hat + (size_t)bh * nq * D;
@@ -678,10 +684,14 @@ void k_fwd_dec(AttnArgs a) {
   const float sl2 = a.softmax_scale * kLog2e;
   const ColOffsets<D> co(4 * h, 4 * h + 8, lane);
 
-  // ---- bf16 K^ rows (registers) and V^ tiles (LDS copies)
-  const uint16_t* K = a.k_hat + (size_t)bh * nkv * D;
-  const uint16_t* V = a.v_hat + (size_t)bh * nkv * D;
+  // ---- bf16 K^ rows (registers) and V^ tiles (LDS copies); with raw K/V
+  // (k_in set) the kernel fake-quantizes them itself: each key tile belongs
+  // to one wave of one key run, which writes its K^, V^ and scale bytes
+  const bool fuse = !PACKED && a.k_in != nullptr;
+  const uint16_t* K = (fuse ? a.k_in : a.k_hat) + (size_t)bh * nkv * D;
+  const uint16_t* V = (fuse ? a.v_in : a.v_hat) + (size_t)bh * nkv * D;
   bf16x8 kr[PACKED ? 1 : KB];
+  bf16x8 vraw[PACKED ? 1 : CH];
   auto load_k = [&](int it) __attribute__((always_inline)) {
     const int k0 = tile_k0(it);
     const auto r = make_rsrc(K + (size_t)k0 * D, (uint32_t)(min(nkv - k0, BN) * D) * 2u);
@@ -700,6 +710,47 @@ void k_fwd_dec(AttnArgs a) {
       const int p = 64 * c + lane;
       buf_ld16_lds(d, (uint32_t)swz<D>(p / CPR, 8 * (p % CPR)) * 2u,
                    __builtin_amdgcn_readfirstlane(lds_addr(dst + 512 * c)));
+    }
+  };
+  // raw V rows of tile it into registers, chunk for chunk as copy_v places
+  // them (rows past nkv read as zeros)
+  auto load_v_raw = [&](int it) __attribute__((always_inline)) {
+    const int k0 = tile_k0(it);
+    const auto r = make_rsrc(V + (size_t)k0 * D, (uint32_t)(min(nkv - k0, BN) * D) * 2u);
+#pragma unroll
+    for (int c = 0; c < (PACKED ? 1 : CH); ++c) {
+      const int p = 64 * c + lane;
+      vraw[c] = __builtin_bit_cast(bf16x8, buf_ld16(r, (uint32_t)swz<D>(p / CPR, 8 * (p % CPR)) * 2u));
+    }
+  };
+  // fake-quantize tile it: K^ in place in kr (a lane holds 8 columns of a
+  // 16-value group, the lane 32 away the other 8), V^ into this wave's LDS
+  // tile (chunk slot p = 64c + lane holds column chunk swz_chunk(row, p % CPR);
+  // the other half of its group sits in slot p ^ 1, lane ^ 1), and both to
+  // the workspace with their scale bytes (rows below nkv only)
+  auto quant_kv = [&](int it) __attribute__((always_inline)) {
+    const int k0 = tile_k0(it);
+    const size_t row0 = (size_t)bh * nkv + k0;
+#pragma unroll
+    for (int j = 0; j < (PACKED ? 1 : KB); ++j) {
+      uint32_t sb;
+      kr[j] = fq_half_group<32>(kr[j], sb);
+      if (k0 + l32 < nkv) {
+        *reinterpret_cast<bf16x8*>(a.k_hat_out + (row0 + l32) * D + 16 * j + 8 * h) = kr[j];
+        if (h == 0) a.k_scale_out[(row0 + l32) * GPR + j] = (uint8_t)sb;
+      }
+    }
+    uint16_t* dst = ring + (it & 1) * VT;
+#pragma unroll
+    for (int c = 0; c < (PACKED ? 1 : CH); ++c) {
+      const int p = 64 * c + lane, r = p / CPR, lc = swz_chunk<D>(r, p % CPR);
+      uint32_t sb;
+      const bf16x8 vq = fq_half_group<1>(vraw[c], sb);
+      *reinterpret_cast<bf16x8*>(dst + 512 * c + 8 * lane) = vq;
+      if (k0 + r < nkv) {
+        *reinterpret_cast<bf16x8*>(a.v_hat_out + (row0 + r) * D + 8 * lc) = vq;
+        if ((lc & 1) == 0) a.v_scale_out[(row0 + r) * GPR + lc / 2] = (uint8_t)sb;
+      }
     }
   };
 
@@ -778,6 +829,7 @@ void k_fwd_dec(AttnArgs a) {
       // slot sl is free now (K^ of tile it consumed, V^ of tile it in LDS)
       if (it + 2 < n) load_codes(it + 2, slot_tag);
     } else {
+      if (fuse) quant_kv(it);  // this tile's raw rows arrived during the previous step
 #pragma unroll
       for (int k = 0; k < kFwdAhead; ++k) qb[k] = ldq(k);
 #pragma unroll
@@ -789,7 +841,10 @@ void k_fwd_dec(AttnArgs a) {
       // V^ of tile it+1 before K^ of tile it+1: loads complete in issue
       // order, so the wait for K^ at the next step also covers this copy
       if (more) {
-        copy_v(it + 1);
+        if (fuse)
+          load_v_raw(it + 1);
+        else
+          copy_v(it + 1);
         load_k(it + 1);
       }
     }
@@ -863,7 +918,10 @@ void k_fwd_dec(AttnArgs a) {
     if (n > 1) load_codes(1, IntTag<1>());
   } else {
     if (n > 0) {
-      copy_v(0);
+      if (fuse)
+        load_v_raw(0);
+      else
+        copy_v(0);
       load_k(0);
     }
   }

@@ -22,7 +22,7 @@ import pytest
 import torch
 
 from nvfp4_fake_quantized_amd import binding as B
-from oracle.attention import qat_forward_head, quantize_qkv
+from oracle.attention import qat_forward_head
 from oracle.nvfp4 import fake_nvfp4
 from tests._util import check_close, f64_to_bf16_bits, fwd_plan
 
@@ -85,10 +85,20 @@ def _run(b, h, nq, nkv, d, causal):
           f"{S} key runs", flush=True)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     p = B.problem_for(qd, kd, causal, scale)
-    ws = torch.empty(B.attnqat_fwd_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    # 0xFF-filled: the call must write Q^, K^, V^ and their scales itself
+    ws = torch.full((B.attnqat_fwd_workspace_bytes(p),), 0xFF, dtype=torch.uint8, device=DEV)
     o = torch.empty_like(qd)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=DEV)
     B.attnqat_fwd(p, qd, kd, vd, o, lse, ws)
+    torch.cuda.synchronize()
+    L = B.attnqat_workspace_layout(p, B.WS_FWD)
+    parts = {}
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        n = t.numel()
+        parts[name] = (ws[L[f"{name}_hat"]:L[f"{name}_hat"] + 2 * n].view(torch.int16)
+                       .view(t.shape).cpu(),
+                       ws[L[f"{name}_scale"]:L[f"{name}_scale"] + n // 16]
+                       .view(*t.shape[:3], d // 16).cpu())
     # the same forward from packed NVFP4 K/V
     kc, ks = B.attnqat_nvfp4_pack(kd)
     vc, vs = B.attnqat_nvfp4_pack(vd)
@@ -96,17 +106,24 @@ def _run(b, h, nq, nkv, d, causal):
     ws2 = torch.full_like(ws, 0xFF)  # the packed call must write Q^ and its scales itself
     B.attnqat_fwd_packed(p, qd, kc, ks, vc, vs, o2, lse2, ws2)
     torch.cuda.synchronize()
-    L = B.attnqat_workspace_layout(p, B.WS_FWD)
     nqh = b * h * nq * d
     qhat = ws2[L["q_hat"]:L["q_hat"] + 2 * nqh].view(torch.int16).view(b, h, nq, d).cpu()
     qsc = ws2[L["q_scale"]:L["q_scale"] + nqh // 16].view(b, h, nq, d // 16).cpu()
     for bi in range(b):
         for hi in range(h):
-            qh, kh, vh = quantize_qkv(q[bi, hi].double().numpy(), k[bi, hi].double().numpy(),
-                                      v[bi, hi].double().numpy())
-            ref_q, _, ref_sc, _ = fake_nvfp4(q[bi, hi].double().numpy())
-            assert np.array_equal(qhat[bi, hi].numpy().view(np.uint16), f64_to_bf16_bits(ref_q))
-            assert np.array_equal(qsc[bi, hi].numpy(), ref_sc)
+            # Q^, K^, V^ and their scale bytes (the oracle's fake_nvfp4)
+            fq = {name: fake_nvfp4(t[bi, hi].double().numpy())
+                  for name, t in (("q", q), ("k", k), ("v", v))}
+            qh, kh, vh = fq["q"][0], fq["k"][0], fq["v"][0]
+            assert np.array_equal(qhat[bi, hi].numpy().view(np.uint16), f64_to_bf16_bits(qh))
+            assert np.array_equal(qsc[bi, hi].numpy(), fq["q"][2])
+            # the bf16 call's workspace (written by the quantization pass, or
+            # by the 32-query-tile kernel itself)
+            for name in ("q", "k", "v"):
+                xh, xs = parts[name]
+                assert np.array_equal(xh[bi, hi].numpy().view(np.uint16),
+                                      f64_to_bf16_bits(fq[name][0])), (name, bi, hi)
+                assert np.array_equal(xs[bi, hi].numpy(), fq[name][2]), (name, bi, hi)
             o64, l64 = qat_forward_head(qh, kh, vh, scale, causal, quantize=False)
             tag = f"{kind} Nq{nq} Nkv{nkv} D{d} causal={causal}"
             check_close(o[bi, hi].cpu(), o64, f"{tag} O_hp[{bi},{hi}]")
