@@ -610,7 +610,9 @@ def main():
         "fwd_attention": ("mfma", 4.0 * BH * N * N * D * half),
         "bwd_dq": ("mfma", 6.0 * BH * N * N * D * half),
         "bwd_dkdv": ("mfma", 8.0 * BH * N * N * D * half),
-        "fwd_quant_qkv": ("hbm", 3 * elems * (4 + 1 / 16)),
+        # Q, K and V (at D = 128 only K and V: the attention kernel quantizes
+        # its own Q rows)
+        "fwd_quant_qkv": ("hbm", (2 if D == 128 else 3) * elems * (4 + 1 / 16)),
         # Q + delta (reads Q, O_hp, dO; writes Q^, scales, delta); K and V
         # are fake-quantized inside the dK/dV kernel
         "bwd_codec": ("hbm", elems * (8 + 1 / 16) + BH * N * 4),

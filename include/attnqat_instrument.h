@@ -22,8 +22,9 @@ extern "C" {
  * event (hipExtLaunchKernel), so per-kernel durations can be read with
  * hipEventElapsedTime(events[2i], events[2i+1]) without synchronizing inside
  * the call and without extra packets or gaps between the kernels.
- * attnqat_fwd_timed: 4 events; kernel 0 the Q/K/V fake-quant (an empty span
- *   when the forward takes 32-query tiles, which quantize inside the
+ * attnqat_fwd_timed: 4 events; kernel 0 the Q/K/V fake-quant (K/V only at
+ *   head_dim 128, where the attention kernel quantizes Q; an empty span when
+ *   the forward takes 32-query tiles, which quantize Q, K and V inside the
  *   attention kernel), kernel 1 the attention forward (when the forward
  *   covers the keys in runs -- see attnqat_fwd -- its pair spans the
  *   attention launch and the merge launch).

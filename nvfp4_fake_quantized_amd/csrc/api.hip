@@ -328,7 +328,16 @@ int run_fwd(const attnqat_problem* p, const void* q, const void* k, const void* 
     if (e0 != nullptr && (hipEventRecord(e0->start, stream) != hipSuccess ||
                           hipEventRecord(e0->stop, stream) != hipSuccess))
       return ATTNQAT_ERR_HIP;
+  } else if (D == 128) {
+    // K and V in one pass (each K^/V^ tile is read by every query tile of its
+    // head); the attention kernel fake-quantizes each workgroup's Q rows
+    a.q_in = static_cast<const uint16_t*>(q);
+    a.q_hat_out = qh;
+    a.q_scale_out = at<uint8_t>(workspace, L.q_scale);
+    if (attnqat::launch_quant_bf16(jobs + 1, 2, stream, timing(ev, 0)) != hipSuccess)
+      return ATTNQAT_ERR_HIP;
   } else if (attnqat::launch_quant_bf16(jobs, 3, stream, timing(ev, 0)) != hipSuccess) {
+    // D = 64: Q in the same pass (measured faster for causal problems there)
     return ATTNQAT_ERR_HIP;
   }
 
@@ -382,15 +391,10 @@ int run_fwd_packed(const attnqat_problem* p, const void* q, const uint8_t* k_cod
   uint16_t* qh = at<uint16_t>(workspace, L.q_hat);
   uint8_t* qs = at<uint8_t>(workspace, L.q_scale);
   AttnArgs a = {};
-  if (L.kv_decode) {
-    // the 32-query-tile kernel fake-quantizes Q itself (one launch fewer)
-    a.q_in = static_cast<const uint16_t*>(q);
-    a.q_hat_out = qh;
-    a.q_scale_out = qs;
-  } else {
-    QuantJob job = {q, qh, qs, bh * p->seqlen_q * p->head_dim / 16};
-    if (attnqat::launch_quant_bf16(&job, 1, stream) != hipSuccess) return ATTNQAT_ERR_HIP;
-  }
+  // the attention kernels fake-quantize Q themselves (no separate launch)
+  a.q_in = static_cast<const uint16_t*>(q);
+  a.q_hat_out = qh;
+  a.q_scale_out = qs;
   a.q_hat = qh;
   a.k_codes = k_codes;
   a.k_scales = k_scales;

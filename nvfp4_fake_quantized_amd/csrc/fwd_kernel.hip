@@ -211,7 +211,11 @@ void k_fwd(AttnArgs a) {
   const int qblk0 = t.tile * kFwdBM;
   const int qw0 = qblk0 + wave * 32;
   const int qi = qw0 + l32;
-  const uint16_t* Q = a.q_hat + (size_t)bh * nq * D;
+  // with raw Q (q_in set) the workgroup fake-quantizes its own query rows
+  // (a lane holds 8 columns of a 16-value group, the lane 32 away the other
+  // 8), and the first key run writes Q^ and its scale bytes
+  const bool qfuse = a.q_in != nullptr;
+  const uint16_t* Q = (qfuse ? a.q_in : a.q_hat) + (size_t)bh * nq * D;
   const uint16_t* K = a.k_hat + (size_t)bh * nkv * D;
   const uint16_t* V = a.v_hat + (size_t)bh * nkv * D;
 
@@ -219,6 +223,19 @@ void k_fwd(AttnArgs a) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
     qf[kb] = (qi < nq) ? ld_bf16x8(Q + (size_t)qi * D + 16 * kb + 8 * h) : zero_bf16x8();
+  if (qfuse) {
+    const bool wr = qi < nq && (!SPLIT || blockIdx.y == 0);
+    const size_t row = (size_t)bh * nq + qi;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      uint32_t sb;
+      qf[kb] = fq_half_group<32>(qf[kb], sb);
+      if (wr) {
+        *reinterpret_cast<bf16x8*>(a.q_hat_out + row * D + 16 * kb + 8 * h) = qf[kb];
+        if (h == 0) a.q_scale_out[row * KB + kb] = (uint8_t)sb;
+      }
+    }
+  }
 
   f32x16 o[DB];
 #pragma unroll
