@@ -222,7 +222,8 @@ def p_scale_study(p_scales=(1.0, 64.0, 512.0, 2688.0), reps=5):
             for i in range(2 + reps):
                 B.attnqat_bwd_timed(p, q, k, v, o, do, lse, dq, dk, dv, wsb, evs[max(i - 2, 0)])
             torch.cuda.synchronize()
-            bwd_ms = sum(hip.ms(e[0], e[5]) for e in evs) / reps
+            # events: preprocessing, dQ (launched last), dK/dV
+            bwd_ms = sum(hip.ms(e[0], e[3]) for e in evs) / reps
             num = den_a = den_b = 0.0
             zero = total = 0
             for b, h in heads:
@@ -531,7 +532,7 @@ def main():
     per_lists.update({n: [hip.ms(e[2 * j], e[2 * j + 1]) for e in evb]
                       for j, n in enumerate(names_b)})
     per = {n: _stats(x)["median"] for n, x in per_lists.items()}
-    bwd_inst = [hip.ms(e[0], e[5]) for e in evb]
+    bwd_inst = [hip.ms(e[0], e[3]) for e in evb]  # dQ (kernel 1) is launched last
 
     extras = {}
     if not args.no_extras:
