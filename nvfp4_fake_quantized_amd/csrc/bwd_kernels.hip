@@ -21,8 +21,8 @@
 // mask, keys >= Nkv get P = 0, loads beyond the ends read zeros and stores
 // stop at the ends.  When the query blocks cannot fill the chip, the key
 // tiles of each block are split over blockIdx.y: each split writes its fp32
-// dQ^T partial, and k_sum_parts (launched after k_dkdv, with its sums) adds
-// the splits in order (deterministic).
+// dQ^T partial, and k_sum_parts (launched after both attention kernels, with
+// the dK/dV sums) adds the splits in order (deterministic).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
