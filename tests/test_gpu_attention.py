@@ -40,9 +40,17 @@ def _ws_part(ws, off, shape, dtype):
     return ws[off:off + n].view(dtype).view(*shape)
 
 
+def _filled_workspace(nbytes):
+    """A workspace of 0xFF bytes, so that the Q^/K^/V^ checks only pass for
+    parts the call wrote itself (not for what an earlier call left behind)."""
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    return ws
+
+
 def gpu_fwd(q, k, v, causal, scale, p_scale=1.0, stream=None):
     p = B.problem_for(q, k, causal, scale, p_scale)
-    ws = torch.empty(B.attnqat_fwd_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    ws = _filled_workspace(B.attnqat_fwd_workspace_bytes(p))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
     B.attnqat_fwd(p, q, k, v, o, lse, ws, stream)
@@ -52,7 +60,7 @@ def gpu_fwd(q, k, v, causal, scale, p_scale=1.0, stream=None):
 
 def gpu_bwd(q, k, v, o, do, lse, causal, scale, p_scale=1.0, stream=None):
     p = B.problem_for(q, k, causal, scale, p_scale)
-    ws = torch.empty(B.attnqat_bwd_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    ws = _filled_workspace(B.attnqat_bwd_workspace_bytes(p))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     B.attnqat_bwd(p, q, k, v, o, do, lse, dq, dk, dv, ws, stream)
     torch.cuda.synchronize()
