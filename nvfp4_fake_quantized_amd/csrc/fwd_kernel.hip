@@ -513,11 +513,14 @@ __global__ __launch_bounds__(256) void k_fwd_combine(AttnArgs a, int64_t rows) {
 //    the only partial tile of the head comes first and only that step
 //    evaluates a mask;
 //  * the workgroup's Q^ rows sit in LDS and are read as the B operand of
-//    S^T = K^ Q^T (for packed K/V the kernel fake-quantizes the raw Q rows
-//    itself when given them, and the first key run writes Q^ and its scale
-//    bytes to the workspace);
+//    S^T = K^ Q^T (given the raw Q rows, the kernel fake-quantizes them
+//    itself, and the first key run writes Q^ and its scale bytes to the
+//    workspace);
 //  * bf16 K^ rows go global -> registers (A operands) one tile ahead, V^
-//    tiles global -> LDS directly one tile ahead;
+//    tiles global -> LDS directly one tile ahead; given raw K/V instead,
+//    both go to registers one tile ahead, and at the start of the tile's step
+//    the wave fake-quantizes them (each key tile has one owner), writes V^
+//    into its LDS tile and K^, V^ and their scale bytes to the workspace;
 //  * packed K^/V^: codes and scale bytes of two tiles ahead in registers,
 //    dequantized to fp16 (exact: see dec_scale) and multiplied on fp16 MFMAs
 //    (Q^ staged in fp16, also exact; P^T rounded to fp16, finer than the bf16

@@ -66,15 +66,16 @@ struct AttnArgs {
   float* ml_part;         // (BH, kv_splits, nq, 2): base (log2 units), sum
   int kv_splits;          // 0 or 1: no split
   int kv_decode;          // 1: 32-query tiles (k_fwd_dec), kv_splits >= 1 key runs
-  // k_fwd_dec from packed K/V: when q_in is set, the kernel fake-quantizes
-  // its Q rows itself and the first key run of each query tile writes Q^ and
-  // its scale bytes to q_hat_out / q_scale_out
+  // k_fwd and k_fwd_dec: when q_in is set, the kernel fake-quantizes its Q
+  // rows itself and the first key run of each query tile writes Q^ and its
+  // scale bytes to q_hat_out / q_scale_out
   const uint16_t* q_in;   // (BH, nq, D) bf16
   uint16_t* q_hat_out;
   uint8_t* q_scale_out;   // (BH, nq, D/16)
-  // k_dkdv: when k_in is set, the kernel fake-quantizes the K and V rows of
-  // its key block itself, and the first query run of each key block writes
-  // K^, V^ and their scale bytes (for k_dq, which runs after it)
+  // k_dkdv and k_fwd_dec (from bf16 K/V): when k_in is set, the kernel
+  // fake-quantizes the K and V rows it owns (k_dkdv: its key block, whose
+  // first query run writes them; k_fwd_dec: its key tiles) and writes K^, V^
+  // and their scale bytes (k_dq, which runs after k_dkdv, reads them)
   const uint16_t* k_in;   // (BH, nkv, D) bf16
   const uint16_t* v_in;
   uint16_t* k_hat_out;
