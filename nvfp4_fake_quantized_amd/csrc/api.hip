@@ -453,9 +453,7 @@ int run_bwd(const attnqat_problem* p, const void* q, const void* k, const void* 
                                  at<uint8_t>(workspace, L.q_scale),
                                  delta,
                                  bh * p->seqlen_q};
-  const QuantJob kj = {k, kh, at<uint8_t>(workspace, L.k_scale), 0};
-  const QuantJob vj = {v, vh, at<uint8_t>(workspace, L.v_scale), 0};
-  if (attnqat::launch_bwd_codec(qd, kj, vj, p->head_dim, stream, timing(ev, 0)) != hipSuccess)
+  if (attnqat::launch_bwd_codec(qd, p->head_dim, stream, timing(ev, 0)) != hipSuccess)
     return ATTNQAT_ERR_HIP;
 
   AttnArgs a = {};

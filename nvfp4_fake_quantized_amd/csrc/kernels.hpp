@@ -111,9 +111,8 @@ hipError_t launch_quant_bf16(const QuantJob* jobs, int njobs, hipStream_t stream
 hipError_t launch_pack_bf16(const QuantJob& job, uint8_t* codes, hipStream_t stream);
 // fake_nvfp4 over one fp32 tensor.
 hipError_t launch_quant_f32(const QuantJob& job, hipStream_t stream);
-// The backward's preprocessing in one launch: Q fake-quant fused with
-// delta = rowsum(O_hp * dO) (fp32), and K and V fake-quant when their jobs
-// have groups (none: only Q + delta is launched); D in {64, 128}.
+// The backward's preprocessing: Q fake-quant fused with
+// delta = rowsum(O_hp * dO) (fp32); D in {64, 128}.
 struct QDeltaJob {
   const uint16_t* q;
   const uint16_t* o_hp;
@@ -123,8 +122,8 @@ struct QDeltaJob {
   float* delta;
   int64_t rows;  // batch * heads * seqlen_q
 };
-hipError_t launch_bwd_codec(const QDeltaJob& qd, const QuantJob& k, const QuantJob& v,
-                            int head_dim, hipStream_t stream, const LaunchEvents* ev = nullptr);
+hipError_t launch_bwd_codec(const QDeltaJob& qd, int head_dim, hipStream_t stream,
+                            const LaunchEvents* ev = nullptr);
 
 hipError_t launch_fwd(const AttnArgs& a, int head_dim, hipStream_t stream,
                       const LaunchEvents* ev = nullptr);

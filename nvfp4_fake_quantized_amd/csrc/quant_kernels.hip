@@ -2,12 +2,10 @@
 //
 // One thread owns one group of 16 contiguous values ("NVFP4 Attention QAT
 // Backward", §Overview: one E4M3 scale per 16 values); a wave covers 64
-// consecutive groups, i.e. 2 KiB of contiguous bf16 input.  k_bwd_codec
-// holds the backward's preprocessing (same page, §Overview: the fused Q
-// fake-quantization / delta kernel, and optionally the K/V fake-quantization
-// in the same grid: blockIdx.y selects Q + delta, K or V).  The backward
-// itself runs only its Q + delta part: its dK/dV kernel fake-quantizes K and V
-// (each workgroup the rows of its own key block).
+// consecutive groups, i.e. 2 KiB of contiguous bf16 input.  k_bwd_codec is
+// the backward's preprocessing (same page, §Overview: the fused Q
+// fake-quantization / delta kernel); the K/V fake-quantization runs inside the
+// dK/dV kernel (each workgroup the rows of its own key block).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -138,18 +136,11 @@ __device__ __forceinline__ void q_delta_group(const QDeltaJob& J, int64_t g) {
   if (active && (g % GPR) == 0) J.delta[g / GPR] = part;
 }
 
-// blockIdx.y = 0: Q + delta; 1: K; 2: V.  Blocks past a part's end exit.
+// Q + delta over all rows; blocks past the end exit.
 template <int GPR>
-__global__ __launch_bounds__(kThreads) void k_bwd_codec(QDeltaJob qd, QuantJob kj,
-                                                        QuantJob vj) {
+__global__ __launch_bounds__(kThreads) void k_bwd_codec(QDeltaJob qd) {
   const int64_t g0 = (int64_t)blockIdx.x * kThreads;
-  const int64_t g = g0 + threadIdx.x;
-  if (blockIdx.y == 0) {
-    if (g0 < qd.rows * GPR) q_delta_group<GPR>(qd, g);  // uniform per workgroup
-  } else {
-    const QuantJob& J = blockIdx.y == 1 ? kj : vj;
-    if (g < J.groups) quant_group(J, g);
-  }
+  if (g0 < qd.rows * GPR) q_delta_group<GPR>(qd, g0 + threadIdx.x);  // uniform per workgroup
 }
 
 inline unsigned grid_for(int64_t groups) {
@@ -183,18 +174,14 @@ hipError_t launch_quant_f32(const QuantJob& job, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_codec(const QDeltaJob& qd, const QuantJob& k, const QuantJob& v,
-                            int head_dim, hipStream_t stream, const LaunchEvents* ev) {
+hipError_t launch_bwd_codec(const QDeltaJob& qd, int head_dim, hipStream_t stream,
+                            const LaunchEvents* ev) {
   const int gpr = head_dim / 16;
-  int64_t maxg = qd.rows * gpr;
-  if (k.groups > maxg) maxg = k.groups;
-  if (v.groups > maxg) maxg = v.groups;
-  if (maxg == 0) return hipSuccess;
-  // without K/V groups (the backward quantizes K and V inside k_dkdv) only
-  // the Q + delta part is launched
-  const dim3 grid(grid_for(maxg), (k.groups > 0 || v.groups > 0) ? 3 : 1);
-  if (gpr == 8) return launch(k_bwd_codec<8>, grid, dim3(kThreads), stream, ev, qd, k, v);
-  return launch(k_bwd_codec<4>, grid, dim3(kThreads), stream, ev, qd, k, v);
+  const int64_t groups = qd.rows * gpr;
+  if (groups == 0) return hipSuccess;
+  const dim3 grid(grid_for(groups));
+  if (gpr == 8) return launch(k_bwd_codec<8>, grid, dim3(kThreads), stream, ev, qd);
+  return launch(k_bwd_codec<4>, grid, dim3(kThreads), stream, ev, qd);
 }
 
 }  // namespace attnqat
